@@ -1,0 +1,211 @@
+/*
+ * qimg.h — C ABI of the shared Q8_1 activation-image library for AMD MI355X (gfx950).
+ *
+ * An activation producer (RMSNorm, RMSNorm x gamma, SwiGLU or GeGLU-erf) writes its f32
+ * output and, in the same pass, a block-quantized Q8_1 image of that output. The image is
+ * then read by any number of Q4_0-weight mat-vec projections (MMVQ): ordinary readers and
+ * routed MUL_MAT_ID expert slots that process only the live rows of a padded bucket.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P1] "Share temporary Q8_1 activation images" (llama.cpp fork, PR #117):
+ *        Overview, Coverage, GLU producer evidence.
+ *   [P2] "r49 - A-quantize prepass shared-A dedup: consecutive-window memoization":
+ *        section 2 Principle, section 3.1 Design choices.
+ *   [P3] "qwen3_5 CUDA: a captured bucket's padding rows no longer go through the routed
+ *        experts" (TensorFold PR #1047): What this changes, Receipt.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership.  Every data pointer is device memory owned by the caller. The reader arrays
+ *   (qimg_q4_0_reader / qimg_q4_0_expert_reader) are host memory and are copied into the
+ *   kernel arguments before the call returns. The library allocates nothing, keeps no
+ *   reference after return and holds no mutable global state: an image is refreshed by
+ *   every call that writes it, never cached across calls ([P1] Coverage: images refresh on
+ *   every execution; [P2] section 2: no cache persists across executions).
+ * Execution.  Calls enqueue work on `stream` (a hipStream_t; NULL is the default stream)
+ *   and return without synchronising. They never read device memory on the host, so they
+ *   may be recorded into a HIP graph. The live-row count is read on the device at run time,
+ *   so one recorded graph serves every live count ([P3] What this changes).
+ * Errors.  A negative status means the arguments were rejected on the host and nothing was
+ *   enqueued. QIMG_EHIP means a HIP launch failed; the stream state is then undefined.
+ *   Errors found on the device are reported through the routed workspace error word.
+ * Sizes.  K (the reduction width) must be a positive multiple of 32 (one Q8_1 block):
+ *   [P1] Coverage requires whole Q8_1 blocks for output and image row widths.
+ *   K <= QIMG_MAX_K. Row strides are in elements and must keep 16-byte alignment.
+ *
+ * Data layouts
+ * ------------
+ * Q8_1 image (one allocation, two planes; rows = producer rows, RB = qimg_row_blocks(K)):
+ *   codes plane : int8  codes[rows][RB][32]            at byte 0
+ *   ds plane    : uint32 ds[rows][RB]                  at byte rows*RB*32
+ *                 low half = fp16 d (block scale amax/127), high half = fp16 s (d * sum of
+ *                 the block's codes), little-endian.
+ *   Blocks K/32 <= b < RB of every live row are written as zero bytes (row padding to a
+ *   multiple of 16 blocks, i.e. 512 elements). Rows >= live count are never written.
+ * Q4_0 weights (one reader, or one expert of a routed reader):
+ *   qs plane : uint8  qs[N][K/32][16]; byte j of a block holds element j in its low nibble
+ *              and element j+16 in its high nibble.
+ *   d plane  : fp16   d[N][K/32]; weight = d * (nibble - 8).
+ *   Routed readers stack E experts: qs[E][N][K/32][16], d[E][N][K/32].
+ */
+#ifndef QIMG_H
+#define QIMG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QIMG_ABI_VERSION 1
+
+/* status codes */
+#define QIMG_OK 0
+#define QIMG_EINVAL (-1)       /* null required pointer, bad size, bad op code */
+#define QIMG_EALIGN (-2)       /* a plane base or stride breaks the required alignment */
+#define QIMG_EALIAS (-3)       /* an output overlaps an input or another output */
+#define QIMG_EUNSUPPORTED (-4) /* shape outside the supported range (e.g. K > QIMG_MAX_K) */
+#define QIMG_EWORKSPACE (-5)   /* routed workspace missing or smaller than required */
+#define QIMG_EHIP (-6)         /* a HIP runtime call failed */
+
+#define QIMG_MAX_K 32768
+#define QIMG_MAX_READERS 8
+
+/* GLU producer formulas ([P1] Coverage: F32 SwiGLU and GeGLU-erf producers) */
+#define QIMG_GLU_SWIGLU 0    /* y = g / (1 + exp(-g)) * u                      */
+#define QIMG_GLU_GEGLU_ERF 1 /* y = 0.5 * g * (1 + erf(g / sqrt(2))) * u       */
+
+/* Routed workspace error-word bits (set on the device, read by the caller after sync). */
+#define QIMG_ERR_EXPERT_RANGE 1 /* a live pair named an expert outside [0, E); it was skipped */
+#define QIMG_ERR_LIVE_CLAMPED 2 /* *live_rows was above the bucket size (or negative); clamped */
+
+/* Human-readable text for a status code. Never returns NULL. */
+const char* qimg_strerror(int status);
+
+/* QIMG_ABI_VERSION of the loaded library. */
+int qimg_abi_version(void);
+
+/* Image row blocks RB = round_up(K/32, 16); 0 when K is not a positive multiple of 32. */
+int32_t qimg_row_blocks(int32_t K);
+
+/* Bytes of an image of `rows` rows: rows * RB * 36; 0 on a bad K or rows < 0. */
+int64_t qimg_image_bytes(int32_t rows, int32_t K);
+
+/*
+ * RMSNorm producer ([P1] Coverage: RMS-alone and RMS+MUL producers emit images while every
+ * original F32 store remains). For each live row i (i < live, live = *live_rows clamped to
+ * [0, rows], or rows when live_rows is NULL):
+ *   S = sum of x[i][k]^2 in the library's fixed reduction order; r = 1/sqrt(S/K + eps)
+ *   y[i][k] = (x[i][k] * r) * gamma[k]        (gamma == NULL: y = x * r)
+ * and, when img != NULL, the Q8_1 image row i of y (see qimg_quantize_q8_1 for the block
+ * rule). img == NULL writes y only: the separate-quantizer ("original") arm.
+ *   x     : f32 [rows][ldx], 16-byte aligned, ldx % 4 == 0, ldx >= K
+ *   gamma : f32 [K], 16-byte aligned, or NULL
+ *   y     : f32 [rows][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= K; must not overlap x,
+ *           gamma or img
+ *   img   : qimg_image_bytes(rows, K) bytes, 16-byte aligned, or NULL
+ *   live_rows : device int32, or NULL
+ * Rows >= live are not read and not written.
+ */
+int qimg_emit_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps, int32_t rows,
+                      const int32_t* live_rows, int32_t K, float* y, int64_t ldy, void* img,
+                      void* stream);
+
+/*
+ * GLU producer ([P1] Coverage: F32 SwiGLU and GeGLU-erf producers with separate or packed
+ * inputs emit images; original F32 outputs remain). For live rows i and k < K:
+ *   g = gate[i*ldg + k], u = up[i*ldu + k], y[i][k] = act(g) * u
+ * with act per `op` (QIMG_GLU_*). Packed gate|up input: gate = gu, up = gu + K, ldg = ldu = 2K.
+ *   gate, up : f32, 16-byte aligned, strides % 4 == 0
+ *   y, img, live_rows : as for qimg_emit_rmsnorm
+ */
+int qimg_emit_glu(int32_t op, const float* gate, int64_t ldg, const float* up, int64_t ldu,
+                  int32_t rows, const int32_t* live_rows, int32_t K, float* y, int64_t ldy,
+                  void* img, void* stream);
+
+/*
+ * The separate activation quantizer: the launch the fused producers remove ([P1] Overview),
+ * kept as the control arm and as the fallback when emission is declined. For each live row
+ * and each 32-element block of y:
+ *   amax = max |y|; d = amax / 127; id = 1/d; c = round-half-away-from-zero(y * id)
+ *   d16 = fp16(d); s16 = fp16((float)(sum of c) * d)    (both round-to-nearest-even)
+ * A block whose amax is 0 (or whose 1/d is not finite) is all zero bytes. Produces the same
+ * bytes as the fused producers' image of the same y.
+ *   y   : f32 [rows][ldy], 16-byte aligned, ldy % 4 == 0
+ *   img : qimg_image_bytes(rows, K) bytes, 16-byte aligned; must not overlap y
+ */
+int qimg_quantize_q8_1(const float* y, int64_t ldy, int32_t rows, const int32_t* live_rows,
+                       int32_t K, void* img, void* stream);
+
+/* One ordinary Q4_0 reader of an image. */
+typedef struct {
+  const void* qs;  /* uint8 [N][K/32][16], 16-byte aligned */
+  const void* d;   /* fp16  [N][K/32], 4-byte aligned */
+  int32_t N;       /* output rows (> 0) */
+  int32_t reserved;
+  float* out;      /* f32, out[t * ldo + n] for image row t, n < N; 4-byte aligned */
+  int64_t ldo;     /* >= N */
+} qimg_q4_0_reader;
+
+/*
+ * Ordinary MMVQ readers ([P1] Coverage: ordinary MUL_MAT on its MMVQ path with arbitrarily
+ * many compatible readers of one image). One launch serves up to QIMG_MAX_READERS readers:
+ *   out_r[t][n] = sum over blocks b of d_w[n][b] * (d16[t][b] * sumi - 8 * s16[t][b])
+ *   sumi = sum_{j<16} (qs[n][b][j] & 15) * c[t][b][j] + (qs[n][b][j] >> 4) * c[t][b][j+16]
+ * for image rows t < live (live as above; rows = image rows). Rows t >= live of every out
+ * are not written. Outputs must not overlap each other, the image or the weights.
+ */
+int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                   int32_t rows, const int32_t* live_rows, int32_t K, void* stream);
+
+/* One routed (MUL_MAT_ID) Q4_0 reader over E stacked experts. */
+typedef struct {
+  const void* qs;  /* uint8 [E][N][K/32][16], 16-byte aligned */
+  const void* d;   /* fp16  [E][N][K/32], 4-byte aligned */
+  int32_t N;       /* output rows per expert (> 0) */
+  int32_t reserved;
+  float* out;      /* f32, out[(row * top_k + slot) * ld_pair + n] */
+  int64_t ld_pair; /* >= N */
+} qimg_q4_0_expert_reader;
+
+/* Workspace bytes mmvq_id_q4_0_q8_1 needs: 16 + 4*(E + (E+1) + bucket*top_k), 256-rounded. */
+size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E);
+
+/*
+ * Routed MMVQ readers ([P1] Coverage: quantized MUL_MAT_ID on its MMVQ path; the image is
+ * independent of route ids and serves ID-distinct readers. [P3] What this changes: only the
+ * first live rows' pairs are planned; padding rows get no picks, no plan items, no expert
+ * work and no writes; launches stay sized for the bucket and read the live count at run time).
+ * For every live pair p = row*top_k + slot (row < live, e = ids[p] in [0, E)):
+ *   out_r[p][n] = the ordinary reader formula with expert e's weights and image row `row`.
+ *   ids       : device int32 [bucket][top_k]; entries of padding rows are never read
+ *   live_rows : device int32 (clamped to [0, bucket]), or NULL for all bucket rows
+ *   img       : image with `bucket` rows
+ *   workspace : device, >= mmvq_id_workspace_bytes(bucket, top_k, E), 16-byte aligned.
+ *     Fully rewritten by every call (no clearing needed) with the routing plan:
+ *       int32 word 0: error bits (QIMG_ERR_*), word 1: live pair count P = live*top_k,
+ *       words 2..3: reserved,
+ *       int32 counts[E]   : live pairs per expert
+ *       int32 offsets[E+1]: exclusive prefix of counts (offsets[E] = valid live pairs)
+ *       int32 members[P]  : pair ids grouped by ascending expert, ascending within an expert
+ * Pair outputs are independent of which other pairs share an expert, so a live row's outputs
+ * equal those of a one-row call on the same data, bit for bit ([P3] Receipt).
+ */
+int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
+                      const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
+                      const int32_t* live_rows, int32_t K, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Debug export of the per-block integer dot products of one ordinary reader, computed by
+ * the same device code the readers use:
+ *   sumi[t][n][b] (int32, [rows][N][K/32]) for all image rows t < rows.
+ */
+int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, int32_t rows,
+                             int32_t K, int32_t* sumi, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QIMG_H */

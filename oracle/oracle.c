@@ -1,0 +1,384 @@
+/*
+ * oracle.c — plain, slow CPU definition of the shared Q8_1 activation-image path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library. The product path (the HIP library) never calls it, and the two
+ * share no code, header, table or constant generator.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared oracle.c -lm
+ * (x86-64 SSE arithmetic: every float operation is a single IEEE binary32 rounding; fmaf is
+ * the correctly rounded fused multiply-add of C99.)
+ *
+ * What it computes. The fused producer must give exactly what "producer, then the separate
+ * quantizer, then the readers" gives ("Share temporary Q8_1 activation images", Overview:
+ * emission removes a separate quantization launch and reread while reduction trees and
+ * quantization rounding stay intact). So this file spells out that plain pipeline:
+ *   rms / glu producer (f32, the F32 output the pages keep)  ->  per-32-block Q8_1 quantizer
+ *   ->  Q4_0 x Q8_1 readers evaluated in float64 from the quantized operands
+ *   ->  routed plan (stable grouping of the live pairs by expert).
+ * Where the pages are silent (rounding mode, reduction order, exp/erf, layouts) the reading
+ * adopted is stated at the function and listed in the design notes.
+ */
+#define _DEFAULT_SOURCE /* M_LN2, M_LOG2E, M_SQRT1_2 */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------------------------
+ * binary16 conversion. The Q8_1 block stores "half scales/sums" ("Share temporary Q8_1
+ * activation images", GLU producer evidence, validation list). f32 -> f16 is IEEE
+ * round-to-nearest-even with subnormals kept and overflow to infinity.
+ * Written with double arithmetic: the value is scaled to an integer multiple of its f16 ulp
+ * (exact in double), rounded with nearbyint (ties to even), and re-encoded.
+ * ---------------------------------------------------------------------------------------- */
+uint16_t orc_f32_to_f16(float f) {
+  uint32_t bits;
+  memcpy(&bits, &f, 4);
+  uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+  if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+  double a = fabs((double)f);
+  if (isinf(f)) return (uint16_t)(sign | 0x7c00u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);               /* a = m * 2^e, m in [0.5, 1): exponent of a is e-1 */
+  int ex = e - 1;             /* a in [2^ex, 2^(ex+1)) */
+  if (ex < -14) ex = -14;     /* subnormal range shares the ulp of the smallest normal */
+  double ulp = ldexp(1.0, ex - 10);
+  double q = nearbyint(a / ulp); /* a/ulp exact (power-of-two scaling); ties to even */
+  /* q in [0, 2048]; value = q * ulp */
+  uint32_t h;
+  if (ex == -14 && q < 1024.0) {
+    h = (uint32_t)q; /* subnormal (or the smallest normal when q reaches 1024) */
+  } else {
+    /* q in [1024, 2048]: q == 2048 carries into the next binade automatically */
+    h = (uint32_t)((ex + 15) << 10) + (uint32_t)(q - 1024.0);
+    if (h >= 0x7c00u) h = 0x7c00u; /* overflow to infinity */
+  }
+  return (uint16_t)(sign | h);
+}
+
+void orc_f32_to_f16_array(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(x[i]);
+}
+
+/* Exact binary16 -> double. */
+double orc_f16_to_f64(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(m + 1024), e - 25);
+  return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * exp_q: the exponential the GLU producers use, defined here so that CPU and GPU evaluate the
+ * same operation sequence (the pages name the SwiGLU/GeGLU-erf formulas but no exp):
+ *   Cody-Waite reduction  n = rint(x * log2(e)), r = (x - n*LN2_HI) - n*LN2_LO (two fmas),
+ *   degree-7 Taylor polynomial of e^r (coefficients 1/k! rounded to f32) by Horner with fma,
+ *   result = ldexp(p, n).
+ * LN2_HI is ln 2 rounded to f32 with its low 12 significand bits cleared (so n*LN2_HI is exact
+ * for |n| < 2^12), LN2_LO the f32 nearest ln 2 - LN2_HI. Saturation: NaN passes through;
+ * x > 88.8 gives +inf; x < -86 gives +0 (results that would need f32 subnormals are flushed).
+ * ---------------------------------------------------------------------------------------- */
+static float g_ln2_hi, g_ln2_lo, g_log2e, g_inv_fact[8];
+static int g_consts_ready = 0;
+
+static void orc_init_consts(void) {
+  if (g_consts_ready) return;
+  float ln2f = (float)M_LN2;
+  uint32_t b;
+  memcpy(&b, &ln2f, 4);
+  b &= ~0xfffu;
+  memcpy(&g_ln2_hi, &b, 4);
+  g_ln2_lo = (float)(M_LN2 - (double)g_ln2_hi);
+  g_log2e = (float)M_LOG2E;
+  double f = 1.0;
+  for (int k = 0; k < 8; ++k) {
+    if (k > 0) f *= (double)k;
+    g_inv_fact[k] = (float)(1.0 / f);
+  }
+  g_consts_ready = 1;
+}
+
+float orc_exp_q(float x) {
+  orc_init_consts();
+  if (x != x) return x;
+  if (x > 88.8f) return INFINITY;
+  if (x < -86.0f) return 0.0f;
+  float n = rintf(x * g_log2e);
+  float r = fmaf(-n, g_ln2_hi, x);
+  r = fmaf(-n, g_ln2_lo, r);
+  float p = g_inv_fact[7];
+  for (int k = 6; k >= 0; --k) p = fmaf(p, r, g_inv_fact[k]);
+  return ldexpf(p, (int)n);
+}
+
+void orc_exp_q_array(const float* x, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_exp_q(x[i]);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * erfc_q(z), z >= 0: the Chebyshev-fitted complementary error function of Numerical Recipes
+ * ("erfcc": erfc(z) = t * exp(-z^2 - 1.26551223 + t*P(t)), t = 1/(1 + z/2); published
+ * fractional error below 1.2e-7 everywhere), evaluated in f32 by Horner with fma, with exp_q.
+ * ---------------------------------------------------------------------------------------- */
+float orc_erfc_q(float z) {
+  float t = 1.0f / (1.0f + 0.5f * z);
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  float arg = fmaf(-z, z, p);
+  return t * orc_exp_q(arg);
+}
+
+void orc_erfc_q_array(const float* z, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_erfc_q(z[i]);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * GLU activations ("Share temporary Q8_1 activation images", Coverage: F32 SwiGLU and
+ * GeGLU-erf producers keep their original formulas). Textbook definitions:
+ *   SwiGLU    : act(g) = g * sigmoid(g) = g / (1 + exp(-g))
+ *   GeGLU-erf : act(g) = g * Phi(g) = 0.5 * g * (1 + erf(g / sqrt 2))
+ * with 1 + erf(z) = erfc(-z) for z < 0 and 2 - erfc(z) for z >= 0. y = act(g) * u.
+ * ---------------------------------------------------------------------------------------- */
+float orc_glu_act(int op, float g) {
+  if (op == 0) {
+    float e = orc_exp_q(-g);
+    float den = 1.0f + e;
+    return g / den;
+  } else {
+    float z = g * (float)M_SQRT1_2;
+    float ope = (z < 0.0f) ? orc_erfc_q(-z) : 2.0f - orc_erfc_q(z);
+    return (0.5f * g) * ope;
+  }
+}
+
+void orc_glu(int op, const float* gate, int64_t ldg, const float* up, int64_t ldu, int rows, int K,
+             float* y, int64_t ldy) {
+  for (int i = 0; i < rows; ++i)
+    for (int k = 0; k < K; ++k) {
+      float act = orc_glu_act(op, gate[(int64_t)i * ldg + k]);
+      y[(int64_t)i * ldy + k] = act * up[(int64_t)i * ldu + k];
+    }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * RMS producer ("Share temporary Q8_1 activation images", Coverage: RMS-alone and RMS+MUL
+ * producers emit the image; original F32 stores remain).
+ *   S = sum x^2 in the fixed order below, mean = S / K, r = 1 / sqrt(mean + eps),
+ *   y = (x * r) * gamma   (gamma absent: y = x * r), each operation one f32 rounding,
+ *   division and square root correctly rounded.
+ * Fixed order of S (the pages only require reduction trees to stay intact, Overview):
+ *   leaf c (c < K/4) = fma(x3,x3, fma(x2,x2, fma(x1,x1, x0*x0))) over x[4c..4c+3];
+ *   lane l in [0,64) owns leaves c = l + 64 j, j < J' (J' = next power of two >= ceil(K/256),
+ *   a missing leaf is +0); each lane sums its J' leaves by a balanced pairwise tree over j;
+ *   the 64 lane sums are combined by a balanced pairwise tree over l.
+ * ---------------------------------------------------------------------------------------- */
+static float pairwise_tree(float* v, int n) { /* n a power of two; v is overwritten */
+  for (int w = n; w > 1; w >>= 1)
+    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  return v[0];
+}
+
+float orc_rms_sumsq(const float* x, int K) {
+  int C = K / 4;
+  int J = (K + 255) / 256;
+  int Jp = 1;
+  while (Jp < J) Jp <<= 1;
+  float lane_sum[64];
+  float* v = (float*)malloc(sizeof(float) * (size_t)Jp);
+  for (int l = 0; l < 64; ++l) {
+    for (int j = 0; j < Jp; ++j) {
+      int c = l + 64 * j;
+      if (c < C) {
+        const float* q = x + 4 * c;
+        v[j] = fmaf(q[3], q[3], fmaf(q[2], q[2], fmaf(q[1], q[1], q[0] * q[0])));
+      } else {
+        v[j] = 0.0f;
+      }
+    }
+    lane_sum[l] = pairwise_tree(v, Jp);
+  }
+  free(v);
+  return pairwise_tree(lane_sum, 64);
+}
+
+void orc_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps, int rows, int K,
+                 float* y, int64_t ldy) {
+  for (int i = 0; i < rows; ++i) {
+    const float* xr = x + (int64_t)i * ldx;
+    float S = orc_rms_sumsq(xr, K);
+    float mean = S / (float)K;
+    float r = 1.0f / sqrtf(mean + eps);
+    for (int k = 0; k < K; ++k) {
+      float t = xr[k] * r;
+      y[(int64_t)i * ldy + k] = gamma ? t * gamma[k] : t;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Q8_1 quantizer, per 32-element block (the block the pages' image carries: int8 codes with a
+ * half scale and a half sum; "Share temporary Q8_1 activation images", GLU producer evidence
+ * validation list; the scale is amax/127 and the sum is d times the sum of the codes):
+ *   amax = max|y|; if amax == 0: all-zero block.
+ *   d = amax / 127, id = 1 / d (if id is not finite: all-zero block),
+ *   c = roundf(y * id)  (round half away from zero),
+ *   d16 = f16(d), s16 = f16((float)(sum c) * d).
+ * Image layout: codes[rows][RB][32] int8, then ds[rows][RB] uint32 (d16 | s16 << 16), with
+ * RB = round_up(K/32, 16); blocks K/32 <= b < RB are zero ([P1] Coverage: image row widths are
+ * whole blocks; the padding is part of the compared image bytes). Returns the number of
+ * non-finite inputs met (the producer's live rows must be finite).
+ * ---------------------------------------------------------------------------------------- */
+int orc_row_blocks(int K) { return ((K / 32 + 15) / 16) * 16; }
+
+int orc_quantize(const float* y, int64_t ldy, int rows, int K, uint8_t* img) {
+  int Kb = K / 32, RB = orc_row_blocks(K);
+  int8_t* codes = (int8_t*)img;
+  uint32_t* ds = (uint32_t*)(img + (size_t)rows * RB * 32);
+  int bad = 0;
+  for (int i = 0; i < rows; ++i) {
+    for (int b = 0; b < RB; ++b) {
+      int8_t* cb = codes + ((size_t)i * RB + b) * 32;
+      uint32_t* db = ds + (size_t)i * RB + b;
+      memset(cb, 0, 32);
+      *db = 0;
+      if (b >= Kb) continue;
+      const float* yb = y + (int64_t)i * ldy + 32 * b;
+      float amax = 0.0f;
+      for (int j = 0; j < 32; ++j) {
+        if (!isfinite(yb[j])) bad++;
+        float a = fabsf(yb[j]);
+        if (a > amax) amax = a;
+      }
+      if (amax == 0.0f) continue;
+      float d = amax / 127.0f;
+      float id = 1.0f / d;
+      if (!isfinite(id)) continue;
+      int sum = 0;
+      for (int j = 0; j < 32; ++j) {
+        int c = (int)roundf(yb[j] * id);
+        if (c > 127 || c < -127) bad++;
+        cb[j] = (int8_t)c;
+        sum += c;
+      }
+      uint16_t d16 = orc_f32_to_f16(d);
+      uint16_t s16 = orc_f32_to_f16((float)sum * d);
+      *db = (uint32_t)d16 | ((uint32_t)s16 << 16);
+    }
+  }
+  return bad;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Readers. Q4_0 weights: qs[N][Kb][16] (byte j: element j low nibble, element j+16 high
+ * nibble), d[N][Kb] f16, weight = d * (nibble - 8). The block integer dot
+ *   sumi = sum_j (qs[j] & 15) * c[j] + (qs[j] >> 4) * c[j+16]
+ * is taken on the raw nibbles; the offset 8 is removed with the image's stored sum s16, which
+ * is why a Q8_1 block carries it:
+ *   out[t][n] = sum_b dw * (d16 * sumi - 8 * s16)     evaluated in float64, ascending b.
+ * ("Share temporary Q8_1 activation images", Coverage: MMVQ readers of the standard Q8_1
+ * activation image; GLU producer evidence: Q4_0 component graphs.)
+ * ---------------------------------------------------------------------------------------- */
+static int32_t block_dot(const uint8_t* qs, const int8_t* c) {
+  int32_t s = 0;
+  for (int j = 0; j < 16; ++j) s += (int32_t)(qs[j] & 15) * c[j] + (int32_t)(qs[j] >> 4) * c[j + 16];
+  return s;
+}
+
+void orc_blockdots(const uint8_t* qs, int N, int K, const uint8_t* img, int img_rows, int rows,
+                   int32_t* sumi) {
+  int Kb = K / 32, RB = orc_row_blocks(K);
+  const int8_t* codes = (const int8_t*)img;
+  (void)img_rows;
+  for (int t = 0; t < rows; ++t)
+    for (int n = 0; n < N; ++n)
+      for (int b = 0; b < Kb; ++b)
+        sumi[((size_t)t * N + n) * Kb + b] =
+            block_dot(qs + ((size_t)n * Kb + b) * 16, codes + ((size_t)t * RB + b) * 32);
+}
+
+static double reader_row(const uint8_t* qs, const uint16_t* d, int Kb, const int8_t* crow,
+                         const uint32_t* dsrow) {
+  double acc = 0.0;
+  for (int b = 0; b < Kb; ++b) {
+    int32_t s = block_dot(qs + (size_t)b * 16, crow + (size_t)b * 32);
+    double dw = orc_f16_to_f64(d[b]);
+    double da = orc_f16_to_f64((uint16_t)(dsrow[b] & 0xffffu));
+    double sa = orc_f16_to_f64((uint16_t)(dsrow[b] >> 16));
+    acc += dw * (da * (double)s - 8.0 * sa);
+  }
+  return acc;
+}
+
+/* Ordinary reader: out[t][n] for t < rows (the live image rows), image of img_rows rows. */
+void orc_mmvq(const uint8_t* qs, const uint16_t* d, int N, int K, const uint8_t* img, int img_rows,
+              int rows, double* out) {
+  int Kb = K / 32, RB = orc_row_blocks(K);
+  const int8_t* codes = (const int8_t*)img;
+  const uint32_t* ds = (const uint32_t*)(img + (size_t)img_rows * RB * 32);
+  for (int t = 0; t < rows; ++t)
+    for (int n = 0; n < N; ++n)
+      out[(size_t)t * N + n] = reader_row(qs + (size_t)n * Kb * 16, d + (size_t)n * Kb, Kb,
+                                          codes + (size_t)t * RB * 32, ds + (size_t)t * RB);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Routed plan ("qwen3_5 CUDA: a captured bucket's padding rows no longer go through the routed
+ * experts", What this changes and Receipt): only the first live rows' pairs p = row*top_k+slot
+ * (row < live) are planned; the sum of the plan items' counts is live*top_k and the largest
+ * member is below that; padding rows get no picks. The plan is a stable counting sort of the
+ * live pairs by expert id: counts[E], offsets[E+1] (exclusive prefix), members grouped by
+ * ascending expert and ascending p within an expert. Pairs naming an expert outside [0, E)
+ * are left out; the function returns how many there were.
+ * ---------------------------------------------------------------------------------------- */
+int orc_plan(const int32_t* ids, int live, int top_k, int E, int32_t* counts, int32_t* offsets,
+             int32_t* members) {
+  int P = live * top_k, bad = 0;
+  if (E <= 0) return P;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int p = 0; p < P; ++p) {
+    int e = ids[p];
+    if (e < 0 || e >= E) bad++;
+    else counts[e]++;
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int p = 0; p < P; ++p) {
+    int e = ids[p];
+    if (e < 0 || e >= E) continue;
+    members[offsets[e] + fill[e]++] = p;
+  }
+  free(fill);
+  return bad;
+}
+
+/* Routed reader: out[p][n] for live pairs p < live*top_k whose expert is in range; expert e's
+ * weights are qs + e*N*Kb*16, d + e*N*Kb; image row = p / top_k. Pairs with a bad expert
+ * are not written. */
+void orc_mmvq_id(const uint8_t* qs, const uint16_t* d, int E, int N, int K, const uint8_t* img,
+                 int img_rows, const int32_t* ids, int live, int top_k, double* out) {
+  int Kb = K / 32, RB = orc_row_blocks(K);
+  const int8_t* codes = (const int8_t*)img;
+  const uint32_t* ds = (const uint32_t*)(img + (size_t)img_rows * RB * 32);
+  for (int p = 0; p < live * top_k; ++p) {
+    int e = ids[p], t = p / top_k;
+    if (e < 0 || e >= E) continue;
+    const uint8_t* qe = qs + (size_t)e * N * Kb * 16;
+    const uint16_t* de = d + (size_t)e * N * Kb;
+    for (int n = 0; n < N; ++n)
+      out[(size_t)p * N + n] = reader_row(qe + (size_t)n * Kb * 16, de + (size_t)n * Kb, Kb,
+                                          codes + (size_t)t * RB * 32, ds + (size_t)t * RB);
+  }
+}

@@ -1,0 +1,218 @@
+"""Python view of the plain CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the benchmark's
+CPU-baseline leg, never by the product package. It shares no code with the HIP library.
+
+Each wrapper names the C function it calls; the definitions and the passages of the pages
+they follow are at those functions in oracle.c.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c99"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (plain gcc; no GPU code)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        sig = {
+            "orc_f32_to_f16": (ctypes.c_uint16, [f32]),
+            "orc_f32_to_f16_array": (None, [P, P, i64]),
+            "orc_f16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
+            "orc_exp_q": (f32, [f32]),
+            "orc_exp_q_array": (None, [P, P, i64]),
+            "orc_erfc_q": (f32, [f32]),
+            "orc_erfc_q_array": (None, [P, P, i64]),
+            "orc_glu_act": (f32, [i32, f32]),
+            "orc_glu": (None, [i32, P, i64, P, i64, i32, i32, P, i64]),
+            "orc_rms_sumsq": (f32, [P, i32]),
+            "orc_rmsnorm": (None, [P, i64, P, f32, i32, i32, P, i64]),
+            "orc_row_blocks": (i32, [i32]),
+            "orc_quantize": (i32, [P, i64, i32, i32, P]),
+            "orc_blockdots": (None, [P, i32, i32, P, i32, i32, P]),
+            "orc_mmvq": (None, [P, P, i32, i32, P, i32, i32, P]),
+            "orc_plan": (i32, [P, i32, i32, i32, P, P, P]),
+            "orc_mmvq_id": (None, [P, P, i32, i32, i32, P, i32, P, i32, i32, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def row_blocks(K: int) -> int:
+    return int(lib().orc_row_blocks(K))
+
+
+def image_bytes(rows: int, K: int) -> int:
+    return rows * row_blocks(K) * 36
+
+
+# ---- scalar / elementwise --------------------------------------------------------------------
+def f32_to_f16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_f32_to_f16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def f16_to_f64(h: int) -> float:
+    return float(lib().orc_f16_to_f64(int(h)))
+
+
+def exp_q(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty_like(x)
+    lib().orc_exp_q_array(_p(x), _p(out), x.size)
+    return out
+
+
+def erfc_q(z) -> np.ndarray:
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    out = np.empty_like(z)
+    lib().orc_erfc_q_array(_p(z), _p(out), z.size)
+    return out
+
+
+# ---- producers -------------------------------------------------------------------------------
+def rms_sumsq(x_row: np.ndarray) -> np.float32:
+    x_row = np.ascontiguousarray(x_row, dtype=np.float32)
+    return np.float32(lib().orc_rms_sumsq(_p(x_row), x_row.shape[0]))
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray | None, eps: float, rows: int | None = None) -> np.ndarray:
+    """orc_rmsnorm over the first `rows` rows of x [R][K]; returns y [rows][K] f32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, K = x.shape
+    rows = R if rows is None else rows
+    y = np.zeros((rows, K), dtype=np.float32)
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
+    lib().orc_rmsnorm(_p(x), K, None if g is None else _p(g), ctypes.c_float(eps), rows, K, _p(y), K)
+    return y
+
+
+GLU_OPS = {"swiglu": 0, "geglu_erf": 1}
+
+
+def glu(gu: np.ndarray, op: str, rows: int | None = None) -> np.ndarray:
+    """orc_glu over packed gate|up rows gu [R][2K] (gate half first); returns y [rows][K]."""
+    gu = np.ascontiguousarray(gu, dtype=np.float32)
+    R, K2 = gu.shape
+    K = K2 // 2
+    rows = R if rows is None else rows
+    y = np.zeros((rows, K), dtype=np.float32)
+    base = gu.ctypes.data
+    lib().orc_glu(GLU_OPS[op], ctypes.c_void_p(base), K2, ctypes.c_void_p(base + 4 * K), K2,
+                  rows, K, _p(y), K)
+    return y
+
+
+# ---- quantizer -------------------------------------------------------------------------------
+def quantize(y: np.ndarray, img_rows: int | None = None) -> np.ndarray:
+    """orc_quantize: Q8_1 image bytes (uint8) of y [rows][K] laid out for img_rows rows.
+
+    Rows of the image beyond y's rows are left zero here (the GPU leaves them unwritten)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    rows, K = y.shape
+    img_rows = rows if img_rows is None else img_rows
+    RB = row_blocks(K)
+    full = np.zeros(img_rows * RB * 36, dtype=np.uint8)
+    part = np.zeros(rows * RB * 36, dtype=np.uint8)
+    bad = lib().orc_quantize(_p(y), K, rows, K, _p(part))
+    if bad:
+        raise ValueError("oracle quantizer met %d non-finite or out-of-range values" % bad)
+    # place the `rows`-row planes into the img_rows-row layout
+    full[: rows * RB * 32] = part[: rows * RB * 32]
+    full[img_rows * RB * 32: img_rows * RB * 32 + rows * RB * 4] = part[rows * RB * 32:]
+    return full
+
+
+def image_planes(img: np.ndarray, img_rows: int, K: int):
+    """Views (codes int8 [rows][RB][32], d16 uint16 [rows][RB], s16 uint16 [rows][RB])."""
+    RB = row_blocks(K)
+    img = np.asarray(img, dtype=np.uint8)
+    codes = img[: img_rows * RB * 32].view(np.int8).reshape(img_rows, RB, 32)
+    ds = img[img_rows * RB * 32: img_rows * RB * 36].view(np.uint32).reshape(img_rows, RB)
+    return codes, (ds & 0xFFFF).astype(np.uint16), (ds >> 16).astype(np.uint16)
+
+
+# ---- readers ---------------------------------------------------------------------------------
+def blockdots(qs: np.ndarray, K: int, img: np.ndarray, img_rows: int, rows: int) -> np.ndarray:
+    """orc_blockdots: sumi [rows][N][Kb] int32."""
+    qs = np.ascontiguousarray(qs, dtype=np.uint8)
+    Kb = K // 32
+    N = qs.size // (Kb * 16)
+    out = np.empty((rows, N, Kb), dtype=np.int32)
+    img = np.ascontiguousarray(img, dtype=np.uint8)
+    lib().orc_blockdots(_p(qs), N, K, _p(img), img_rows, rows, _p(out))
+    return out
+
+
+def mmvq(qs: np.ndarray, d16: np.ndarray, K: int, img: np.ndarray, img_rows: int, rows: int) -> np.ndarray:
+    """orc_mmvq: float64 out [rows][N] of one ordinary Q4_0 reader."""
+    qs = np.ascontiguousarray(qs, dtype=np.uint8)
+    d16 = np.ascontiguousarray(d16, dtype=np.uint16)
+    Kb = K // 32
+    N = qs.size // (Kb * 16)
+    out = np.empty((rows, N), dtype=np.float64)
+    img = np.ascontiguousarray(img, dtype=np.uint8)
+    lib().orc_mmvq(_p(qs), _p(d16), N, K, _p(img), img_rows, rows, _p(out))
+    return out
+
+
+def plan(ids: np.ndarray, live: int, E: int):
+    """orc_plan: (counts[E], offsets[E+1], members[valid pairs], n_bad)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    top_k = ids.shape[1]
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    members = np.full(max(live * top_k, 1), -1, dtype=np.int32)
+    bad = lib().orc_plan(_p(ids), live, top_k, E, _p(counts), _p(offsets), _p(members))
+    return counts, offsets, members[: offsets[E]].copy(), int(bad)
+
+
+def mmvq_id(qs: np.ndarray, d16: np.ndarray, E: int, K: int, img: np.ndarray, img_rows: int,
+            ids: np.ndarray, live: int) -> np.ndarray:
+    """orc_mmvq_id: float64 out [live*top_k][N]; pairs with a bad expert stay NaN."""
+    qs = np.ascontiguousarray(qs, dtype=np.uint8)
+    d16 = np.ascontiguousarray(d16, dtype=np.uint16)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    top_k = ids.shape[1]
+    Kb = K // 32
+    N = qs.size // (E * Kb * 16)
+    out = np.full((live * top_k, N), np.nan, dtype=np.float64)
+    img = np.ascontiguousarray(img, dtype=np.uint8)
+    lib().orc_mmvq_id(_p(qs), _p(d16), E, N, K, _p(img), img_rows, _p(ids), live, top_k, _p(out))
+    return out

@@ -1,0 +1,181 @@
+"""Pins of the oracle's readers and routed plan (CPU only).
+
+block dot    -> brute force over an explicitly unpacked weight vector; closed-form nibbles
+reader (f64) -> brute-force float64 dequantize-and-dot, which differs from the Q8_1 form by
+                a known closed form (the image stores s in fp16)
+accuracy     -> NMSE against the unquantized float64 activation <= 5e-4, the CPU bound of
+                "Share temporary Q8_1 activation images", GLU producer evidence
+plan         -> brute-force sort of the live pairs; the receipt counts of the padded-bucket page
+routed       -> reduces to the ordinary reader with the pair's expert and image row
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from q8_activation_quant_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _unpack_weights(qs):
+    """Element j of a block: low nibble of byte j (j < 16), high nibble of byte j-16."""
+    lo = (qs & 15).astype(np.int64)
+    hi = (qs >> 4).astype(np.int64)
+    return np.concatenate([lo, hi], axis=-1)  # [..., 32]
+
+
+def _f16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _random_image(g, rows, K):
+    y = g.standard_normal((rows, K)).astype(np.float32)
+    return y, O.quantize(y)
+
+
+def test_blockdots_brute_force():
+    g = np.random.default_rng(0)
+    K, N, T = 96, 5, 3
+    w = W.q4_0_weights(g, (N,), K)
+    y, img = _random_image(g, T, K)
+    sumi = O.blockdots(w.qs, K, img, T, T)
+    codes, _, _ = O.image_planes(img, T, K)
+    wq = _unpack_weights(w.qs)  # [N][Kb][32]
+    ref = np.einsum("nbj,tbj->tnb", wq, codes[:, : K // 32].astype(np.int64))
+    assert np.array_equal(sumi, ref)
+    assert np.abs(sumi).max() <= 15 * 127 * 32
+
+
+@pytest.mark.parametrize("byte,expect", [(0x00, "zero"), (0xFF, "all15"), (0x0F, "lo15"), (0xF0, "hi15")])
+def test_blockdots_closed_form_nibbles(byte, expect):
+    g = np.random.default_rng(1)
+    K = 32
+    y, img = _random_image(g, 1, K)
+    codes, _, _ = O.image_planes(img, 1, K)
+    c = codes[0, 0].astype(np.int64)
+    qs = np.full((1, 1, 16), byte, np.uint8)
+    s = int(O.blockdots(qs, K, img, 1, 1)[0, 0, 0])
+    want = {"zero": 0, "all15": 15 * c.sum(), "lo15": 15 * c[:16].sum(), "hi15": 15 * c[16:].sum()}[expect]
+    assert s == want
+
+
+def test_reader_matches_bruteforce_dequantize_and_dot():
+    g = np.random.default_rng(2)
+    for K, N, T in [(32, 3, 1), (64, 4, 2), (2592, 3, 2)]:
+        w = W.q4_0_weights(g, (N,), K)
+        y, img = _random_image(g, T, K)
+        out = O.mmvq(w.qs, w.d, K, img, T, T)
+        Kb = K // 32
+        codes, d16, s16 = O.image_planes(img, T, K)
+        wq = _unpack_weights(w.qs).astype(np.float64) - 8.0      # [N][Kb][32]
+        wd = wq * _f16(w.d)[..., None]                            # dequantized weights
+        ad = codes[:, :Kb].astype(np.float64) * _f16(d16[:, :Kb])[..., None]  # dequantized act
+        bf = np.einsum("nbj,tbj->tn", wd, ad)
+        # the Q8_1 form subtracts 8*d_w*s16 where the dequantized form subtracts
+        # 8*d_w*d16*sum(c): o - bf = sum_b 8 d_w (d16 sum(c) - s16)
+        diff = np.einsum("nb,tb->tn", _f16(w.d),
+                         8.0 * (_f16(d16[:, :Kb]) * codes[:, :Kb].astype(np.float64).sum(-1) - _f16(s16[:, :Kb])))
+        scale = np.einsum("nbj,tbj->tn", np.abs(wd), np.abs(ad)) + np.abs(diff) + 1e-300
+        assert (np.abs(out - bf - diff) <= 1e-12 * scale).all()
+
+
+def test_all_eight_weight_block_shows_the_stored_sum():
+    # every nibble 8 -> dequantized weight 0, so the dequantized dot is 0 and the Q8_1 form
+    # returns exactly sum_b d_w * 8 * (d16*sum(c) - s16)
+    g = np.random.default_rng(3)
+    K = 256
+    y, img = _random_image(g, 1, K)
+    qs = np.full((1, K // 32, 16), 0x88, np.uint8)
+    d = np.full((1, K // 32), np.float16(0.5).view(np.uint16), np.uint16)
+    out = O.mmvq(qs, d, K, img, 1, 1)[0, 0]
+    codes, d16, s16 = O.image_planes(img, 1, K)
+    Kb = K // 32
+    expect = np.sum(0.5 * 8.0 * (_f16(d16[0, :Kb]) * codes[0, :Kb].sum(-1) - _f16(s16[0, :Kb])))
+    assert abs(out - expect) <= 1e-15 * (np.abs(_f16(s16)).sum() * 4 + 1e-300)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4])
+def test_nmse_against_unquantized_float64(config):
+    wl = W.make(config, small=True)
+    K = wl.K
+    if wl.producer == "rmsnorm":
+        y = O.rmsnorm(wl.x, wl.gamma, W.EPS)
+        x64 = wl.x.astype(np.float64)
+        y64 = x64 / np.sqrt(np.mean(x64 ** 2, axis=1, keepdims=True) + W.EPS) * wl.gamma.astype(np.float64)
+    else:
+        import scipy.special
+        y = O.glu(wl.gu, wl.producer)
+        g64, u64 = wl.gu[:, :K].astype(np.float64), wl.gu[:, K:].astype(np.float64)
+        y64 = g64 / (1 + np.exp(-g64)) * u64
+    img = O.quantize(y)
+    T = y.shape[0]
+    for r in wl.readers:
+        qs = r.qs.reshape(-1, K // 32, 16)[:64]
+        d = r.d.reshape(-1, K // 32)[:64]
+        out = O.mmvq(qs, d, K, img, T, T)
+        wd = (_unpack_weights(qs).astype(np.float64) - 8.0) * _f16(d)[..., None]
+        ref = y64 @ wd.reshape(wd.shape[0], -1).T  # unquantized activation, same weights
+        nmse = np.sum((out - ref) ** 2) / np.sum(ref ** 2)
+        assert nmse <= 5e-4, nmse
+
+
+def _read_receipt():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "routed_plan_receipt.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append([int(v) for v in line.split()])
+    return rows
+
+
+@pytest.mark.parametrize("bucket,live,top_k,pairs,largest", _read_receipt())
+def test_plan_receipt_counts(bucket, live, top_k, pairs, largest):
+    E = 256
+    g = np.random.default_rng(bucket * 1000 + live)
+    ids, _ = W.topk_ids(g, bucket, E, top_k)
+    counts, offsets, members, bad = O.plan(ids, live, E)
+    assert bad == 0 and counts.sum() == pairs and offsets[E] == pairs
+    assert members.max() == largest and len(members) == pairs
+
+
+def test_plan_against_brute_force_sort():
+    g = np.random.default_rng(4)
+    for bucket, k, E in [(128, 9, 256), (8, 8, 128), (5, 3, 4), (1, 1, 1)]:
+        ids, _ = W.topk_ids(g, bucket, E, k) if k <= E else (None, None)
+        for live in sorted({0, 1, bucket // 2, bucket}):
+            counts, offsets, members, bad = O.plan(ids, live, E)
+            P = live * k
+            flat = ids.reshape(-1)[:P]
+            ref = [p for _, p in sorted((int(flat[p]), p) for p in range(P))]
+            assert members.tolist() == ref
+            assert np.array_equal(counts, np.bincount(flat, minlength=E))
+            assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+            assert sorted(members.tolist()) == list(range(P))
+
+
+def test_plan_skips_out_of_range_experts():
+    ids = np.array([[0, 5], [9, 1], [-1, 2]], np.int32)
+    counts, offsets, members, bad = O.plan(ids, 3, 6)
+    assert bad == 2
+    assert members.tolist() == [0, 3, 5, 1]  # experts 0, 1, 2, 5
+    assert offsets[6] == 4
+
+
+def test_routed_reduces_to_ordinary_reader():
+    g = np.random.default_rng(5)
+    E, N, K, B, k, live = 6, 3, 64, 4, 2, 3
+    w = W.q4_0_weights(g, (E, N), K)
+    ids, _ = W.topk_ids(g, B, E, k)
+    y, img = _random_image(g, B, K)
+    out = O.mmvq_id(w.qs, w.d, E, K, img, B, ids, live)
+    codes, d16, s16 = O.image_planes(img, B, K)
+    Kb = K // 32
+    for p in range(live * k):
+        t, e = p // k, ids.reshape(-1)[p]
+        wd = (_unpack_weights(w.qs[e]).astype(np.float64) - 8.0) * _f16(w.d[e])[..., None]
+        ad = codes[t, :Kb].astype(np.float64) * _f16(d16[t, :Kb])[..., None]
+        diff = 8.0 * (_f16(d16[t, :Kb]) * codes[t, :Kb].sum(-1) - _f16(s16[t, :Kb]))
+        ref = np.einsum("nbj,bj->n", wd, ad) + _f16(w.d[e]) @ diff
+        assert np.allclose(out[p], ref, rtol=1e-12, atol=1e-14)
