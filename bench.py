@@ -1,0 +1,335 @@
+"""Benchmark of the shared Q8_1 activation-image path on one MI355X.
+
+A step is one component graph: the fused producer writes the f32 output and the Q8_1 image,
+then the Q4_0 readers consume the image. Default workload: T=8 tokens, K=8192, RMSNorm x gamma,
+three readers N=8192/1024/1024 (the ordinary K8192/T8 component graph).
+
+Timing: a HIP graph holds R instances of the step, each with its own copy of every tensor,
+with R x weights >= 1 GiB so replays stream weights from HBM rather than from the 256 MB
+Infinity Cache. W warmup steps, then exactly K timed steps, bracketed by synchronisation.
+The reader kernel is also timed alone (a graph of R reader launches) for the roofline line.
+The CPU baseline is the plain oracle on the host, single-threaded, on a bounded sample.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+ROT_BYTES = 1 << 30
+
+
+def _t():
+    import torch
+    return torch
+
+
+class Instance:
+    """Device tensors of one copy of a workload's component graph."""
+
+    def __init__(self, wl, host_dev_cache=None):
+        from q8_activation_quant_amd import qimg
+        torch = _t()
+        self.wl = wl
+        T, K = wl.T, wl.K
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+        if wl.producer == "rmsnorm":
+            self.x = dev(wl.x)
+            self.gamma = dev(wl.gamma)
+        else:
+            self.gu = dev(wl.gu)
+        self.y = torch.empty(T, K, dtype=torch.float32, device="cuda")
+        self.img = torch.empty(qimg.image_bytes(T, K), dtype=torch.uint8, device="cuda")
+        self.live = torch.tensor([wl.live if wl.live is not None else T], dtype=torch.int32, device="cuda")
+        self.specs = []
+        for r in wl.readers:
+            N = r.d.shape[-2]
+            out = torch.empty(*((T, wl.top_k, N) if wl.routed else (T, N)), dtype=torch.float32, device="cuda")
+            self.specs.append((dev(r.qs), dev(r.d), out))
+        if wl.routed:
+            self.ids = dev(wl.ids)
+            self.ws = torch.empty(qimg.workspace_bytes(T, wl.top_k, wl.E) // 4, dtype=torch.int32, device="cuda")
+
+    def produce(self, with_img=True):
+        from q8_activation_quant_amd import qimg
+        wl = self.wl
+        img = self.img if with_img else None
+        live = self.live if wl.routed or wl.live is not None else None
+        if wl.producer == "rmsnorm":
+            qimg.emit_rmsnorm(self.x, self.gamma, 1e-6, self.y, img, live)
+        else:
+            K = wl.K
+            qimg.emit_glu(wl.producer, self.gu[:, :K], self.gu[:, K:], self.y, img, live)
+
+    def quantize(self):
+        from q8_activation_quant_amd import qimg
+        live = self.live if self.wl.routed or self.wl.live is not None else None
+        qimg.quantize_q8_1(self.y, self.img, live)
+
+    def read(self):
+        from q8_activation_quant_amd import qimg
+        wl = self.wl
+        if wl.routed:
+            qimg.mmvq_id(self.specs, wl.E, self.img, self.ids, self.live, wl.K, self.ws)
+        else:
+            qimg.mmvq(self.specs, self.img, wl.T, wl.K)
+
+    def step(self, arm="fused"):
+        if arm == "fused":
+            self.produce(True)
+        else:  # control: producer keeps only f32, then the separate quantizer launch
+            self.produce(False)
+            self.quantize()
+        self.read()
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move per component graph: producer inputs read, f32 output
+    written, image written once and read once, the distinct weights read once (routed: only
+    the experts some live pair selects), ids read, outputs written."""
+    from q8_activation_quant_amd import qimg
+    T, K = wl.T, wl.K
+    L = wl.live if wl.live is not None else T
+    Kb = K // 32
+    prod = (2 * L * K * 4) if wl.producer != "rmsnorm" else (L * K * 4 + K * 4)
+    prod += L * K * 4                      # f32 output
+    img = L * Kb * 36                      # image bytes written (= read) for live rows
+    if wl.routed:
+        used = np.unique(wl.ids[:L].reshape(-1))
+        w = sum(len(used) * r.d.shape[-2] * Kb * 18 for r in wl.readers)
+        out = sum(L * wl.top_k * r.d.shape[-2] * 4 for r in wl.readers)
+        ids = L * wl.top_k * 4
+    else:
+        w = sum(r.d.shape[-2] * Kb * 18 for r in wl.readers)
+        out = sum(L * r.d.shape[-2] * 4 for r in wl.readers)
+        ids = 0
+    return {"producer": prod, "image_write": img, "image_read": img, "weights": w, "outputs": out,
+            "ids": ids, "total": prod + 2 * img + w + out + ids,
+            "reader_kernel": img + w + out + ids}
+
+
+def weight_bytes(wl):
+    return sum(r.qs.nbytes + r.d.nbytes for r in wl.readers)
+
+
+def make_instances(wl, rot_bytes=ROT_BYTES):
+    R = max(1, int(np.ceil(rot_bytes / max(weight_bytes(wl), 1))))
+    return [Instance(wl) for _ in range(R)]
+
+
+def time_graph(fns, steps, warmup, runs=3):
+    """Capture fns (one call per instance) in one graph; replay to cover `warmup` then exactly
+    `steps` calls (a remainder graph covers steps not divisible by the instance count).
+    Returns the per-call microseconds of each run."""
+    torch = _t()
+    R = len(fns)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    rem = steps % R
+    g_rem = None
+    if rem:
+        g_rem = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_rem):
+            for f in fns[:rem]:
+                f()
+    for _ in range(max(1, int(np.ceil(warmup / R)))):
+        g.replay()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(runs):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps // R):
+            g.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) * 1e3 / steps)
+    return res
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """The plain oracle (single thread) over the same component graph; returns us per graph."""
+    from oracle import oracle as O
+    T, K = wl.T, wl.K
+    L = wl.live if wl.live is not None else T
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        if wl.producer == "rmsnorm":
+            y = O.rmsnorm(wl.x[:L], wl.gamma, 1e-6)
+        else:
+            y = O.glu(wl.gu[:L], wl.producer)
+        img = O.quantize(y, img_rows=T)
+        for r in wl.readers:
+            if wl.routed:
+                O.plan(wl.ids, L, wl.E)
+                O.mmvq_id(r.qs, r.d, wl.E, K, img, T, wl.ids, L)
+            else:
+                O.mmvq(r.qs, r.d, K, img, T, L)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() + times[-1] > t_end or len(times) >= 5:
+            break
+    return float(np.median(times)) * 1e6, len(times)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "q8_activation_quant_amd", "csrc", "qimg.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kind):
+    """HBM bytes per reader launch from the committed rocprofv3 --pmc summary, or None when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "mmvq_k8192_t8_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get(kind)
+
+
+WORKLOAD_NAMES = {
+    1: "tiny ordinary: T1 K2560 RMSNorm x gamma -> Q8_1 image -> 2 Q4_0 readers N2560",
+    2: "ordinary K8192/T8: RMSNorm x gamma -> Q8_1 image -> 3 Q4_0 readers N8192/1024/1024",
+    3: "GLU T8: SwiGLU over packed gate|up [8, 2x14336] -> Q8_1 image -> Q4_0 down reader N4096",
+    4: "routed T8 K2560 E128 top8: RMSNorm x gamma -> image -> gate+up Q4_0 experts [128,768,2560]",
+    5: "padded bucket 128 K2048 E256 top9: RMSNorm x gamma -> image -> Q4_0 experts [256,512,2048]",
+}
+
+
+def run(config, steps, warmup, live=None, glu_op="swiglu", want_cpu=True, arms=("fused", "control")):
+    torch = _t()
+    from q8_activation_quant_amd import workloads as W
+    wl = W.make(config, live=live, glu_op=glu_op)
+    insts = make_instances(wl)
+    nb = algorithmic_bytes(wl)
+    per_arm = {}
+    # ABBA over the two arms
+    order = list(arms) + list(reversed(arms)) if len(arms) > 1 else list(arms)
+    for arm in order:
+        us = time_graph([(lambda i=i, a=arm: i.step(a)) for i in insts], steps, warmup)
+        per_arm.setdefault(arm, []).extend(us)
+    kern = time_graph([i.read for i in insts], steps, warmup)
+    prod = time_graph([(lambda i=i: i.produce(True)) for i in insts], steps, warmup)
+    res = {
+        "wl": wl, "R": len(insts), "bytes": nb,
+        "us": {a: float(np.median(v)) for a, v in per_arm.items()},
+        "us_range": {a: [float(min(v)), float(max(v))] for a, v in per_arm.items()},
+        "reader_us": float(np.median(kern)), "producer_us": float(np.median(prod)),
+    }
+    if want_cpu:
+        res["cpu_us"], res["cpu_reps"] = cpu_baseline(wl)
+    del insts
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4600)
+    ap.add_argument("--warmup", type=int, default=460)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--live", type=int, default=None)
+    ap.add_argument("--glu", default="swiglu", choices=["swiglu", "geglu_erf"])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also print one extra line per workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see the design notes "
+              "for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    torch = _t()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from q8_activation_quant_amd import qimg
+    qimg.lib()
+
+    r = run(args.config, args.steps, args.warmup, live=args.live, glu_op=args.glu, want_cpu=not args.no_cpu)
+    wl, nb = r["wl"], r["bytes"]
+    us = r["us"]["fused"]
+    reader_gbs = nb["reader_kernel"] / (r["reader_us"] * 1e-6) / 1e9
+    traffic = pmc_traffic("hbm_bytes_per_launch")
+    line = {
+        "metric": "us per component graph + achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": round(us, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xu4->int32 dots, f32 producer and accumulation",
+        "data": "synthetic (seeded numpy PCG64; shapes/distributions of the workload)",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "T": wl.T, "K": wl.K,
+                   "readers_N": wl.reader_rows, "producer": wl.producer, "arm": "fused",
+                   "graph_instances": r["R"], "live_rows": wl.live},
+        "achieved_GBs": round(nb["total"] / (us * 1e-6) / 1e9, 1),
+        "pct_of_hbm_peak": round(100 * nb["total"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+        "algorithmic_bytes": nb["total"],
+        "control_us": round(r["us"].get("control", float("nan")), 3),
+        "less_gpu_time_vs_control_pct": round(100 * (1 - us / r["us"]["control"]), 2) if "control" in r["us"] else None,
+        "us_range": r["us_range"],
+        "producer_us": round(r["producer_us"], 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mmvq_kernel (Q4_0 x Q8_1 readers)",
+            "achieved": round(reader_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(reader_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": nb["reader_kernel"],
+            "avg_launch_us": round(r["reader_us"], 3),
+        },
+    }
+    if "cpu_us" in r:
+        line["cpu_baseline"] = {"value": round(r["cpu_us"], 1), "unit": "us", "cores": 1, "kind": "oracle",
+                                "sample": "%d full component graph(s) of the same workload (median)" % r["cpu_reps"]}
+    print(json.dumps(line), flush=True)
+    if args.all:
+        for c, live in [(1, None), (3, None), (4, None), (5, 1), (5, 9), (5, 113), (5, 114), (5, 128)]:
+            rr = run(c, args.steps, args.warmup, live=live, want_cpu=False)
+            nb2 = rr["bytes"]
+            u2 = rr["us"]["fused"]
+            print(json.dumps({"workload": WORKLOAD_NAMES[c], "live": live, "fused_us": round(u2, 3),
+                              "control_us": round(rr["us"]["control"], 3),
+                              "reader_us": round(rr["reader_us"], 3), "producer_us": round(rr["producer_us"], 3),
+                              "algorithmic_bytes": nb2["total"],
+                              "GBs": round(nb2["total"] / (u2 * 1e-6) / 1e9, 1),
+                              "pct_hbm": round(100 * nb2["total"] / (u2 * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+                              "reader_GBs": round(nb2["reader_kernel"] / (rr["reader_us"] * 1e-6) / 1e9, 1)}),
+                  flush=True)
+
+
+if __name__ == "__main__":
+    main()

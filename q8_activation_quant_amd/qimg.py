@@ -1,0 +1,174 @@
+"""Python binding of libqimg.so (the C ABI declared in include/qimg.h).
+
+Argument marshalling only: tensors are passed as device pointers with their strides, and the
+stream is torch's current HIP stream. Every step of the path runs in the library's kernels.
+The library must be built (``python -m q8_activation_quant_amd.build`` or
+``__graft_entry__.build()``); there is no fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqimg.so")
+
+OK, EINVAL, EALIGN, EALIAS, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+GLU_SWIGLU, GLU_GEGLU_ERF = 0, 1
+GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF}
+ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
+MAX_READERS = 8
+ABI_VERSION = 1
+
+EXPORTS = (
+    "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
+    "qimg_emit_rmsnorm", "qimg_emit_glu", "qimg_quantize_q8_1", "mmvq_q4_0_q8_1",
+    "mmvq_id_workspace_bytes", "mmvq_id_q4_0_q8_1", "mmvq_q4_0_q8_1_blockdots",
+)
+
+
+class QimgError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, strerror(status), status))
+
+
+class Reader(ctypes.Structure):
+    _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("N", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64)]
+
+
+class ExpertReader(ctypes.Structure):
+    _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("N", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("out", ctypes.c_void_p), ("ld_pair", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqimg.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqimg.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        sig = {
+            "qimg_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "qimg_abi_version": (ctypes.c_int, []),
+            "qimg_row_blocks": (i32, [i32]),
+            "qimg_image_bytes": (i64, [i32, i32]),
+            "qimg_emit_rmsnorm": (ctypes.c_int, [P, i64, P, f32, i32, P, i32, P, i64, P, P]),
+            "qimg_emit_glu": (ctypes.c_int, [i32, P, i64, P, i64, i32, P, i32, P, i64, P, P]),
+            "qimg_quantize_q8_1": (ctypes.c_int, [P, i64, i32, P, i32, P, P]),
+            "mmvq_q4_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
+            "mmvq_id_workspace_bytes": (ctypes.c_size_t, [i32, i32, i32]),
+            "mmvq_id_q4_0_q8_1": (ctypes.c_int, [ctypes.POINTER(ExpertReader), i32, i32, P, P, i32,
+                                                 i32, P, i32, P, ctypes.c_size_t, P]),
+            "mmvq_q4_0_q8_1_blockdots": (ctypes.c_int, [ctypes.POINTER(Reader), P, i32, i32, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.qimg_abi_version() != ABI_VERSION:
+            raise RuntimeError("libqimg.so ABI %d, binding expects %d" % (L.qimg_abi_version(), ABI_VERSION))
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().qimg_strerror(status).decode()
+
+
+def _check(status: int, fn: str) -> None:
+    if status != OK:
+        raise QimgError(status, fn)
+
+
+def row_blocks(K: int) -> int:
+    return int(lib().qimg_row_blocks(K))
+
+
+def image_bytes(rows: int, K: int) -> int:
+    return int(lib().qimg_image_bytes(rows, K))
+
+
+def workspace_bytes(bucket: int, top_k: int, E: int) -> int:
+    return int(lib().mmvq_id_workspace_bytes(bucket, top_k, E))
+
+
+# ---- torch marshalling --------------------------------------------------------------------
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ld(t):
+    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+
+
+def emit_rmsnorm(x, gamma, eps, y, img=None, live_rows=None, stream=None):
+    """y = rmsnorm(x) * gamma (gamma may be None); img (uint8) receives the Q8_1 image."""
+    rows, K = x.shape
+    _check(lib().qimg_emit_rmsnorm(_ptr(x), _ld(x), _ptr(gamma), ctypes.c_float(eps), rows,
+                                   _ptr(live_rows), K, _ptr(y), _ld(y), _ptr(img), _stream(stream)),
+           "qimg_emit_rmsnorm")
+
+
+def emit_glu(op, gate, up, y, img=None, live_rows=None, stream=None):
+    """y = act(gate) * up; gate/up may be the halves of one packed [rows, 2K] tensor."""
+    op = GLU_OPS[op] if isinstance(op, str) else op
+    rows, K = gate.shape
+    _check(lib().qimg_emit_glu(op, _ptr(gate), _ld(gate), _ptr(up), _ld(up), rows, _ptr(live_rows),
+                               K, _ptr(y), _ld(y), _ptr(img), _stream(stream)), "qimg_emit_glu")
+
+
+def quantize_q8_1(y, img, live_rows=None, stream=None):
+    rows, K = y.shape
+    _check(lib().qimg_quantize_q8_1(_ptr(y), _ld(y), rows, _ptr(live_rows), K, _ptr(img),
+                                    _stream(stream)), "qimg_quantize_q8_1")
+
+
+def _readers(specs, cls):
+    arr = (cls * len(specs))()
+    for i, (qs, d, out) in enumerate(specs):
+        N = qs.shape[-3]
+        arr[i] = cls(ctypes.c_void_p(qs.data_ptr()), ctypes.c_void_p(d.data_ptr()), N, 0,
+                     ctypes.c_void_p(out.data_ptr()), out.stride(-2))
+    return arr
+
+
+def mmvq(readers, img, rows, K, live_rows=None, stream=None):
+    """Ordinary readers: readers = [(qs [N,K/32,16] u8, d [N,K/32] fp16 bits, out [rows,N] f32)]."""
+    arr = _readers(readers, Reader)
+    _check(lib().mmvq_q4_0_q8_1(arr, len(readers), _ptr(img), rows, _ptr(live_rows), K,
+                                _stream(stream)), "mmvq_q4_0_q8_1")
+
+
+def mmvq_id(readers, E, img, ids, live_rows, K, workspace, stream=None):
+    """Routed readers: readers = [(qs [E,N,K/32,16], d [E,N,K/32], out [bucket,top_k,N])];
+    ids [bucket, top_k] int32; live_rows: int32 device tensor of one element, or None."""
+    bucket, top_k = ids.shape
+    arr = _readers(readers, ExpertReader)
+    _check(lib().mmvq_id_q4_0_q8_1(arr, len(readers), E, _ptr(img), _ptr(ids), bucket, top_k,
+                                   _ptr(live_rows), K, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "mmvq_id_q4_0_q8_1")
+
+
+def blockdots(qs, d, img, rows, K, sumi, stream=None):
+    """sumi [rows, N, K/32] int32 of one ordinary reader (debug export)."""
+    N = qs.shape[0]
+    r = Reader(ctypes.c_void_p(qs.data_ptr()), ctypes.c_void_p(d.data_ptr()), N, 0,
+               ctypes.c_void_p(sumi.data_ptr()), N)
+    _check(lib().mmvq_q4_0_q8_1_blockdots(ctypes.byref(r), _ptr(img), rows, K, _ptr(sumi),
+                                          _stream(stream)), "mmvq_q4_0_q8_1_blockdots")

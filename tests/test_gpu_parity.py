@@ -1,0 +1,425 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Bars: f32 producer outputs, Q8_1 image bytes (codes, half scales/sums, padding), per-block
+int32 dots and routed plans bit-exact; reader outputs within normwise relative error 1e-5 of
+the float64 oracle and within the per-element rounding bound; NMSE against the unquantized
+float64 activation <= 5e-4. Rows past the live count are never written (sentinel bytes stay).
+"""
+import numpy as np
+import pytest
+
+import helpers as H
+from oracle import oracle as O
+from q8_activation_quant_amd import qimg
+from q8_activation_quant_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = H.torch()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qimg.lib()  # raises when the HIP library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def sync():
+    H.torch().cuda.synchronize()
+
+
+def split_image(img, rows, K):
+    RB = qimg.row_blocks(K)
+    return img[: rows * RB * 32].reshape(rows, RB * 32), img[rows * RB * 32: rows * RB * 36].reshape(rows, RB * 4)
+
+
+def run_producer(wl, live=None, with_img=True, pass_live=False, x=None, gu=None):
+    """Run the fused producer on sentinel-filled outputs; returns host (y, img)."""
+    T, K = wl.T, wl.K
+    y = H.sentinel_f32(T, K)
+    img = H.sentinel_u8(qimg.image_bytes(T, K)) if with_img else None
+    lt = H.live_tensor(live) if (pass_live or live is not None) else None
+    if wl.producer == "rmsnorm":
+        xd = H.dev(wl.x if x is None else x)
+        qimg.emit_rmsnorm(xd, H.dev(wl.gamma), W.EPS, y, img, lt)
+    else:
+        gd = H.dev(wl.gu if gu is None else gu)
+        qimg.emit_glu(wl.producer, gd[:, :K], gd[:, K:], y, img, lt)
+    sync()
+    return H.host(y), (None if img is None else H.host(img))
+
+
+def check_producer(wl, y, img, live=None):
+    live = wl.T if live is None else live
+    y_o, img_o = H.oracle_producer(wl, live)
+    assert np.array_equal(y[:live].view(np.uint32), y_o.view(np.uint32)), "f32 producer output differs"
+    assert (y[live:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding rows of y were written"
+    if img is not None:
+        c, d = split_image(img, wl.T, wl.K)
+        co, do = split_image(img_o, wl.T, wl.K)
+        assert np.array_equal(c[:live], co[:live]), "image codes differ"
+        assert np.array_equal(d[:live], do[:live]), "image scales/sums differ"
+        assert (c[live:] == H.SENTINEL_BYTE).all() and (d[live:] == H.SENTINEL_BYTE).all(), \
+            "padding rows of the image were written"
+    return y_o, img_o
+
+
+# ---- producers ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("config", [1, 2, 4])
+def test_emit_rmsnorm_bit_exact(config):
+    wl = W.make(config, small=True)
+    print("emit_rmsnorm config", config, flush=True)
+    y, img = run_producer(wl)
+    check_producer(wl, y, img)
+
+
+@pytest.mark.parametrize("op", ["swiglu", "geglu_erf"])
+def test_emit_glu_bit_exact(op):
+    wl = W.make(3, glu_op=op, small=True)
+    print("emit_glu", op, flush=True)
+    y, img = run_producer(wl)
+    check_producer(wl, y, img)
+
+
+@pytest.mark.parametrize("op", ["swiglu", "geglu_erf"])
+def test_emit_glu_extreme_gates_bit_exact(op):
+    # gates over the saturation paths of exp/erfc: far negative, large positive, zero, tiny
+    K = 2048
+    g = np.random.default_rng(11)
+    gate = np.concatenate([np.linspace(-120, 120, K // 2), g.standard_normal(K // 2) * 30]).astype(np.float32)
+    gate[:8] = [0.0, -0.0, 1e-30, -1e-30, 88.7, -88.7, 87.0, -87.0]
+    gu = np.stack([np.concatenate([gate, g.standard_normal(K).astype(np.float32)]),
+                   np.concatenate([-gate, np.ones(K, np.float32)])])
+    wl = W.Workload(0, "extreme", 2, K, op, gu=gu)
+    y, img = run_producer(wl)
+    check_producer(wl, y, img)
+
+
+@pytest.mark.parametrize("K", [32, 256, 2592, 14336, 32768])
+def test_emit_rmsnorm_shapes(K):
+    g = np.random.default_rng(K)
+    x = (g.standard_normal((3, K)) * np.array([1.0, 1e3, 1e-3])[:, None]).astype(np.float32)
+    wl = W.Workload(0, "K%d" % K, 3, K, "rmsnorm", x=x, gamma=g.normal(1, 0.1, K).astype(np.float32))
+    y, img = run_producer(wl)
+    check_producer(wl, y, img)
+
+
+def test_emit_rmsnorm_without_gamma_and_zero_row():
+    K = 2560
+    x = np.random.default_rng(3).standard_normal((2, K)).astype(np.float32)
+    x[1] = 0
+    T = H.torch()
+    y = H.sentinel_f32(2, K)
+    img = H.sentinel_u8(qimg.image_bytes(2, K))
+    qimg.emit_rmsnorm(H.dev(x), None, W.EPS, y, img)
+    sync()
+    y_o = O.rmsnorm(x, None, W.EPS)
+    assert np.array_equal(H.host(y).view(np.uint32), y_o.view(np.uint32))
+    assert np.array_equal(H.host(img), O.quantize(y_o))
+    assert not H.host(img)[: 2 * qimg.row_blocks(K) * 36].reshape(-1)[qimg.row_blocks(K) * 32: 2 * qimg.row_blocks(K) * 32].any()
+
+
+def test_fused_image_equals_separate_quantizer():
+    # the emitted image must be the bytes of the original separate quantizer applied to the
+    # stored f32 output (control arm == candidate arm)
+    for config in (2, 3):
+        wl = W.make(config, small=True)
+        y, img = run_producer(wl)
+        y_only, none = run_producer(wl, with_img=False)
+        assert none is None and np.array_equal(y.view(np.uint32), y_only.view(np.uint32))
+        img2 = H.sentinel_u8(qimg.image_bytes(wl.T, wl.K))
+        qimg.quantize_q8_1(H.dev(y_only), img2)
+        sync()
+        assert np.array_equal(H.host(img2), img)
+
+
+def test_quantizer_golden_and_special_blocks():
+    K = 64
+    y = np.zeros((3, K), np.float32)
+    y[0, :6] = [127, 2.5, -2.5, 0.5, -0.5, 1.5]           # ties: half away from zero
+    y[1, :32] = np.arange(-16, 16) / 8.0                   # exact multiples of d
+    y[1, 0] = -127 / 8.0
+    y[2, 32:] = 1e-38                                      # 1/d overflows: zero block
+    img = H.sentinel_u8(qimg.image_bytes(3, K))
+    qimg.quantize_q8_1(H.dev(y), img)
+    sync()
+    assert np.array_equal(H.host(img), O.quantize(y))
+
+
+# ---- block dots ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("K", [32, 2592, 8192])
+def test_blockdots_bit_exact(K):
+    g = np.random.default_rng(K + 1)
+    T, N = 3, 37
+    y = g.standard_normal((T, K)).astype(np.float32)
+    img = O.quantize(y)
+    w = W.q4_0_weights(g, (N,), K)
+    sumi = H.torch().empty((T, N, K // 32), dtype=H.torch().int32, device="cuda")
+    qimg.blockdots(H.dev(w.qs), H.dev(w.d), H.dev(img), T, K, sumi)
+    sync()
+    assert np.array_equal(H.host(sumi), O.blockdots(w.qs, K, img, T, T))
+
+
+# ---- ordinary readers ----------------------------------------------------------------------------
+def run_readers(wl, img_host, rows=None, live=None):
+    T = wl.T if rows is None else rows
+    torch = H.torch()
+    img = H.dev(img_host)
+    outs, specs = [], []
+    for r in wl.readers:
+        N = r.d.shape[-2]
+        out = H.sentinel_f32(T, N)
+        specs.append((H.dev(r.qs), H.dev(r.d), out))
+        outs.append(out)
+    qimg.mmvq(specs, img, T, wl.K, H.live_tensor(live) if live is not None else None)
+    sync()
+    return [H.host(o) for o in outs]
+
+
+def check_ordinary(wl, img_o, outs, live=None, nmse=True):
+    live = wl.T if live is None else live
+    codes, da, sa = O.image_planes(img_o, wl.T, wl.K)
+    Kb = wl.K // 32
+    for i, (r, out) in enumerate(zip(wl.readers, outs)):
+        o64 = O.mmvq(r.qs, r.d, wl.K, img_o, wl.T, live)
+        dw = np.abs(H.f16(r.d))
+        A = np.einsum("nb,tb->tn", dw, np.abs(H.f16(da[:live, :Kb])) * 15 * np.abs(codes[:live, :Kb].astype(np.float64)).sum(-1)
+                      + 8 * np.abs(H.f16(sa[:live, :Kb])))
+        H.check_reader(out[:live], o64, A, wl.K, "reader %d" % i)
+        assert (out[live:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding rows of out written"
+        if nmse:
+            ref = H.unquantized_ref(wl, r.qs, r.d, live)
+            e = H.nmse(out[:live], ref)
+            assert e <= 5e-4, "reader %d NMSE %.3g" % (i, e)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3])
+def test_ordinary_small(config):
+    wl = W.make(config, small=True)
+    print("ordinary small config", config, flush=True)
+    y, img = run_producer(wl)
+    _, img_o = check_producer(wl, y, img)
+    check_ordinary(wl, img_o, run_readers(wl, img))
+
+
+@pytest.mark.parametrize("config", [1, 2, 3])
+def test_ordinary_full_size(config):
+    wl = W.make(config)
+    print("ordinary full config", config, flush=True)
+    y, img = run_producer(wl)
+    _, img_o = check_producer(wl, y, img)
+    check_ordinary(wl, img_o, run_readers(wl, img), nmse=(config != 3))
+
+
+def test_ordinary_geglu_full_size():
+    wl = W.make(3, glu_op="geglu_erf")
+    y, img = run_producer(wl)
+    _, img_o = check_producer(wl, y, img)
+    check_ordinary(wl, img_o, run_readers(wl, img), nmse=False)
+
+
+@pytest.mark.parametrize("K,T,Ns", [(32, 1, [5]), (2592, 13, [37, 64, 3]), (32768, 2, [9]), (2048, 8, [1, 300])])
+def test_ordinary_edge_shapes(K, T, Ns):
+    g = np.random.default_rng(K * 7 + T)
+    x = g.standard_normal((T, K)).astype(np.float32)
+    wl = W.Workload(0, "edge", T, K, "rmsnorm", x=x, gamma=g.normal(1, 0.1, K).astype(np.float32),
+                    readers=[W.q4_0_weights(g, (N,), K) for N in Ns])
+    y, img = run_producer(wl)
+    _, img_o = check_producer(wl, y, img)
+    check_ordinary(wl, img_o, run_readers(wl, img), nmse=False)
+
+
+def test_ordinary_live_rows_and_empty():
+    wl = W.make(2, small=True)
+    y, img = run_producer(wl)
+    _, img_o = check_producer(wl, y, img)
+    for live in (0, 3, 8):
+        check_ordinary(wl, img_o, run_readers(wl, img, live=live), live=live, nmse=False)
+    # zero rows is a no-op
+    qimg.mmvq([(H.dev(r.qs), H.dev(r.d), H.sentinel_f32(1, r.d.shape[0])) for r in wl.readers],
+              H.dev(img), 0, wl.K)
+    qimg.emit_rmsnorm(H.dev(wl.x[:0]), H.dev(wl.gamma), W.EPS, H.sentinel_f32(0, wl.K), None)
+
+
+def test_readers_deterministic():
+    wl = W.make(2)
+    y, img = run_producer(wl)
+    a = run_readers(wl, img)
+    for _ in range(2):
+        b = run_readers(wl, img)
+        for u, v in zip(a, b):
+            assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
+
+
+# ---- routed readers ------------------------------------------------------------------------------
+def run_routed(wl, img_dev, ids_host, live=None, bucket=None):
+    torch = H.torch()
+    B = wl.T if bucket is None else bucket
+    ws = torch.empty(qimg.workspace_bytes(B, wl.top_k, wl.E) // 4, dtype=torch.int32, device="cuda")
+    ws.fill_(-7)
+    outs, specs = [], []
+    for r in wl.readers:
+        N = r.d.shape[-2]
+        out = H.sentinel_f32(B, wl.top_k, N)
+        specs.append((r._dev_qs, r._dev_d, out))
+        outs.append(out)
+    qimg.mmvq_id(specs, wl.E, img_dev, H.dev(ids_host), H.live_tensor(live) if live is not None else None,
+                 wl.K, ws)
+    sync()
+    return [H.host(o) for o in outs], H.host(ws)
+
+
+def attach_dev_weights(wl):
+    for r in wl.readers:
+        if not hasattr(r, "_dev_qs"):
+            r._dev_qs, r._dev_d = H.dev(r.qs), H.dev(r.d)
+
+
+def check_plan(ws, ids, live, E, top_k):
+    counts, offsets, members, bad = O.plan(ids, live, E)
+    P = live * top_k
+    assert ws[0] == 0 and ws[1] == P
+    g_counts = ws[4: 4 + E]
+    g_offsets = ws[4 + E: 4 + 2 * E + 1]
+    g_members = ws[4 + 2 * E + 1: 4 + 2 * E + 1 + P]
+    assert np.array_equal(g_counts, counts) and np.array_equal(g_offsets, offsets)
+    assert np.array_equal(g_members, members)
+    assert g_counts.sum() == P and (P == 0 or g_members.max() == P - 1)
+
+
+def check_routed(wl, img_o, outs, live, ids=None):
+    ids = wl.ids if ids is None else ids
+    codes, da, sa = O.image_planes(img_o, wl.T, wl.K)
+    Kb = wl.K // 32
+    P = live * wl.top_k
+    flat_ids = ids.reshape(-1)[:P]
+    for i, (r, out) in enumerate(zip(wl.readers, outs)):
+        o64 = O.mmvq_id(r.qs, r.d, wl.E, wl.K, img_o, wl.T, ids, live)   # [P][N]
+        got = out.reshape(-1, out.shape[-1])
+        A = np.empty_like(o64)
+        ta = np.abs(H.f16(da[:, :Kb])) * 15 * np.abs(codes[:, :Kb].astype(np.float64)).sum(-1) + 8 * np.abs(H.f16(sa[:, :Kb]))
+        for p in range(P):
+            e, t = flat_ids[p], p // wl.top_k
+            A[p] = np.abs(H.f16(r.d[e])) @ ta[t]
+        H.check_reader(got[:P], o64, A, wl.K, "routed reader %d" % i)
+        assert (got[P:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding pairs were written"
+
+
+def test_routed_config4_full():
+    wl = W.make(4)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl)
+    _, img_o = check_producer(wl, y, img)
+    outs, ws = run_routed(wl, H.dev(img), wl.ids)
+    check_plan(ws, wl.ids, wl.T, wl.E, wl.top_k)
+    check_routed(wl, img_o, outs, wl.T)
+
+
+def test_routed_reduces_to_ordinary_bitwise():
+    # a pair's routed output equals the ordinary reader of its expert on its image row
+    wl = W.make(4, small=True)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl)
+    outs, _ = run_routed(wl, H.dev(img), wl.ids)
+    for p in (0, 13, 63):
+        t, e = p // wl.top_k, wl.ids.reshape(-1)[p]
+        r = wl.readers[0]
+        ow = W.Workload(0, "ord", wl.T, wl.K, "rmsnorm", readers=[W.Q4Weights(r.qs[e], r.d[e])])
+        o = run_readers(ow, img)[0]
+        assert np.array_equal(o[t].view(np.uint32), outs[0][t, p % wl.top_k].view(np.uint32))
+
+
+def test_routed_bad_expert_ids_are_skipped_and_flagged():
+    wl = W.make(4, small=True)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl)
+    ids = wl.ids.copy()
+    ids[2, 3] = wl.E + 5
+    ids[5, 0] = -1
+    outs, ws = run_routed(wl, H.dev(img), ids)
+    assert ws[0] & qimg.ERR_EXPERT_RANGE
+    for out in outs:
+        assert (out[2, 3].view(np.uint8) == H.SENTINEL_BYTE).all()
+        assert (out[5, 0].view(np.uint8) == H.SENTINEL_BYTE).all()
+    counts, offsets, members, bad = O.plan(ids, wl.T, wl.E)
+    assert bad == 2 and ws[4 + 2 * wl.E] == offsets[wl.E]
+    # live count above the bucket is clamped and flagged
+    outs, ws = run_routed(wl, H.dev(img), wl.ids, live=wl.T + 3)
+    assert ws[0] & qimg.ERR_LIVE_CLAMPED and ws[1] == wl.T * wl.top_k
+
+
+# ---- padded bucket -------------------------------------------------------------------------------
+@pytest.mark.parametrize("live", [1, 9, 113, 114, 128])
+def test_padded_bucket(live):
+    print("padded bucket live", live, flush=True)
+    wl = W.make(5, live=live)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl, live=live)
+    _, img_o = check_producer(wl, y, img, live=live)
+    img_d = H.dev(img)
+    outs, ws = run_routed(wl, img_d, wl.ids, live=live)
+    check_plan(ws, wl.ids, live, wl.E, wl.top_k)
+    check_routed(wl, img_o, outs, live)
+    # a different poison in the padding rows changes nothing
+    x2 = wl.x.copy()
+    W.poison_rows(x2, live, phase=1)
+    y2, img2 = run_producer(wl, live=live, x=x2)
+    assert np.array_equal(y2[:live].view(np.uint32), y[:live].view(np.uint32))
+    assert np.array_equal(img2, img)
+    # live rows equal one-row runs, byte for byte
+    for t in sorted({0, live // 2, live - 1}):
+        w1 = W.Workload(5, "one row", 1, wl.K, "rmsnorm", x=wl.x[t:t + 1].copy(), gamma=wl.gamma,
+                        readers=wl.readers, E=wl.E, top_k=wl.top_k, ids=wl.ids[t:t + 1].copy())
+        y1, img1 = run_producer(w1)
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32))
+        o1, _ = run_routed(w1, H.dev(img1), w1.ids)
+        for a, b in zip(o1, outs):
+            assert np.array_equal(a[0].view(np.uint32), b[t].view(np.uint32))
+
+
+def test_padded_bucket_graph_replay_at_changing_live_counts():
+    torch = H.torch()
+    wl = W.make(5, live=128)
+    attach_dev_weights(wl)
+    B, K, k = wl.T, wl.K, wl.top_k
+    x_d = H.dev(wl.x)
+    g_d = H.dev(wl.gamma)
+    ids_d = H.dev(wl.ids)
+    live_d = H.live_tensor(B)
+    y_d = H.sentinel_f32(B, K)
+    img_d = H.sentinel_u8(qimg.image_bytes(B, K))
+    ws = torch.empty(qimg.workspace_bytes(B, k, wl.E) // 4, dtype=torch.int32, device="cuda")
+    outs = [H.sentinel_f32(B, k, r.d.shape[-2]) for r in wl.readers]
+    specs = [(r._dev_qs, r._dev_d, o) for r, o in zip(wl.readers, outs)]
+
+    def step():
+        qimg.emit_rmsnorm(x_d, g_d, W.EPS, y_d, img_d, live_d)
+        qimg.mmvq_id(specs, wl.E, img_d, ids_d, live_d, K, ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for phase, live in enumerate([1, 9, 113, 114, 128, 113, 9, 1]):
+        x = wl.x.copy()
+        W.poison_rows(x, live, phase)
+        x_d.copy_(torch.from_numpy(x))
+        live_d.fill_(live)
+        y_d.view(torch.uint8).fill_(H.SENTINEL_BYTE)
+        img_d.fill_(H.SENTINEL_BYTE)
+        for o in outs:
+            o.view(torch.uint8).fill_(H.SENTINEL_BYTE)
+        sync()
+        graph.replay()
+        sync()
+        w_live = W.Workload(5, "replay", B, K, "rmsnorm", x=x, gamma=wl.gamma, readers=wl.readers,
+                            E=wl.E, top_k=k, ids=wl.ids, live=live)
+        _, img_o = check_producer(w_live, H.host(y_d), H.host(img_d), live=live)
+        check_plan(H.host(ws), wl.ids, live, wl.E, k)
+        check_routed(w_live, img_o, [H.host(o) for o in outs], live)
