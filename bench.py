@@ -56,7 +56,7 @@ class Instance:
         for r in wl.readers:
             N = r.d.shape[-2]
             out = torch.empty(*((T, wl.top_k, N) if wl.routed else (T, N)), dtype=torch.float32, device="cuda")
-            self.specs.append((dev(r.qs), dev(r.d), out))
+            self.specs.append((qimg.tile_q4_0(dev(r.qs), dev(r.d), K), N, out))
         if wl.routed:
             self.ids = dev(wl.ids)
             self.ws = torch.empty(qimg.workspace_bytes(T, wl.top_k, wl.E) // 4, dtype=torch.int32, device="cuda")

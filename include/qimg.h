@@ -42,11 +42,18 @@
  *                 the block's codes), little-endian.
  *   Blocks K/32 <= b < RB of every live row are written as zero bytes (row padding to a
  *   multiple of 16 blocks, i.e. 512 elements). Rows >= live count are never written.
- * Q4_0 weights (one reader, or one expert of a routed reader):
+ * Q4_0 weights, standard order (the input of qimg_q4_0_tile; one reader or one expert):
  *   qs plane : uint8  qs[N][K/32][16]; byte j of a block holds element j in its low nibble
  *              and element j+16 in its high nibble.
  *   d plane  : fp16   d[N][K/32]; weight = d * (nibble - 8).
  *   Routed readers stack E experts: qs[E][N][K/32][16], d[E][N][K/32].
+ * Q4_0 weights, reader tiles (made once by qimg_q4_0_tile, read by the readers): rows are cut
+ *   into 16-row tiles, K/32 blocks into chunks of 4 (padding rows and blocks are zero). With
+ *   TL = ceil(N/16), KC = ceil(K/128) and chunk c = (e*TL + tile)*KC + s:
+ *   codes : bytes [c*1024 + 16*l, +16) = block 4*s + l/16 of row 16*tile + l%16, l < 64
+ *   scales: fp16 at byte E*TL*KC*1024 + 2*(c*64 + l), same (row, block)
+ *   The same blocks as the standard order, reordered so that one 64-lane load moves 1 KB of
+ *   contiguous weights.
  */
 #ifndef QIMG_H
 #define QIMG_H
@@ -58,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 1
+#define QIMG_ABI_VERSION 3
 
 /* status codes */
 #define QIMG_OK 0
@@ -138,10 +145,21 @@ int qimg_emit_glu(int32_t op, const float* gate, int64_t ldg, const float* up, i
 int qimg_quantize_q8_1(const float* y, int64_t ldy, int32_t rows, const int32_t* live_rows,
                        int32_t K, void* img, void* stream);
 
+/* Bytes of the tiled weights of N rows x K (E experts; 1 for an ordinary reader); 0 on bad
+ * arguments. */
+int64_t qimg_q4_0_tiled_bytes(int32_t N, int32_t K, int32_t E);
+
+/*
+ * Reorder standard Q4_0 planes (qs, d; E experts of N rows) into reader tiles. A one-time
+ * weight preparation, not part of the per-token path. tiled: qimg_q4_0_tiled_bytes(N, K, E)
+ * bytes, 16-byte aligned, must not overlap qs or d. qs 16-byte aligned, d 2-byte aligned.
+ */
+int qimg_q4_0_tile(const void* qs, const void* d, int32_t N, int32_t K, int32_t E, void* tiled,
+                   void* stream);
+
 /* One ordinary Q4_0 reader of an image. */
 typedef struct {
-  const void* qs;  /* uint8 [N][K/32][16], 16-byte aligned */
-  const void* d;   /* fp16  [N][K/32], 4-byte aligned */
+  const void* w;   /* tiled weights (qimg_q4_0_tile, E = 1), 16-byte aligned */
   int32_t N;       /* output rows (> 0) */
   int32_t reserved;
   float* out;      /* f32, out[t * ldo + n] for image row t, n < N; 4-byte aligned */
@@ -153,16 +171,16 @@ typedef struct {
  * many compatible readers of one image). One launch serves up to QIMG_MAX_READERS readers:
  *   out_r[t][n] = sum over blocks b of d_w[n][b] * (d16[t][b] * sumi - 8 * s16[t][b])
  *   sumi = sum_{j<16} (qs[n][b][j] & 15) * c[t][b][j] + (qs[n][b][j] >> 4) * c[t][b][j+16]
- * for image rows t < live (live as above; rows = image rows). Rows t >= live of every out
- * are not written. Outputs must not overlap each other, the image or the weights.
+ * (qs, d_w: the reader's weights in standard order; the reader takes them tiled) for image
+ * rows t < live (live as above; rows = image rows). Rows t >= live of every out are not
+ * written. Outputs must not overlap each other, the image or the weights.
  */
 int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
                    int32_t rows, const int32_t* live_rows, int32_t K, void* stream);
 
 /* One routed (MUL_MAT_ID) Q4_0 reader over E stacked experts. */
 typedef struct {
-  const void* qs;  /* uint8 [E][N][K/32][16], 16-byte aligned */
-  const void* d;   /* fp16  [E][N][K/32], 4-byte aligned */
+  const void* w;   /* tiled weights of all E experts (qimg_q4_0_tile), 16-byte aligned */
   int32_t N;       /* output rows per expert (> 0) */
   int32_t reserved;
   float* out;      /* f32, out[(row * top_k + slot) * ld_pair + n] */
@@ -198,9 +216,10 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
                       size_t workspace_bytes, void* stream);
 
 /*
- * Debug export of the per-block integer dot products of one ordinary reader, computed by
- * the same device code the readers use:
- *   sumi[t][n][b] (int32, [rows][N][K/32]) for all image rows t < rows.
+ * Debug export of the per-block integer dot products of one ordinary reader, computed by the
+ * same device code the readers run (the matrix-core dot of each weight block with each image
+ * row): sumi[t][n][b] (int32, [rows][N][K/32]) for all image rows t < rows. sumi must not
+ * overlap the image or the weights.
  */
 int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, int32_t rows,
                              int32_t K, int32_t* sumi, void* stream);

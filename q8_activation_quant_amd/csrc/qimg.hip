@@ -9,16 +9,13 @@
 //        experts" (TensorFold PR #1047): What this changes, Receipt.
 //
 // Kernels
-//   emit_kernel<OP,JW>   one workgroup per live row: (RMS reduction) -> f32 output -> per
-//                        32-block Q8_1 quantization, all in one pass over the row.
-//   mmvq_kernel<LPR,NWM> Q4_0 x Q8_1 readers. A lane owns one 32-weight block column of the
-//                        K axis and keeps that block of every image column it serves in VGPRs;
-//                        the workgroup then streams weight rows (16-byte block loads, adjacent
-//                        lanes on adjacent blocks) and reduces per-lane block terms with a
-//                        transpose-butterfly and a fixed cross-wave sum. Ordinary readers take
-//                        the live image rows as columns; routed readers take the live pairs of
-//                        one expert, found by a stable scan of the ids in the same launch.
-//   blockdots_kernel     debug export of the per-block integer dots (same device dot code).
+//   emit_kernel<OP,JW>       one workgroup per live row: (RMS reduction) -> f32 output -> per
+//                            32-block Q8_1 quantization, all in one pass over the row.
+//   mmvq_tiled_kernel<N,D>   Q4_0 x Q8_1 readers on the matrix cores (v_mfma_i32_16x16x64_i8)
+//                            over tiled weights: ordinary readers take the live image rows as
+//                            columns, routed readers the live pairs of one expert, found by a
+//                            stable scan of the ids in the same launch. D: block-dot export.
+//   tile_q4_0_kernel         one-time reordering of standard Q4_0 planes into reader tiles.
 //
 // Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off (no fast-math), so every float
 // operation written here is one IEEE binary32 operation with round-to-nearest-even; f32
@@ -112,29 +109,6 @@ __device__ __forceinline__ float geglu_erf_act(float g) {
   const float z = g * kSqrtHalf;
   const float ope = (z < 0.0f) ? erfc_q(-z) : 2.0f - erfc_q(z);
   return (0.5f * g) * ope;
-}
-
-// Q4_0 block: 16 bytes, byte j = element j (low nibble) | element j+16 (high nibble).
-// Activation block: 32 int8 codes as 8 dwords (elements 0..15 in a[0..3], 16..31 in a[4..7]).
-// sumi = sum_j lo_j * c_j + hi_j * c_{j+16}, with v_dot4 (signed; nibbles are 0..15).
-__device__ __forceinline__ void unpack_q4(const uint4 q, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
-  lo[0] = q.x & 0x0f0f0f0fu; hi[0] = (q.x >> 4) & 0x0f0f0f0fu;
-  lo[1] = q.y & 0x0f0f0f0fu; hi[1] = (q.y >> 4) & 0x0f0f0f0fu;
-  lo[2] = q.z & 0x0f0f0f0fu; hi[2] = (q.z >> 4) & 0x0f0f0f0fu;
-  lo[3] = q.w & 0x0f0f0f0fu; hi[3] = (q.w >> 4) & 0x0f0f0f0fu;
-}
-__device__ __forceinline__ int block_sumi(const uint32_t (&lo)[4], const uint32_t (&hi)[4],
-                                          const int32_t* a) {
-  int s = 0;
-  s = __builtin_amdgcn_sdot4((int)lo[0], a[0], s, false);
-  s = __builtin_amdgcn_sdot4((int)lo[1], a[1], s, false);
-  s = __builtin_amdgcn_sdot4((int)lo[2], a[2], s, false);
-  s = __builtin_amdgcn_sdot4((int)lo[3], a[3], s, false);
-  s = __builtin_amdgcn_sdot4((int)hi[0], a[4], s, false);
-  s = __builtin_amdgcn_sdot4((int)hi[1], a[5], s, false);
-  s = __builtin_amdgcn_sdot4((int)hi[2], a[6], s, false);
-  s = __builtin_amdgcn_sdot4((int)hi[3], a[7], s, false);
-  return s;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -299,272 +273,375 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Readers
+// Readers: Q4_0 x Q8_1 mat-vec on the matrix cores.
+//
+// Weights are read in a tiled Q4_0 order made once by qimg_q4_0_tile: the rows of a reader are
+// cut into 16-row tiles and the K axis into chunks of 4 blocks; chunk (tile, s) is 1 KB of
+// codes, lane l holding the 16 bytes of block 4 s + (l >> 4) of row (l & 15), then 128 B of
+// fp16 scales in the same lane order. One wave load instruction thus moves 1 KB of contiguous
+// weights, 16 bytes per lane (narrower or scattered loads run at a fraction of HBM bandwidth on
+// this part).
+//
+// Dot products: v_mfma_i32_16x16x64_i8, D[m][n] = sum_k A[m][k] B[k][n], where lane l supplies
+// A row (l & 15) and B column (l & 15) over k-group (l >> 4) (16 values each) and receives
+// D rows 4 (l >> 4) .. +3 of column (l & 15).
+//   B: the lane's own weight block, low nibbles (elements 0..15) in one MFMA and high nibbles
+//      (elements 16..31) in a second one that accumulates onto the first.
+//   A: block-diagonal over the four k-groups: row m carries image column 4 tg + (m & 3) of the
+//      block in k-group (m >> 2), zero elsewhere.
+// So D[4 g + v][n] of lane (n, g) is the block integer dot of its own block with image column
+// 4 tg + v: the lane then applies its block scale, acc += d_w * (d_a * sumi - 8 s_a), summing
+// its chunks in K order; the four k-group lanes of a row are added (lanes n, n+16: then with
+// n+32), then the waves' K ranges in ascending wave order. The sum for one output does not
+// depend on the other columns, the live count or the tiles of the workgroup.
+//
+// Image columns (live image rows, or a routed expert's live pairs) are staged in LDS per pass of
+// up to 8: codes [block][column][32], d_a and -8 s_a as f32 [block][8].
 // ---------------------------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+
 struct ReaderDesc {
-  const uint8_t* qs;
-  const uint16_t* d;
+  const uint8_t* qs;  // tiled codes (1 KB per chunk)
+  const uint16_t* d;  // tiled scales (64 per chunk)
   float* out;
-  int64_t ld;   // ordinary: ldo per image row; routed: ld_pair per pair
-  int32_t N;
-  int32_t pad;
+  int64_t ld;         // ordinary: per image row; routed: per pair
+  int32_t N;          // rows
+  int32_t tiles;      // ceil(N / 16): tiles per expert
 };
 
-struct MmvqArgs {
+struct ReadArgs {
   ReaderDesc r[QIMG_MAX_READERS];
-  int32_t tile_start[QIMG_MAX_READERS + 1];  // tile prefix over readers (per expert if routed)
+  int32_t tile_start[QIMG_MAX_READERS + 1];  // tile prefix over readers (within one expert)
   const uint8_t* codes;
   const uint32_t* ds;
   const int32_t* live_rows;
-  const int32_t* ids;   // routed only
-  int32_t* ws;          // routed only: plan workspace
-  int32_t n_readers, RB, Kb, rows, TR, top_k, E, routed;
+  const int32_t* ids;  // routed: [bucket][top_k]
+  int32_t* ws;         // routed: plan workspace
+  int32_t* sumi;       // debug: block dots of reader 0, [rows][N][Kb]
+  int32_t n_readers, RB, Kb, KC, rows, top_k, E, routed;
+  int32_t wg_per_unit;  // workgroups per expert (routed) or in total (ordinary)
+  int32_t tiles_total;  // tiles per expert summed over readers
+  int32_t tp;           // image columns per LDS pass (8, 4, 2 or 1)
+  int32_t lds_da, lds_ms, lds_zero, lds_red, lds_cols;  // byte offsets (codes at 0)
 };
 
-// Transpose-butterfly over LPR lanes of V values per lane. At the level of mask M a lane
-// keeps the half of its values selected by its lane bit M and adds the partner's copy of that
-// half, so after log2(LPR) levels lane bl of the segment holds the complete sums of values
-// [bl*V/LPR, (bl+1)*V/LPR) (V >= LPR), or of value bl/(LPR/V) (V < LPR; the remaining levels
-// are plain butterflies). Every value is summed over the lanes by the same tree.
-template <int M, int N>
-__device__ __forceinline__ void tbfly(float* v, int lane) {
-  if constexpr (M > 0) {
-    if constexpr (N > 1) {
-      constexpr int H = N / 2;
-      const bool up = (lane & M) != 0;
+// Stage image columns [c0, c0 + nc) in LDS. Column c is image row c (ordinary) or
+// cols[c] / top_k (routed). Loads are issued in batches of 8 per thread before their stores.
+__device__ __forceinline__ void stage_columns(const ReadArgs& p, unsigned char* smem,
+                                              const int32_t* cols, int c0, int nc) {
+  const int Kbp = 4 * p.KC, TP = p.tp;
+  float* daL = reinterpret_cast<float*>(smem + p.lds_da);
+  float* msL = reinterpret_cast<float*>(smem + p.lds_ms);
+  const int nitems = Kbp * TP * 2;  // (block, column, half)
+  for (int base = threadIdx.x; base < nitems; base += 8 * blockDim.x) {
+    uint4 v[8];
 #pragma unroll
-      for (int i = 0; i < H; ++i) {
-        const float send = up ? v[i] : v[i + H];
-        const float keep = up ? v[i + H] : v[i];
-        v[i] = keep + __shfl_xor(send, M, 64);
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * blockDim.x;
+      const int half = i & 1, t = (i >> 1) % TP, b = (i >> 1) / TP;
+      v[j] = make_uint4(0, 0, 0, 0);
+      if (i < nitems && t < nc && b < p.Kb) {
+        const int c = c0 + t;
+        const int irow = p.routed ? cols[c] / p.top_k : c;
+        v[j] = reinterpret_cast<const uint4*>(p.codes + ((int64_t)irow * p.RB + b) * 32)[half];
       }
-      tbfly<M / 2, H>(v, lane);
-    } else {
-      v[0] = v[0] + __shfl_xor(v[0], M, 64);
-      tbfly<M / 2, 1>(v, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * blockDim.x;
+      if (i < nitems) reinterpret_cast<uint4*>(smem)[i] = v[j];  // (b*TP + t)*32 + 16*half
     }
   }
+  const int nds = Kbp * 8;  // (block, column slot of 8)
+  for (int base = threadIdx.x; base < nds; base += 8 * blockDim.x) {
+    uint32_t dsw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * blockDim.x;
+      const int t = i & 7, b = i >> 3;
+      dsw[j] = 0u;
+      if (i < nds && t < nc && b < p.Kb) {
+        const int c = c0 + t;
+        const int irow = p.routed ? cols[c] / p.top_k : c;
+        dsw[j] = p.ds[(int64_t)irow * p.RB + b];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * blockDim.x;
+      if (i < nds) {
+        daL[i] = h2f(dsw[j]);
+        msL[i] = -8.0f * h2f(dsw[j] >> 16);
+      }
+    }
+  }
+  if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[threadIdx.x] = 0u;
 }
 
-constexpr int kGroup = 4;  // weight rows per lane between two reductions
-
-// One pass of a row tile against up to CT image columns cols[c0 .. c0+ncols).
-// red: LDS [NW][TR*CT]. Writes the finished outputs.
-template <int LPR, int CT>
-__device__ __forceinline__ void reader_pass(const MmvqArgs& p, const ReaderDesc& R,
-                                            const uint8_t* __restrict__ qs,
-                                            const uint16_t* __restrict__ dw_plane, int n0,
-                                            int n_end, const int32_t* cols, int c0, int ncols,
-                                            float* red) {
-  constexpr int RPW = 64 / LPR;
-  constexpr int V = kGroup * CT;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int NW = blockDim.x >> 6;
-  const int r = lane / LPR;
-  const int bl = lane % LPR;
-  const int blk = w * LPR + bl;
-  const bool act = blk < p.Kb;
-  const int Kb = p.Kb;
-
-  // this lane's activation block for each column, kept in VGPRs for the whole tile
-  int32_t a[CT][8];
-  float da[CT], ms[CT];
-#pragma unroll
-  for (int c = 0; c < CT; ++c) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[c][i] = 0;
-    da[c] = 0.0f;
-    ms[c] = 0.0f;
-    if (act && c < ncols) {
-      const int col = cols[c0 + c];
-      const int irow = p.routed ? col / p.top_k : col;
-      const int64_t bi = (int64_t)irow * p.RB + blk;
-      const int4 lo = reinterpret_cast<const int4*>(p.codes)[bi * 2];
-      const int4 hi = reinterpret_cast<const int4*>(p.codes)[bi * 2 + 1];
-      a[c][0] = lo.x; a[c][1] = lo.y; a[c][2] = lo.z; a[c][3] = lo.w;
-      a[c][4] = hi.x; a[c][5] = hi.y; a[c][6] = hi.z; a[c][7] = hi.w;
-      const uint32_t dsw = p.ds[bi];
-      da[c] = h2f(dsw);
-      ms[c] = -8.0f * h2f(dsw >> 16);
-    }
-  }
-
-  const int nrows = n_end - n0;
-  for (int g0 = 0; g0 < nrows; g0 += kGroup * RPW) {
-    float acc[V];
-#pragma unroll
-    for (int s = 0; s < kGroup; ++s) {
-      const int n = n0 + g0 + s * RPW + r;
-      uint4 q = make_uint4(0, 0, 0, 0);
-      float dwf = 0.0f;
-      if (act && n < n_end) {
-        const int64_t wi = (int64_t)n * Kb + blk;
-        q = reinterpret_cast<const uint4*>(qs)[wi];
-        dwf = h2f(dw_plane[wi]);
-      }
-      uint32_t lo[4], hi[4];
-      unpack_q4(q, lo, hi);
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const int si = block_sumi(lo, hi, a[c]);
-        const float x = __builtin_fmaf(da[c], (float)si, ms[c]);  // d_a*sumi - 8*s_a
-        acc[s * CT + c] = dwf * x;
-      }
-    }
-    tbfly<LPR / 2, V>(acc, lane);
-    // scatter this lane's finished values into the per-wave LDS slots
-    float* rw = red + (int64_t)w * (p.TR * CT);
-    if constexpr (V >= LPR) {
-      constexpr int PER = V / LPR;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int vi = bl * PER + i;
-        const int s = vi / CT, c = vi % CT;
-        rw[(g0 + s * RPW + r) * CT + c] = acc[i];
-      }
-    } else {
-      constexpr int DUP = LPR / V;
-      if (bl % DUP == 0) {
-        const int vi = bl / DUP;
-        const int s = vi / CT, c = vi % CT;
-        rw[(g0 + s * RPW + r) * CT + c] = acc[0];
-      }
-    }
-  }
-  __syncthreads();
-  // fixed cross-wave order: ascending wave index
-  for (int o = threadIdx.x; o < nrows * CT; o += blockDim.x) {
-    const int c = o % CT;
-    if (c >= ncols) continue;
-    float t = red[o];
-    for (int ww = 1; ww < NW; ++ww) t = t + red[(int64_t)ww * (p.TR * CT) + o];
-    const int n = n0 + o / CT;
-    const int col = cols[c0 + c];
-    R.out[(int64_t)col * R.ld + n] = t;
-  }
-  __syncthreads();
-}
-
-template <int LPR>
-__device__ __forceinline__ void reader_columns(const MmvqArgs& p, const ReaderDesc& R,
-                                               const uint8_t* qs, const uint16_t* dwp, int n0,
-                                               int n_end, const int32_t* cols, int ncols,
-                                               float* red) {
-  for (int c0 = 0; c0 < ncols; c0 += 8) {
-    const int ct = ncols - c0 < 8 ? ncols - c0 : 8;
-    if (ct > 4) reader_pass<LPR, 8>(p, R, qs, dwp, n0, n_end, cols, c0, ct, red);
-    else if (ct > 2) reader_pass<LPR, 4>(p, R, qs, dwp, n0, n_end, cols, c0, ct, red);
-    else if (ct > 1) reader_pass<LPR, 2>(p, R, qs, dwp, n0, n_end, cols, c0, ct, red);
-    else reader_pass<LPR, 1>(p, R, qs, dwp, n0, n_end, cols, c0, ct, red);
-  }
-}
-
-// Dynamic LDS: int32 cols[max_cols] then float red[NW][TR*8].
-template <int LPR, int NWM>
-__global__ __launch_bounds__(NWM * 64) void mmvq_kernel(MmvqArgs p, int max_cols) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int32_t* cols = reinterpret_cast<int32_t*>(smem);
-  float* red = reinterpret_cast<float*>(smem + ((max_cols * 4 + 15) & ~15));
-  __shared__ int wave_cnt[16];
+// Stable scan of the live pairs routed to expert e: cols[0..n) = pair ids in ascending order.
+// The workgroup of tile range 0 also writes expert e's plan entries ([P3] What this changes:
+// only the first live rows' pairs are planned; padding rows' ids are never read).
+__device__ int scan_expert(const ReadArgs& p, int e, int live, int clamped, bool write_plan,
+                           int32_t* cols) {
+  __shared__ int wave_cnt[kWaves];
   __shared__ int red_i[4];
-
-  int clamped = 0;
-  const int live = clamp_live(p.live_rows, p.rows, &clamped);
-  const int tiles = p.tile_start[p.n_readers];
-  const int unit = blockIdx.x / tiles;  // expert (routed) or 0
-  const int tile = blockIdx.x % tiles;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, NW = blockDim.x >> 6;
-
-  int ncols;
-  if (!p.routed) {
-    ncols = live;
-    for (int i = threadIdx.x; i < live; i += blockDim.x) cols[i] = i;
+  const int P = live * p.top_k;
+  if (threadIdx.x < 4) red_i[threadIdx.x] = 0;
+  __syncthreads();
+  int n_lt = 0, n_valid = 0, n_bad = 0, base = 0;
+  for (int p0 = 0; p0 < P; p0 += blockDim.x) {
+    const int pi = p0 + threadIdx.x;
+    const int id = pi < P ? p.ids[pi] : -1;
+    const bool valid = pi < P && id >= 0 && id < p.E;
+    n_bad += (pi < P && !valid) ? 1 : 0;
+    n_valid += valid ? 1 : 0;
+    n_lt += (valid && id < e) ? 1 : 0;
+    const bool match = valid && id == e;
+    const unsigned long long bal = __ballot(match);
+    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[w] = __popcll(bal);
     __syncthreads();
-  } else {
-    // Stable scan of the live pairs for this expert ([P3] What this changes: only the first
-    // live rows' pairs are planned; padding rows' ids are never read).
-    const int e = unit;
-    const int P = live * p.top_k;
-    if (threadIdx.x < 4) red_i[threadIdx.x] = 0;
-    __syncthreads();
-    int n_lt = 0, n_valid = 0, n_bad = 0, base = 0;
-    for (int p0 = 0; p0 < P; p0 += blockDim.x) {
-      const int pi = p0 + threadIdx.x;
-      const int id = pi < P ? p.ids[pi] : -1;
-      const bool valid = pi < P && id >= 0 && id < p.E;
-      n_bad += (pi < P && !valid) ? 1 : 0;
-      n_valid += valid ? 1 : 0;
-      n_lt += (valid && id < e) ? 1 : 0;
-      const bool match = valid && id == e;
-      const unsigned long long bal = __ballot(match);
-      const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) wave_cnt[w] = __popcll(bal);
-      __syncthreads();
-      int pre = 0, tot = 0;
-      for (int i = 0; i < NW; ++i) {
-        pre += i < w ? wave_cnt[i] : 0;
-        tot += wave_cnt[i];
-      }
-      if (match) cols[base + pre + rank] = pi;
-      base += tot;
-      __syncthreads();
+    int pre = 0, tot = 0;
+    for (int i = 0; i < NW; ++i) {
+      pre += i < w ? wave_cnt[i] : 0;
+      tot += wave_cnt[i];
     }
-    ncols = base;
-    if (tile == 0) {
-      atomicAdd(&red_i[0], n_lt);
-      atomicAdd(&red_i[1], n_valid);
-      atomicAdd(&red_i[2], n_bad);
-      __syncthreads();
-      const int off = red_i[0];
-      int32_t* counts = p.ws + 4;
-      int32_t* offsets = counts + p.E;
-      int32_t* members = offsets + p.E + 1;
-      if (threadIdx.x == 0) {
-        counts[e] = ncols;
-        offsets[e] = off;
+    if (match) cols[base + pre + rank] = pi;
+    base += tot;
+    __syncthreads();
+  }
+  if (write_plan) {
+    atomicAdd(&red_i[0], n_lt);
+    atomicAdd(&red_i[1], n_valid);
+    atomicAdd(&red_i[2], n_bad);
+    __syncthreads();
+    const int off = red_i[0];
+    int32_t* counts = p.ws + 4;
+    int32_t* offsets = counts + p.E;
+    int32_t* members = offsets + p.E + 1;
+    if (threadIdx.x == 0) {
+      counts[e] = base;
+      offsets[e] = off;
+    }
+    for (int i = threadIdx.x; i < base; i += blockDim.x) members[off + i] = cols[i];
+    if (e == 0 && threadIdx.x == 0) {
+      p.ws[0] = (red_i[2] ? QIMG_ERR_EXPERT_RANGE : 0) | (clamped ? QIMG_ERR_LIVE_CLAMPED : 0);
+      p.ws[1] = P;
+      p.ws[2] = 0;
+      p.ws[3] = 0;
+      offsets[p.E] = red_i[1];
+    }
+  }
+  __syncthreads();
+  return base;
+}
+
+template <int NTM, bool DOTS>
+__global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int KU = NTM <= 2 ? 4 : 2;  // chunks per prefetch batch (two batches in flight)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int KC = p.KC, TP = p.tp;
+  const int cs0 = KC * w / kWaves, cs1 = KC * (w + 1) / kWaves;
+  int clamped = 0;
+  const int live = DOTS ? p.rows : clamp_live(p.live_rows, p.rows, &clamped);
+  const int unit = blockIdx.x / p.wg_per_unit;  // expert (routed) or 0
+  const int wgi = blockIdx.x % p.wg_per_unit;
+  const int t0 = (int)((int64_t)p.tiles_total * wgi / p.wg_per_unit);
+  const int t1 = (int)((int64_t)p.tiles_total * (wgi + 1) / p.wg_per_unit);
+  int32_t* cols = reinterpret_cast<int32_t*>(smem + p.lds_cols);
+  const float* daL = reinterpret_cast<const float*>(smem + p.lds_da);
+  const float* msL = reinterpret_cast<const float*>(smem + p.lds_ms);
+  float* red = reinterpret_cast<float*>(smem + p.lds_red);
+
+  const int ncols = p.routed ? scan_expert(p, unit, live, clamped, wgi == 0, cols) : live;
+  if (ncols == 0 || t0 >= t1) return;
+
+  for (int c0 = 0; c0 < ncols; c0 += TP) {
+    const int nc = ncols - c0 < TP ? ncols - c0 : TP;
+    const int TG = (nc + 3) >> 2;  // token groups of 4 columns
+    // A operand addresses (per token group and half): 16 LDS bytes, or the zero slot
+    const int m = n;  // A row of this lane
+    int a_off[2];
+    bool a_on[2];
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      const int col = 4 * tg + (m & 3);
+      a_on[tg] = (m >> 2) == g && col < nc;
+      a_off[tg] = (g * TP + col) * 32;
+    }
+    for (int tb = t0; tb < t1; tb += NTM) {
+      const int nt = t1 - tb < NTM ? t1 - tb : NTM;
+      const uint4* qp[NTM];
+      const uint16_t* dp[NTM];
+      int rl[NTM], rr[NTM];
+#pragma unroll
+      for (int t = 0; t < NTM; ++t) {
+        const int tile = tb + (t < nt ? t : nt - 1);  // idle slots re-read the last tile
+        int ri = 0;
+        while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
+        const int lt = tile - p.tile_start[ri];
+        rr[t] = ri;
+        rl[t] = lt * 16 + n;  // this lane's weight row in reader ri
+        const int64_t chunk0 = ((int64_t)unit * p.r[ri].tiles + lt) * KC;
+        qp[t] = reinterpret_cast<const uint4*>(p.r[ri].qs) + chunk0 * 64 + lane;
+        dp[t] = p.r[ri].d + chunk0 * 64 + lane;
       }
-      for (int i = threadIdx.x; i < ncols; i += blockDim.x) members[off + i] = cols[i];
-      if (e == 0 && threadIdx.x == 0) {
-        p.ws[0] = (red_i[2] ? QIMG_ERR_EXPERT_RANGE : 0) | (clamped ? QIMG_ERR_LIVE_CLAMPED : 0);
-        p.ws[1] = P;
-        p.ws[2] = 0;
-        p.ws[3] = 0;
-        offsets[p.E] = red_i[1];
+      float acc[NTM][8];
+#pragma unroll
+      for (int t = 0; t < NTM; ++t)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[t][v] = 0.0f;
+
+      uint4 qa[KU][NTM], qb[KU][NTM];
+      uint32_t da_[KU][NTM], db_[KU][NTM];
+      auto load = [&](uint4 (&q)[KU][NTM], uint32_t (&d)[KU][NTM], int kb) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          const int cs = kb + u < cs1 ? kb + u : cs1 - 1;  // past the range: repeat the last
+#pragma unroll
+          for (int t = 0; t < NTM; ++t) {
+            q[u][t] = qp[t][(int64_t)cs * 64];
+            d[u][t] = dp[t][(int64_t)cs * 64];
+          }
+        }
+      };
+      auto compute = [&](const uint4 (&q)[KU][NTM], const uint32_t (&d)[KU][NTM], int kb) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          const int cs = kb + u;
+          if (cs >= cs1) break;
+          v4i blo[NTM], bhi[NTM];
+          float dw[NTM];
+#pragma unroll
+          for (int t = 0; t < NTM; ++t) {
+            blo[t][0] = (int)(q[u][t].x & 0x0f0f0f0fu);
+            blo[t][1] = (int)(q[u][t].y & 0x0f0f0f0fu);
+            blo[t][2] = (int)(q[u][t].z & 0x0f0f0f0fu);
+            blo[t][3] = (int)(q[u][t].w & 0x0f0f0f0fu);
+            bhi[t][0] = (int)((q[u][t].x >> 4) & 0x0f0f0f0fu);
+            bhi[t][1] = (int)((q[u][t].y >> 4) & 0x0f0f0f0fu);
+            bhi[t][2] = (int)((q[u][t].z >> 4) & 0x0f0f0f0fu);
+            bhi[t][3] = (int)((q[u][t].w >> 4) & 0x0f0f0f0fu);
+            dw[t] = h2f(d[u][t]);
+          }
+          const int blk = 4 * cs + g;  // this lane's block
+#pragma unroll
+          for (int tg = 0; tg < 2; ++tg) {
+            if (tg >= TG) break;
+            const int lo = a_on[tg] ? cs * (4 * TP * 32) + a_off[tg] : p.lds_zero;
+            const int hi = a_on[tg] ? lo + 16 : p.lds_zero;
+            const v4i alo = *reinterpret_cast<const v4i*>(smem + lo);
+            const v4i ahi = *reinterpret_cast<const v4i*>(smem + hi);
+            const float4 da4 = *reinterpret_cast<const float4*>(daL + blk * 8 + 4 * tg);
+            const float4 ms4 = *reinterpret_cast<const float4*>(msL + blk * 8 + 4 * tg);
+#pragma unroll
+            for (int t = 0; t < NTM; ++t) {
+              if (t >= nt) break;
+              const v4i zero = {0, 0, 0, 0};
+              v4i dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[t], zero, 0, 0, 0);
+              dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[t], dd, 0, 0, 0);
+              if constexpr (DOTS) {
+                if (rl[t] < p.r[0].N && blk < p.Kb) {
+#pragma unroll
+                  for (int v = 0; v < 4; ++v) {
+                    const int col = c0 + 4 * tg + v;
+                    if (4 * tg + v < nc)
+                      p.sumi[((int64_t)col * p.r[0].N + rl[t]) * p.Kb + blk] = dd[v];
+                  }
+                }
+              } else {
+                acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.x, (float)dd[0], ms4.x), acc[t][4 * tg + 0]);
+                acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.y, (float)dd[1], ms4.y), acc[t][4 * tg + 1]);
+                acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.z, (float)dd[2], ms4.z), acc[t][4 * tg + 2]);
+                acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.w, (float)dd[3], ms4.w), acc[t][4 * tg + 3]);
+              }
+            }
+          }
+        }
+      };
+      if (cs1 > cs0) load(qa, da_, cs0);  // weight loads fly while the image is staged
+      if (tb == t0) {
+        __syncthreads();  // the previous column pass is done with LDS
+        stage_columns(p, smem, cols, c0, nc);
+        __syncthreads();
+      }
+      for (int kb = cs0; kb < cs1; kb += 2 * KU) {
+        load(qb, db_, kb + KU);
+        compute(qa, da_, kb);
+        load(qa, da_, kb + 2 * KU);
+        compute(qb, db_, kb + KU);
+      }
+      if constexpr (!DOTS) {
+        // the four k-group lanes of a row: (g0 + g1) + (g2 + g3)
+#pragma unroll
+        for (int t = 0; t < NTM; ++t)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            acc[t][v] = acc[t][v] + __shfl_xor(acc[t][v], 16, 64);
+            acc[t][v] = acc[t][v] + __shfl_xor(acc[t][v], 32, 64);
+          }
+        // lane (n, g) stores columns 2g, 2g+1 of its row for each tile
+#pragma unroll
+        for (int t = 0; t < NTM; ++t)
+          if (t < nt)
+            *reinterpret_cast<float2*>(red + ((w * NTM + t) * 16 + n) * 8 + 2 * g) =
+                make_float2(g == 0 ? acc[t][0] : g == 1 ? acc[t][2] : g == 2 ? acc[t][4] : acc[t][6],
+                            g == 0 ? acc[t][1] : g == 1 ? acc[t][3] : g == 2 ? acc[t][5] : acc[t][7]);
+        __syncthreads();
+        for (int o = threadIdx.x; o < nt * 128; o += blockDim.x) {
+          const int t = o >> 7, nn = (o >> 3) & 15, col = o & 7;
+          if (col < nc) {
+            const int tile = tb + t;
+            int ri = 0;
+            while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
+            const int row = (tile - p.tile_start[ri]) * 16 + nn;
+            if (row < p.r[ri].N) {
+              float s = red[(t * 16 + nn) * 8 + col];
+              for (int ww = 1; ww < kWaves; ++ww) s = s + red[((ww * NTM + t) * 16 + nn) * 8 + col];
+              const int orow = p.routed ? cols[c0 + col] : c0 + col;
+              p.r[ri].out[(int64_t)orow * p.r[ri].ld + row] = s;
+            }
+          }
+        }
+        __syncthreads();
       }
     }
   }
-  if (ncols == 0) return;
-
-  int ri = 0;
-  while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
-  const ReaderDesc& R = p.r[ri];
-  const int n0 = (tile - p.tile_start[ri]) * p.TR;
-  const int n_end = n0 + p.TR < R.N ? n0 + p.TR : R.N;
-  const int64_t eoff = (int64_t)unit * R.N * p.Kb;  // expert offset in blocks (0 if ordinary)
-  reader_columns<LPR>(p, R, R.qs + eoff * 16, R.d + eoff, n0, n_end, cols, ncols, red);
 }
 
-__global__ void blockdots_kernel(const uint8_t* __restrict__ qs, int N, int Kb,
-                                 const uint8_t* __restrict__ codes, int RB, int rows,
-                                 int32_t* __restrict__ sumi) {
-  const int64_t total = (int64_t)rows * N * Kb;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / ((int64_t)N * Kb);
-    const int64_t rem = i % ((int64_t)N * Kb);
-    const int64_t n = rem / Kb, b = rem % Kb;
-    const uint4 q = reinterpret_cast<const uint4*>(qs)[n * Kb + b];
-    const int4* ab = reinterpret_cast<const int4*>(codes) + (t * RB + b) * 2;
-    const int4 lo = ab[0], hi = ab[1];
-    const int32_t a[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint32_t l4[4], h4[4];
-    unpack_q4(q, l4, h4);
-    sumi[i] = block_sumi(l4, h4, a);
+// Standard Q4_0 planes -> tiled order (see the reader notes above). Rows and blocks past N and
+// K/32 are written as zeros, so tiles and chunks are always whole.
+__global__ void tile_q4_0_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
+                                 int N, int Kb, int KC, int tiles, int E,
+                                 uint8_t* __restrict__ tq, uint16_t* __restrict__ td) {
+  const int64_t total = (int64_t)E * tiles * KC * 64;
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(o & 63);
+    const int64_t c = o >> 6;
+    const int s = (int)(c % KC);
+    const int64_t et = c / KC;
+    const int tile = (int)(et % tiles);
+    const int64_t e = et / tiles;
+    const int row = tile * 16 + (lane & 15);
+    const int blk = 4 * s + (lane >> 4);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    uint16_t dv = 0;
+    if (row < N && blk < Kb) {
+      const int64_t src = (e * N + row) * Kb + blk;
+      v = reinterpret_cast<const uint4*>(qs)[src];
+      dv = d[src];
+    }
+    reinterpret_cast<uint4*>(tq)[o] = v;
+    td[o] = dv;
   }
 }
 
-// ---------------------------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------------------------
 inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -619,49 +696,97 @@ int launch_emit(int op, EmitArgs& a, hipStream_t s) {
   return QIMG_EUNSUPPORTED;
 }
 
-struct ReaderShape {
-  int LPR, NW, TR;
-};
 
-// Lanes per row segment: the candidate in {64, 32, 16} that leaves the fewest idle lanes on
-// the K axis (ties go to the wider segment); NW = waves covering K.
-ReaderShape reader_shape(int Kb, int64_t rows_per_unit, int64_t units) {
-  ReaderShape s{64, 0, 0};
-  int best = 1 << 30;
-  for (int lpr : {64, 32, 16}) {
-    const int nw = (Kb + lpr - 1) / lpr;
-    const int waste = nw * lpr - Kb;
-    if (nw <= 16 && waste < best) {
-      best = waste;
-      s.LPR = lpr;
-      s.NW = nw;
-    }
-  }
-  const int grp = kGroup * (64 / s.LPR);
-  // rows per workgroup tile: aim at ~1024 busy workgroups for ordinary readers, ~16 tiles per
-  // expert for routed ones; a multiple of the reduction group, at most 64 rows.
-  int64_t want = units > 1 ? rows_per_unit / 16 : rows_per_unit / 1024;
-  int tr = grp;
-  while (tr * 2 <= want && tr * 2 <= 64) tr *= 2;
-  s.TR = tr;
-  return s;
+inline int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
 }
 
-int launch_mmvq(MmvqArgs& a, int units, int max_cols, hipStream_t s, const ReaderShape& sh) {
-  const size_t lds = (size_t)((max_cols * 4 + 15) & ~15) + (size_t)sh.NW * sh.TR * 8 * 4;
-  if (lds > 64 * 1024) return QIMG_EUNSUPPORTED;
-  const int tiles = a.tile_start[a.n_readers];
-  dim3 grid((unsigned)((int64_t)tiles * units)), block(sh.NW * 64);
-#define QIMG_MMVQ_CASE(L, NWM)                                                                \
-  if (sh.LPR == L && sh.NW <= NWM) {                                                          \
-    hipLaunchKernelGGL((mmvq_kernel<L, NWM>), grid, block, lds, s, a, max_cols);              \
-    return launch_status();                                                                   \
+inline int64_t tiled_chunks(int32_t N, int32_t K, int32_t E) {
+  const int64_t tiles = (N + 15) / 16, KC = (K / 32 + 3) / 4;
+  return (int64_t)E * tiles * KC;
+}
+
+constexpr int kMaxLds = 160 * 1024;
+
+struct ReadPlan {
+  int grid, ntm, lds;
+};
+
+// LDS layout of the reader: staged codes [4 KC][tp][32], d_a and -8 s_a [4 KC][8] f32, a
+// 16-byte zero slot, cross-wave sums [waves][ntm][16][8] f32, then the routed column list.
+// tp is the widest of 8, 4, 2, 1 image columns per pass that fits.
+inline bool plan_lds(ReadArgs& a, int ntm, int max_cols, int* total) {
+  for (int tp : {8, 4, 2, 1}) {
+    const int codes = 4 * a.KC * tp * 32;
+    const int dsz = 4 * a.KC * 8 * 4;
+    const int red = kWaves * ntm * 16 * 8 * 4;
+    const int cols = ((max_cols > 0 ? max_cols : 1) * 4 + 15) & ~15;
+    const int t = codes + 2 * dsz + 16 + red + cols;
+    if (t <= kMaxLds) {
+      a.tp = tp;
+      a.lds_da = codes;
+      a.lds_ms = codes + dsz;
+      a.lds_zero = codes + 2 * dsz;
+      a.lds_red = a.lds_zero + 16;
+      a.lds_cols = a.lds_red + red;
+      *total = t;
+      return true;
+    }
   }
-  QIMG_MMVQ_CASE(64, 8) QIMG_MMVQ_CASE(64, 16)
-  QIMG_MMVQ_CASE(32, 8) QIMG_MMVQ_CASE(32, 16)
-  QIMG_MMVQ_CASE(16, 8) QIMG_MMVQ_CASE(16, 16)
-#undef QIMG_MMVQ_CASE
-  return QIMG_EUNSUPPORTED;
+  return false;
+}
+
+template <bool DOTS>
+int launch_read(ReadArgs& a, int grid, int ntm, int lds, hipStream_t s) {
+  const void* fn = ntm == 1 ? (const void*)mmvq_tiled_kernel<1, DOTS>
+                 : ntm == 2 ? (const void*)mmvq_tiled_kernel<2, DOTS>
+                 : ntm == 3 ? (const void*)mmvq_tiled_kernel<3, DOTS>
+                            : (const void*)mmvq_tiled_kernel<4, DOTS>;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return QIMG_EHIP;
+  dim3 g(grid), b(kWaves * 64);
+  if (ntm == 1) hipLaunchKernelGGL((mmvq_tiled_kernel<1, DOTS>), g, b, lds, s, a);
+  else if (ntm == 2) hipLaunchKernelGGL((mmvq_tiled_kernel<2, DOTS>), g, b, lds, s, a);
+  else if (ntm == 3) hipLaunchKernelGGL((mmvq_tiled_kernel<3, DOTS>), g, b, lds, s, a);
+  else hipLaunchKernelGGL((mmvq_tiled_kernel<4, DOTS>), g, b, lds, s, a);
+  return launch_status();
+}
+
+inline int ntm_for(int64_t tiles_per_wg) {
+  return tiles_per_wg <= 1 ? 1 : tiles_per_wg <= 2 ? 2 : tiles_per_wg <= 3 ? 3 : 4;
+}
+
+// Ordinary readers: one workgroup per CU (fewer when there are fewer tiles); each takes a
+// contiguous run of tiles over the concatenated readers.
+template <bool DOTS>
+int run_ordinary(ReadArgs& a, hipStream_t s) {
+  const int tiles = a.tile_start[a.n_readers];
+  int G = cu_count();
+  if (tiles < G) G = tiles;
+  a.wg_per_unit = G;
+  a.tiles_total = tiles;
+  const int ntm = ntm_for((tiles + G - 1) / G);
+  int lds = 0;
+  if (!plan_lds(a, ntm, 0, &lds)) return QIMG_EUNSUPPORTED;
+  return launch_read<DOTS>(a, G, ntm, lds, s);
+}
+
+// Routed readers: E x (tile runs of about four tiles) workgroups.
+int run_routed(ReadArgs& a, int max_cols, hipStream_t s) {
+  const int tiles = a.tile_start[a.n_readers];
+  const int per = tiles < 4 ? tiles : 4;
+  a.wg_per_unit = (tiles + per - 1) / per;
+  a.tiles_total = tiles;
+  if ((int64_t)a.wg_per_unit * a.E > 0x7fffffff) return QIMG_EUNSUPPORTED;
+  const int ntm = ntm_for((tiles + a.wg_per_unit - 1) / a.wg_per_unit);
+  int lds = 0;
+  if (!plan_lds(a, ntm, max_cols, &lds)) return QIMG_EUNSUPPORTED;
+  return launch_read<false>(a, a.wg_per_unit * a.E, ntm, lds, s);
 }
 
 }  // namespace
@@ -748,11 +873,46 @@ int qimg_quantize_q8_1(const float* y, int64_t ldy, int32_t rows, const int32_t*
                      stream);
 }
 
-static int check_image(const void* img, int32_t rows, int32_t K) {
+
+int64_t qimg_q4_0_tiled_bytes(int32_t N, int32_t K, int32_t E) {
+  if (N <= 0 || E <= 0 || check_k(K) != QIMG_OK) return 0;
+  return tiled_chunks(N, K, E) * (1024 + 128);
+}
+
+int qimg_q4_0_tile(const void* qs, const void* d, int32_t N, int32_t K, int32_t E, void* tiled,
+                   void* stream) {
+  int st = check_k(K);
+  if (st) return st;
+  if (!qs || !d || !tiled || N <= 0 || E <= 0) return QIMG_EINVAL;
+  if (!al16(qs) || !al(d, 2) || !al16(tiled)) return QIMG_EALIGN;
+  const int Kb = K / 32;
+  const int64_t chunks = tiled_chunks(N, K, E);
+  const Span so = span(tiled, chunks * 1152);
+  if (overlap(so, span(qs, (int64_t)E * N * Kb * 16)) || overlap(so, span(d, (int64_t)E * N * Kb * 2)))
+    return QIMG_EALIAS;
+  const int64_t total = chunks * 64;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(tile_q4_0_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const uint8_t*)qs, (const uint16_t*)d, N, Kb, (Kb + 3) / 4, (N + 15) / 16, E,
+                     (uint8_t*)tiled, (uint16_t*)((uint8_t*)tiled + chunks * 1024));
+  return launch_status();
+}
+
+static int check_image(const void* img) {
   if (!img) return QIMG_EINVAL;
   if (!al16(img)) return QIMG_EALIGN;
-  (void)rows; (void)K;
   return QIMG_OK;
+}
+
+static void fill_common(ReadArgs& a, const void* img, int32_t rows, int32_t K) {
+  const int RB = row_blocks(K);
+  a.codes = (const uint8_t*)img;
+  a.ds = (const uint32_t*)((const uint8_t*)img + (size_t)rows * RB * 32);
+  a.RB = RB;
+  a.Kb = K / 32;
+  a.KC = (K / 32 + 3) / 4;
+  a.rows = rows;
 }
 
 int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
@@ -761,47 +921,40 @@ int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const voi
   if (st) return st;
   if (!readers || n_readers < 1 || n_readers > QIMG_MAX_READERS || rows < 0) return QIMG_EINVAL;
   if (rows == 0) return QIMG_OK;
-  if ((st = check_image(img, rows, K))) return st;
+  if ((st = check_image(img))) return st;
   if (live_rows && !al(live_rows, 4)) return QIMG_EALIGN;
-  const int Kb = K / 32;
   const Span si = span(img, qimg_image_bytes(rows, K));
   const Span sl = live_rows ? span(live_rows, 4) : Span{0, 0};
   Span outs[QIMG_MAX_READERS];
-  int64_t total_rows = 0;
   for (int i = 0; i < n_readers; ++i) {
     const qimg_q4_0_reader& r = readers[i];
-    if (!r.qs || !r.d || !r.out || r.N <= 0 || r.ldo < r.N) return QIMG_EINVAL;
-    if (!al16(r.qs) || !al(r.d, 4) || !al(r.out, 4)) return QIMG_EALIGN;
+    if (!r.w || !r.out || r.N <= 0 || r.ldo < r.N) return QIMG_EINVAL;
+    if (!al16(r.w) || !al(r.out, 4)) return QIMG_EALIGN;
     outs[i] = span(r.out, rows_extent(rows, r.ldo, r.N, 4));
-    const Span sq = span(r.qs, (int64_t)r.N * Kb * 16), sd = span(r.d, (int64_t)r.N * Kb * 2);
-    total_rows += r.N;
-    for (int j = 0; j < n_readers; ++j) {
-      const Span oq = span(readers[j].qs, (int64_t)readers[j].N * Kb * 16);
-      const Span od = span(readers[j].d, (int64_t)readers[j].N * Kb * 2);
-      if (overlap(outs[i], oq) || overlap(outs[i], od)) return QIMG_EALIAS;
-    }
-    if (overlap(outs[i], si) || overlap(outs[i], sl) || overlap(outs[i], sq) || overlap(outs[i], sd))
-      return QIMG_EALIAS;
+    for (int j = 0; j < n_readers; ++j)
+      if (overlap(outs[i], span(readers[j].w, qimg_q4_0_tiled_bytes(readers[j].N, K, 1))))
+        return QIMG_EALIAS;
+    if (overlap(outs[i], si) || overlap(outs[i], sl)) return QIMG_EALIAS;
     for (int j = 0; j < i; ++j)
       if (overlap(outs[i], outs[j])) return QIMG_EALIAS;
   }
-  const ReaderShape sh = reader_shape(Kb, total_rows, 1);
-  MmvqArgs a{};
+  ReadArgs a{};
   int tiles = 0;
   for (int i = 0; i < n_readers; ++i) {
     const qimg_q4_0_reader& r = readers[i];
-    a.r[i] = ReaderDesc{(const uint8_t*)r.qs, (const uint16_t*)r.d, r.out, r.ldo, r.N, 0};
+    const int64_t ch = tiled_chunks(r.N, K, 1);
+    a.r[i] = ReaderDesc{(const uint8_t*)r.w, (const uint16_t*)((const uint8_t*)r.w + ch * 1024),
+                        r.out, r.ldo, r.N, (r.N + 15) / 16};
     a.tile_start[i] = tiles;
-    tiles += (r.N + sh.TR - 1) / sh.TR;
+    tiles += (r.N + 15) / 16;
   }
   a.tile_start[n_readers] = tiles;
-  const int RB = row_blocks(K);
-  a.codes = (const uint8_t*)img;
-  a.ds = (const uint32_t*)((const uint8_t*)img + (size_t)rows * RB * 32);
+  fill_common(a, img, rows, K);
   a.live_rows = live_rows;
-  a.n_readers = n_readers; a.RB = RB; a.Kb = Kb; a.rows = rows; a.TR = sh.TR;
-  a.top_k = 1; a.E = 0; a.routed = 0; a.ids = nullptr; a.ws = nullptr;
-  return launch_mmvq(a, 1, rows, (hipStream_t)stream, sh);
+  a.n_readers = n_readers;
+  a.top_k = 1;
+  a.routed = 0;
+  return run_ordinary<false>(a, (hipStream_t)stream);
 }
 
 size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E) {
@@ -820,11 +973,10 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
       top_k <= 0 || !ids)
     return QIMG_EINVAL;
   if (bucket == 0) return QIMG_OK;
-  if ((st = check_image(img, bucket, K))) return st;
+  if ((st = check_image(img))) return st;
   if (!workspace || workspace_bytes < mmvq_id_workspace_bytes(bucket, top_k, E))
     return QIMG_EWORKSPACE;
   if (!al16(workspace) || !al(ids, 4) || (live_rows && !al(live_rows, 4))) return QIMG_EALIGN;
-  const int Kb = K / 32;
   const int64_t pairs = (int64_t)bucket * top_k;
   const Span si = span(img, qimg_image_bytes(bucket, K));
   const Span sids = span(ids, pairs * 4);
@@ -832,66 +984,68 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
   const Span sw = span(workspace, (int64_t)mmvq_id_workspace_bytes(bucket, top_k, E));
   if (overlap(sw, si) || overlap(sw, sids) || overlap(sw, sl)) return QIMG_EALIAS;
   Span outs[QIMG_MAX_READERS];
-  int maxN = 0;
   for (int i = 0; i < n_readers; ++i) {
     const qimg_q4_0_expert_reader& r = readers[i];
-    if (!r.qs || !r.d || !r.out || r.N <= 0 || r.ld_pair < r.N) return QIMG_EINVAL;
-    if (!al16(r.qs) || !al(r.d, 4) || !al(r.out, 4)) return QIMG_EALIGN;
+    if (!r.w || !r.out || r.N <= 0 || r.ld_pair < r.N) return QIMG_EINVAL;
+    if (!al16(r.w) || !al(r.out, 4)) return QIMG_EALIGN;
     outs[i] = span(r.out, rows_extent(pairs, r.ld_pair, r.N, 4));
-    for (int j = 0; j < n_readers; ++j) {
-      const Span oq = span(readers[j].qs, (int64_t)E * readers[j].N * Kb * 16);
-      const Span od = span(readers[j].d, (int64_t)E * readers[j].N * Kb * 2);
-      if (overlap(outs[i], oq) || overlap(outs[i], od)) return QIMG_EALIAS;
-    }
+    for (int j = 0; j < n_readers; ++j)
+      if (overlap(outs[i], span(readers[j].w, qimg_q4_0_tiled_bytes(readers[j].N, K, E))))
+        return QIMG_EALIAS;
     if (overlap(outs[i], si) || overlap(outs[i], sids) || overlap(outs[i], sl) ||
         overlap(outs[i], sw))
       return QIMG_EALIAS;
     for (int j = 0; j < i; ++j)
       if (overlap(outs[i], outs[j])) return QIMG_EALIAS;
-    if (r.N > maxN) maxN = r.N;
   }
-  const ReaderShape sh = reader_shape(Kb, maxN, E);
-  MmvqArgs a{};
+  if (pairs > (1 << 24)) return QIMG_EUNSUPPORTED;
+  ReadArgs a{};
   int tiles = 0;
   for (int i = 0; i < n_readers; ++i) {
     const qimg_q4_0_expert_reader& r = readers[i];
-    a.r[i] = ReaderDesc{(const uint8_t*)r.qs, (const uint16_t*)r.d, r.out, r.ld_pair, r.N, 0};
+    const int64_t ch = tiled_chunks(r.N, K, E);
+    a.r[i] = ReaderDesc{(const uint8_t*)r.w, (const uint16_t*)((const uint8_t*)r.w + ch * 1024),
+                        r.out, r.ld_pair, r.N, (r.N + 15) / 16};
     a.tile_start[i] = tiles;
-    tiles += (r.N + sh.TR - 1) / sh.TR;
+    tiles += (r.N + 15) / 16;
   }
   a.tile_start[n_readers] = tiles;
-  if ((int64_t)tiles * E > 0x7fffffff) return QIMG_EUNSUPPORTED;
-  const int RB = row_blocks(K);
-  a.codes = (const uint8_t*)img;
-  a.ds = (const uint32_t*)((const uint8_t*)img + (size_t)bucket * RB * 32);
+  fill_common(a, img, bucket, K);
   a.live_rows = live_rows;
   a.ids = ids;
   a.ws = (int32_t*)workspace;
-  a.n_readers = n_readers; a.RB = RB; a.Kb = Kb; a.rows = bucket; a.TR = sh.TR;
-  a.top_k = top_k; a.E = E; a.routed = 1;
-  return launch_mmvq(a, E, (int)pairs, (hipStream_t)stream, sh);
+  a.n_readers = n_readers;
+  a.top_k = top_k;
+  a.E = E;
+  a.routed = 1;
+  return run_routed(a, (int)pairs, (hipStream_t)stream);
 }
 
 int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, int32_t rows,
                              int32_t K, int32_t* sumi, void* stream) {
   int st = check_k(K);
   if (st) return st;
-  if (!reader || !sumi || rows < 0 || !reader->qs || reader->N <= 0) return QIMG_EINVAL;
+  if (!reader || !sumi || rows < 0 || !reader->w || reader->N <= 0) return QIMG_EINVAL;
   if (rows == 0) return QIMG_OK;
-  if ((st = check_image(img, rows, K))) return st;
-  if (!al16(reader->qs) || !al(sumi, 4)) return QIMG_EALIGN;
+  if ((st = check_image(img))) return st;
+  if (!al16(reader->w) || !al(sumi, 4)) return QIMG_EALIGN;
   const int Kb = K / 32;
-  const int64_t total = (int64_t)rows * reader->N * Kb;
-  const Span ss = span(sumi, total * 4);
+  const Span ss = span(sumi, (int64_t)rows * reader->N * Kb * 4);
   if (overlap(ss, span(img, qimg_image_bytes(rows, K))) ||
-      overlap(ss, span(reader->qs, (int64_t)reader->N * Kb * 16)))
+      overlap(ss, span(reader->w, qimg_q4_0_tiled_bytes(reader->N, K, 1))))
     return QIMG_EALIAS;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(blockdots_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                     (const uint8_t*)reader->qs, reader->N, Kb, (const uint8_t*)img,
-                     row_blocks(K), rows, sumi);
-  return launch_status();
+  ReadArgs a{};
+  const int64_t ch = tiled_chunks(reader->N, K, 1);
+  a.r[0] = ReaderDesc{(const uint8_t*)reader->w, (const uint16_t*)((const uint8_t*)reader->w + ch * 1024),
+                      nullptr, 0, reader->N, (reader->N + 15) / 16};
+  a.tile_start[0] = 0;
+  a.tile_start[1] = (reader->N + 15) / 16;
+  fill_common(a, img, rows, K);
+  a.sumi = sumi;
+  a.n_readers = 1;
+  a.top_k = 1;
+  a.routed = 0;
+  return run_ordinary<true>(a, (hipStream_t)stream);
 }
 
 }  // extern "C"

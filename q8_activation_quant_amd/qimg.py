@@ -18,12 +18,13 @@ GLU_SWIGLU, GLU_GEGLU_ERF = 0, 1
 GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 1
+ABI_VERSION = 3
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
     "qimg_emit_rmsnorm", "qimg_emit_glu", "qimg_quantize_q8_1", "mmvq_q4_0_q8_1",
     "mmvq_id_workspace_bytes", "mmvq_id_q4_0_q8_1", "mmvq_q4_0_q8_1_blockdots",
+    "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile",
 )
 
 
@@ -34,13 +35,13 @@ class QimgError(RuntimeError):
 
 
 class Reader(ctypes.Structure):
-    _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("N", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64)]
+    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64)]
 
 
 class ExpertReader(ctypes.Structure):
-    _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("N", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("out", ctypes.c_void_p), ("ld_pair", ctypes.c_int64)]
+    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("ld_pair", ctypes.c_int64)]
 
 
 _lib = None
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "mmvq_id_q4_0_q8_1": (ctypes.c_int, [ctypes.POINTER(ExpertReader), i32, i32, P, P, i32,
                                                  i32, P, i32, P, ctypes.c_size_t, P]),
             "mmvq_q4_0_q8_1_blockdots": (ctypes.c_int, [ctypes.POINTER(Reader), P, i32, i32, P, P]),
+            "qimg_q4_0_tiled_bytes": (i64, [i32, i32, i32]),
+            "qimg_q4_0_tile": (ctypes.c_int, [P, P, i32, i32, i32, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -139,24 +142,38 @@ def quantize_q8_1(y, img, live_rows=None, stream=None):
                                     _stream(stream)), "qimg_quantize_q8_1")
 
 
+def tiled_bytes(N, K, E=1):
+    return int(lib().qimg_q4_0_tiled_bytes(N, K, E))
+
+
+def tile_q4_0(qs, d, K, stream=None):
+    """Reorder standard Q4_0 planes (qs [.., N, K/32, 16] u8, d [.., N, K/32] fp16 bits) into
+    the readers' tiled order; returns a new uint8 device tensor."""
+    import torch
+    N = qs.shape[-3]
+    E = 1 if qs.dim() == 3 else qs.shape[0]
+    out = torch.empty(tiled_bytes(N, K, E), dtype=torch.uint8, device=qs.device)
+    _check(lib().qimg_q4_0_tile(_ptr(qs), _ptr(d), N, K, E, _ptr(out), _stream(stream)), "qimg_q4_0_tile")
+    return out
+
+
 def _readers(specs, cls):
+    """specs: [(tiled weights tensor, N, out tensor)]."""
     arr = (cls * len(specs))()
-    for i, (qs, d, out) in enumerate(specs):
-        N = qs.shape[-3]
-        arr[i] = cls(ctypes.c_void_p(qs.data_ptr()), ctypes.c_void_p(d.data_ptr()), N, 0,
-                     ctypes.c_void_p(out.data_ptr()), out.stride(-2))
+    for i, (w, N, out) in enumerate(specs):
+        arr[i] = cls(ctypes.c_void_p(w.data_ptr()), N, 0, ctypes.c_void_p(out.data_ptr()), out.stride(-2))
     return arr
 
 
 def mmvq(readers, img, rows, K, live_rows=None, stream=None):
-    """Ordinary readers: readers = [(qs [N,K/32,16] u8, d [N,K/32] fp16 bits, out [rows,N] f32)]."""
+    """Ordinary readers: readers = [(tiled weights, N, out [rows, N] f32)]."""
     arr = _readers(readers, Reader)
     _check(lib().mmvq_q4_0_q8_1(arr, len(readers), _ptr(img), rows, _ptr(live_rows), K,
                                 _stream(stream)), "mmvq_q4_0_q8_1")
 
 
 def mmvq_id(readers, E, img, ids, live_rows, K, workspace, stream=None):
-    """Routed readers: readers = [(qs [E,N,K/32,16], d [E,N,K/32], out [bucket,top_k,N])];
+    """Routed readers: readers = [(tiled weights of E experts, N, out [bucket, top_k, N])];
     ids [bucket, top_k] int32; live_rows: int32 device tensor of one element, or None."""
     bucket, top_k = ids.shape
     arr = _readers(readers, ExpertReader)
@@ -165,10 +182,8 @@ def mmvq_id(readers, E, img, ids, live_rows, K, workspace, stream=None):
                                    _stream(stream)), "mmvq_id_q4_0_q8_1")
 
 
-def blockdots(qs, d, img, rows, K, sumi, stream=None):
-    """sumi [rows, N, K/32] int32 of one ordinary reader (debug export)."""
-    N = qs.shape[0]
-    r = Reader(ctypes.c_void_p(qs.data_ptr()), ctypes.c_void_p(d.data_ptr()), N, 0,
-               ctypes.c_void_p(sumi.data_ptr()), N)
+def blockdots(w, N, img, rows, K, sumi, stream=None):
+    """sumi [rows, N, K/32] int32: the block dots of one reader's tiled weights (debug export)."""
+    r = Reader(ctypes.c_void_p(w.data_ptr()), N, 0, ctypes.c_void_p(sumi.data_ptr()), N)
     _check(lib().mmvq_q4_0_q8_1_blockdots(ctypes.byref(r), _ptr(img), rows, K, _ptr(sumi),
                                           _stream(stream)), "mmvq_q4_0_q8_1_blockdots")
