@@ -327,57 +327,71 @@ struct ReadArgs {
   int32_t lds_da, lds_ms, lds_zero, lds_red, lds_cols;  // byte offsets (codes at 0)
 };
 
-// Stage image columns [c0, c0 + nc) in LDS. Column c is image row c (ordinary) or
-// cols[c] / top_k (routed). Loads are issued in batches of 8 per thread before their stores.
-__device__ __forceinline__ void stage_columns(const ReadArgs& p, unsigned char* smem,
-                                              const int32_t* cols, int c0, int nc) {
-  const int Kbp = 4 * p.KC, TP = p.tp;
+// Staging of image columns [c0, c0 + nc), blocks [b0, b1), in LDS, by one wave for the blocks
+// of its own K range (no workgroup barrier: the LDS operations of one wave complete in order).
+// Column c is image row c (ordinary) or cols[c] / top_k (routed). A batch is up to 8 codes
+// items (16 bytes) and 8 scale items per lane. Its loads are unconditional (in-bounds
+// addresses; padding items are zeroed at the store), so when the first batch is issued before
+// the first weight loads, its stores wait for it alone while the weights stay in flight.
+struct StageBatch {
+  uint4 v[8];
+  uint32_t dsw[8];
+};
+
+template <bool ROUTED>
+__device__ __forceinline__ void stage_issue(const ReadArgs& p, const int32_t* cols, int c0, int nc,
+                                            int b0, int b1, int base, StageBatch& sb) {
+  const int TP = p.tp;
+  const int nitems = (b1 - b0) * TP * 2;  // (block, column, half)
+  const int nds = (b1 - b0) * 8;          // (block, column slot of 8)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = base + j * 64;
+    const int half = i & 1, t = (i >> 1) % TP, b = b0 + (i >> 1) / TP;
+    const bool ok = i < nitems && t < nc && b < p.Kb;
+    const int c = c0 + (ok ? t : 0);
+    const int irow = ROUTED ? cols[c] / p.top_k : c;
+    const uint32_t off = ok ? (uint32_t)(irow * p.RB + b) * 32u + 16u * half : 0u;
+    sb.v[j] = *reinterpret_cast<const uint4*>(p.codes + off);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = base + j * 64;
+    const int t = i & 7, b = b0 + (i >> 3);
+    const bool ok = i < nds && t < nc && b < p.Kb;
+    const int c = c0 + (ok ? t : 0);
+    const int irow = ROUTED ? cols[c] / p.top_k : c;
+    sb.dsw[j] = p.ds[ok ? (uint32_t)(irow * p.RB + b) : 0u];
+  }
+}
+
+__device__ __forceinline__ void stage_store(const ReadArgs& p, unsigned char* smem, int nc, int b0,
+                                            int b1, int base, const StageBatch& sb) {
+  const int TP = p.tp;
   float* daL = reinterpret_cast<float*>(smem + p.lds_da);
   float* msL = reinterpret_cast<float*>(smem + p.lds_ms);
-  const int nitems = Kbp * TP * 2;  // (block, column, half)
-  for (int base = threadIdx.x; base < nitems; base += 8 * blockDim.x) {
-    uint4 v[8];
+  const int nitems = (b1 - b0) * TP * 2;
+  const int nds = (b1 - b0) * 8;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * blockDim.x;
-      const int half = i & 1, t = (i >> 1) % TP, b = (i >> 1) / TP;
-      v[j] = make_uint4(0, 0, 0, 0);
-      if (i < nitems && t < nc && b < p.Kb) {
-        const int c = c0 + t;
-        const int irow = p.routed ? cols[c] / p.top_k : c;
-        v[j] = reinterpret_cast<const uint4*>(p.codes + ((int64_t)irow * p.RB + b) * 32)[half];
-      }
-    }
+  for (int j = 0; j < 8; ++j) {
+    const int i = base + j * 64;
+    const int t = (i >> 1) % TP, b = b0 + (i >> 1) / TP;
+    if (i < nitems)
+      reinterpret_cast<uint4*>(smem)[b0 * TP * 2 + i] =
+          (t < nc && b < p.Kb) ? sb.v[j] : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * blockDim.x;
-      if (i < nitems) reinterpret_cast<uint4*>(smem)[i] = v[j];  // (b*TP + t)*32 + 16*half
+  for (int j = 0; j < 8; ++j) {
+    const int i = base + j * 64;
+    const int t = i & 7, b = b0 + (i >> 3);
+    const uint32_t w = (t < nc && b < p.Kb) ? sb.dsw[j] : 0u;
+    if (i < nds) {
+      daL[b0 * 8 + i] = h2f(w);
+      msL[b0 * 8 + i] = -8.0f * h2f(w >> 16);
     }
   }
-  const int nds = Kbp * 8;  // (block, column slot of 8)
-  for (int base = threadIdx.x; base < nds; base += 8 * blockDim.x) {
-    uint32_t dsw[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * blockDim.x;
-      const int t = i & 7, b = i >> 3;
-      dsw[j] = 0u;
-      if (i < nds && t < nc && b < p.Kb) {
-        const int c = c0 + t;
-        const int irow = p.routed ? cols[c] / p.top_k : c;
-        dsw[j] = p.ds[(int64_t)irow * p.RB + b];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * blockDim.x;
-      if (i < nds) {
-        daL[i] = h2f(dsw[j]);
-        msL[i] = -8.0f * h2f(dsw[j] >> 16);
-      }
-    }
-  }
-  if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[threadIdx.x] = 0u;
+  const int lane = threadIdx.x & 63;
+  if (lane < 4) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[lane] = 0u;  // own zero slot
 }
 
 // Stable scan of the live pairs routed to expert e: cols[0..n) = pair ids in ascending order.
@@ -439,10 +453,12 @@ __device__ int scan_expert(const ReadArgs& p, int e, int live, int clamped, bool
   return base;
 }
 
-template <int NTM, bool DOTS>
+// MODE: 0 ordinary readers, 1 routed readers, 2 block-dot export (ordinary).
+template <int NTM, int MODE>
 __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
+  constexpr bool DOTS = MODE == 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int KU = NTM <= 2 ? 4 : 2;  // chunks per prefetch batch (two batches in flight)
+  constexpr int KU = NTM <= 2 ? 2 : 1;  // chunks per prefetch batch (two batches in flight)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int KC = p.KC, TP = p.tp;
@@ -458,7 +474,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   const float* msL = reinterpret_cast<const float*>(smem + p.lds_ms);
   float* red = reinterpret_cast<float*>(smem + p.lds_red);
 
-  const int ncols = p.routed ? scan_expert(p, unit, live, clamped, wgi == 0, cols) : live;
+  const int ncols = MODE == 1 ? scan_expert(p, unit, live, clamped, wgi == 0, cols) : live;
   if (ncols == 0 || t0 >= t1) return;
 
   for (int c0 = 0; c0 < ncols; c0 += TP) {
@@ -564,11 +580,25 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
           }
         }
       };
-      if (cs1 > cs0) load(qa, da_, cs0);  // weight loads fly while the image is staged
       if (tb == t0) {
-        __syncthreads();  // the previous column pass is done with LDS
-        stage_columns(p, smem, cols, c0, nc);
-        __syncthreads();
+        // Stage this wave's blocks of the image columns: the first batch's loads go out before
+        // the first weight batch and are stored while those weights are in flight.
+        const int b0 = 4 * cs0, b1 = 4 * cs1;
+        const int nitems = (b1 - b0) * TP * 2;
+        const int nbat = (nitems + 511) / 512 > (b1 - b0 + 63) / 64 ? (nitems + 511) / 512
+                                                                    : (b1 - b0 + 63) / 64;
+        StageBatch sb;
+        stage_issue<MODE == 1>(p, cols, c0, nc, b0, b1, lane, sb);
+        if (cs1 > cs0) load(qa, da_, cs0);
+        stage_store(p, smem, nc, b0, b1, lane, sb);
+        for (int bt = 1; bt < nbat; ++bt) {
+          stage_issue<MODE == 1>(p, cols, c0, nc, b0, b1, lane + 512 * bt, sb);
+          stage_store(p, smem, nc, b0, b1, lane + 512 * bt, sb);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // staged LDS before reads
+        __builtin_amdgcn_wave_barrier();
+      } else if (cs1 > cs0) {
+        load(qa, da_, cs0);
       }
       for (int kb = cs0; kb < cs1; kb += 2 * KU) {
         load(qb, db_, kb + KU);
@@ -582,8 +612,14 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
         for (int t = 0; t < NTM; ++t)
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            acc[t][v] = acc[t][v] + __shfl_xor(acc[t][v], 16, 64);
-            acc[t][v] = acc[t][v] + __shfl_xor(acc[t][v], 32, 64);
+            // v_permlane16_swap of a value with itself yields rows (r0 r0 r2 r2) and
+            // (r1 r1 r3 r3): their sum is the lane-xor-16 pair sum; likewise permlane32
+            const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[t][v]),
+                                                              __float_as_uint(acc[t][v]), false, false);
+            const float a16 = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+            const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a16),
+                                                              __float_as_uint(a16), false, false);
+            acc[t][v] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
           }
         // lane (n, g) stores columns 2g, 2g+1 of its row for each tile
 #pragma unroll
@@ -603,7 +639,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
             if (row < p.r[ri].N) {
               float s = red[(t * 16 + nn) * 8 + col];
               for (int ww = 1; ww < kWaves; ++ww) s = s + red[((ww * NTM + t) * 16 + nn) * 8 + col];
-              const int orow = p.routed ? cols[c0 + col] : c0 + col;
+              const int orow = MODE == 1 ? cols[c0 + col] : c0 + col;
               p.r[ri].out[(int64_t)orow * p.r[ri].ld + row] = s;
             }
           }
@@ -740,20 +776,20 @@ inline bool plan_lds(ReadArgs& a, int ntm, int max_cols, int* total) {
   return false;
 }
 
-template <bool DOTS>
+template <int MODE>
 int launch_read(ReadArgs& a, int grid, int ntm, int lds, hipStream_t s) {
-  const void* fn = ntm == 1 ? (const void*)mmvq_tiled_kernel<1, DOTS>
-                 : ntm == 2 ? (const void*)mmvq_tiled_kernel<2, DOTS>
-                 : ntm == 3 ? (const void*)mmvq_tiled_kernel<3, DOTS>
-                            : (const void*)mmvq_tiled_kernel<4, DOTS>;
+  const void* fn = ntm == 1 ? (const void*)mmvq_tiled_kernel<1, MODE>
+                 : ntm == 2 ? (const void*)mmvq_tiled_kernel<2, MODE>
+                 : ntm == 3 ? (const void*)mmvq_tiled_kernel<3, MODE>
+                            : (const void*)mmvq_tiled_kernel<4, MODE>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
   dim3 g(grid), b(kWaves * 64);
-  if (ntm == 1) hipLaunchKernelGGL((mmvq_tiled_kernel<1, DOTS>), g, b, lds, s, a);
-  else if (ntm == 2) hipLaunchKernelGGL((mmvq_tiled_kernel<2, DOTS>), g, b, lds, s, a);
-  else if (ntm == 3) hipLaunchKernelGGL((mmvq_tiled_kernel<3, DOTS>), g, b, lds, s, a);
-  else hipLaunchKernelGGL((mmvq_tiled_kernel<4, DOTS>), g, b, lds, s, a);
+  if (ntm == 1) hipLaunchKernelGGL((mmvq_tiled_kernel<1, MODE>), g, b, lds, s, a);
+  else if (ntm == 2) hipLaunchKernelGGL((mmvq_tiled_kernel<2, MODE>), g, b, lds, s, a);
+  else if (ntm == 3) hipLaunchKernelGGL((mmvq_tiled_kernel<3, MODE>), g, b, lds, s, a);
+  else hipLaunchKernelGGL((mmvq_tiled_kernel<4, MODE>), g, b, lds, s, a);
   return launch_status();
 }
 
@@ -763,7 +799,7 @@ inline int ntm_for(int64_t tiles_per_wg) {
 
 // Ordinary readers: one workgroup per CU (fewer when there are fewer tiles); each takes a
 // contiguous run of tiles over the concatenated readers.
-template <bool DOTS>
+template <int MODE>
 int run_ordinary(ReadArgs& a, hipStream_t s) {
   const int tiles = a.tile_start[a.n_readers];
   int G = cu_count();
@@ -773,7 +809,7 @@ int run_ordinary(ReadArgs& a, hipStream_t s) {
   const int ntm = ntm_for((tiles + G - 1) / G);
   int lds = 0;
   if (!plan_lds(a, ntm, 0, &lds)) return QIMG_EUNSUPPORTED;
-  return launch_read<DOTS>(a, G, ntm, lds, s);
+  return launch_read<MODE>(a, G, ntm, lds, s);
 }
 
 // Routed readers: E x (tile runs of about four tiles) workgroups.
@@ -786,7 +822,7 @@ int run_routed(ReadArgs& a, int max_cols, hipStream_t s) {
   const int ntm = ntm_for((tiles + a.wg_per_unit - 1) / a.wg_per_unit);
   int lds = 0;
   if (!plan_lds(a, ntm, max_cols, &lds)) return QIMG_EUNSUPPORTED;
-  return launch_read<false>(a, a.wg_per_unit * a.E, ntm, lds, s);
+  return launch_read<1>(a, a.wg_per_unit * a.E, ntm, lds, s);
 }
 
 }  // namespace
@@ -954,7 +990,7 @@ int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const voi
   a.n_readers = n_readers;
   a.top_k = 1;
   a.routed = 0;
-  return run_ordinary<false>(a, (hipStream_t)stream);
+  return run_ordinary<0>(a, (hipStream_t)stream);
 }
 
 size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E) {
@@ -1045,7 +1081,7 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
   a.n_readers = 1;
   a.top_k = 1;
   a.routed = 0;
-  return run_ordinary<true>(a, (hipStream_t)stream);
+  return run_ordinary<2>(a, (hipStream_t)stream);
 }
 
 }  // extern "C"
