@@ -262,6 +262,9 @@ def main():
     ap.add_argument("--glu", default="swiglu", choices=["swiglu", "geglu_erf"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print one extra line per workload")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="counter-collection run: one reader launch per rotated instance of the "
+                         "workload, then a plain 256 MiB device copy (the calibration kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the design notes "
@@ -272,6 +275,24 @@ def main():
     from q8_activation_quant_amd import qimg
     qimg.lib()
 
+    if args.pmc_probe:
+        from q8_activation_quant_amd import workloads as W
+        wl = W.make(args.config, live=args.live, glu_op=args.glu)
+        insts = make_instances(wl)
+        for i in insts:
+            i.produce(True)
+        torch.cuda.synchronize()
+        for i in insts:
+            i.read()
+        torch.cuda.synchronize()
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_probe": WORKLOAD_NAMES[args.config], "reader_launches": len(insts),
+                          "reader_algorithmic_bytes": algorithmic_bytes(wl)["reader_kernel"],
+                          "calibration_copy_bytes": src.numel()}), flush=True)
+        return
     r = run(args.config, args.steps, args.warmup, live=args.live, glu_op=args.glu, want_cpu=not args.no_cpu)
     wl, nb = r["wl"], r["bytes"]
     us = r["us"]["fused"]
@@ -302,7 +323,7 @@ def main():
         "producer_us": round(r["producer_us"], 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "mmvq_kernel (Q4_0 x Q8_1 readers)",
+            "kernel": "mmvq_tiled_kernel (Q4_0 x Q8_1 readers)",
             "achieved": round(reader_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

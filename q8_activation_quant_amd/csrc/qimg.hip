@@ -51,6 +51,40 @@ __device__ __forceinline__ int clamp_live(const int32_t* live_rows, int rows, in
   return live;
 }
 
+// Cross-lane moves without LDS: DPP (quad_perm, row mirrors) within a 16-lane row, and the
+// gfx950 permlane swaps across rows. pair_sum_* return v(l) + v(partner) where the partner set
+// pairs lanes exactly as a balanced pairwise tree over lane index needs when every lane of a
+// group already holds that group's value (the sum of a pair is the same in both lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_n(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16 lanes
+__device__ __forceinline__ float pair_sum_rows(float v) {  // lanes l and l ^ 16
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float pair_sum_halves(float v) {  // lanes l and l ^ 32
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// Balanced pairwise tree over the 64 lanes in lane order (every lane receives the total).
+__device__ __forceinline__ float wave_tree_sum(float v) {
+  v = v + dpp_f<kDppXor1>(v);
+  v = v + dpp_f<kDppXor2>(v);
+  v = v + dpp_f<kDppHalfMirror>(v);
+  v = v + dpp_f<kDppMirror>(v);
+  v = pair_sum_rows(v);
+  return pair_sum_halves(v);
+}
+
 // exp_q: Cody-Waite reduction by ln 2 split into a 12-bit-short high part and an f32 low part,
 // degree-7 Taylor polynomial of e^r with coefficients 1/k! rounded to f32 (Horner, fma), then
 // scaling by 2^n. NaN passes through, x > 88.8 gives +inf, x < -86 gives +0 (no subnormal
@@ -150,9 +184,10 @@ __device__ __forceinline__ float tree_sum(float (&v)[JW]) {
 __device__ __forceinline__ void quantize_leaf(const float4 y, int row, int blk, int lane,
                                               const EmitArgs& p) {
   float amax = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  // group of 8 lanes: max is exact in any order
+  amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+  amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+  amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
   uint32_t packed = 0, dsw = 0;
   int sum = 0;
   const float d = amax / 127.0f;
@@ -167,9 +202,9 @@ __device__ __forceinline__ void quantize_leaf(const float4 y, int row, int blk, 
              ((uint32_t)(c2 & 0xff) << 16) | ((uint32_t)(c3 & 0xff) << 24);
     sum = c0 + c1 + c2 + c3;
   }
-  sum += __shfl_xor(sum, 1, 64);
-  sum += __shfl_xor(sum, 2, 64);
-  sum += __shfl_xor(sum, 4, 64);
+  sum += dpp_n<kDppXor1>(sum);
+  sum += dpp_n<kDppXor2>(sum);
+  sum += dpp_n<kDppHalfMirror>(sum);
   if (!zero) dsw = f2h(d) | (f2h((float)sum * d) << 16);
   const int64_t blk_idx = (int64_t)row * p.RB + blk;
   reinterpret_cast<uint32_t*>(p.codes)[blk_idx * 8 + (lane & 7)] = packed;
@@ -186,11 +221,17 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
   const int C = p.K >> 2;
   const float* arow = p.a + (int64_t)row * p.lda;
 
-  float4 v[JW];
+  // all input loads of the row go out at once (in bounds: leaves past K re-read leaf 0 and
+  // are zeroed): x (or gate, or y) and gamma (or up)
+  float4 v[JW], u[JW];
+  const float* brow = (OP == OP_SWIGLU || OP == OP_GEGLU) ? p.b + (int64_t)row * p.ldb : p.b;
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj) {
     const int c = lane + 64 * (w * JW + jj);
-    v[jj] = c < C ? *reinterpret_cast<const float4*>(arow + 4 * c) : make_float4(0, 0, 0, 0);
+    const int cc = c < C ? c : 0;
+    v[jj] = *reinterpret_cast<const float4*>(arow + 4 * cc);
+    if (c >= C) v[jj] = make_float4(0, 0, 0, 0);
+    if (OP != OP_QUANT && brow) u[jj] = *reinterpret_cast<const float4*>(brow + 4 * cc);
   }
 
   if constexpr (OP == OP_RMS) {
@@ -210,9 +251,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (i < n / 2) t[i] = t[2 * i] + t[2 * i + 1];
-    float S = t[0];
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) S = S + __shfl_xor(S, m, 64);
+    const float S = wave_tree_sum(t[0]);
     const float mean = S / (float)p.K;
     const float r = 1.0f / __builtin_sqrtf(mean + p.eps);
 #pragma unroll
@@ -221,25 +260,24 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
       float4 y;
       y.x = v[jj].x * r; y.y = v[jj].y * r; y.z = v[jj].z * r; y.w = v[jj].w * r;
       if (p.b && c < C) {
-        const float4 g = *reinterpret_cast<const float4*>(p.b + 4 * c);
+        const float4 g = u[jj];
         y.x = y.x * g.x; y.y = y.y * g.y; y.z = y.z * g.z; y.w = y.w * g.w;
       }
       v[jj] = y;
     }
   } else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU) {
-    const float* brow = p.b + (int64_t)row * p.ldb;
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
       const int c = lane + 64 * (w * JW + jj);
       if (c < C) {
-        const float4 u = *reinterpret_cast<const float4*>(brow + 4 * c);
+        const float4 uu = u[jj];
         float4 y;
         if constexpr (OP == OP_SWIGLU) {
-          y.x = swiglu_act(v[jj].x) * u.x; y.y = swiglu_act(v[jj].y) * u.y;
-          y.z = swiglu_act(v[jj].z) * u.z; y.w = swiglu_act(v[jj].w) * u.w;
+          y.x = swiglu_act(v[jj].x) * uu.x; y.y = swiglu_act(v[jj].y) * uu.y;
+          y.z = swiglu_act(v[jj].z) * uu.z; y.w = swiglu_act(v[jj].w) * uu.w;
         } else {
-          y.x = geglu_erf_act(v[jj].x) * u.x; y.y = geglu_erf_act(v[jj].y) * u.y;
-          y.z = geglu_erf_act(v[jj].z) * u.z; y.w = geglu_erf_act(v[jj].w) * u.w;
+          y.x = geglu_erf_act(v[jj].x) * uu.x; y.y = geglu_erf_act(v[jj].y) * uu.y;
+          y.z = geglu_erf_act(v[jj].z) * uu.z; y.w = geglu_erf_act(v[jj].w) * uu.w;
         }
         v[jj] = y;
       }
