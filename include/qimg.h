@@ -78,6 +78,8 @@ extern "C" {
 
 #define QIMG_MAX_K 32768
 #define QIMG_MAX_READERS 8
+#define QIMG_MAX_EXPERTS 1024       /* routed readers: E */
+#define QIMG_MAX_ROUTED_PAIRS 4096  /* routed readers: bucket * top_k */
 
 /* GLU producer formulas ([P1] Coverage: F32 SwiGLU and GeGLU-erf producers) */
 #define QIMG_GLU_SWIGLU 0    /* y = g / (1 + exp(-g)) * u                      */

@@ -11,10 +11,11 @@
 // Kernels
 //   emit_kernel<OP,JW>       one workgroup per live row: (RMS reduction) -> f32 output -> per
 //                            32-block Q8_1 quantization, all in one pass over the row.
-//   mmvq_tiled_kernel<N,D>   Q4_0 x Q8_1 readers on the matrix cores (v_mfma_i32_16x16x64_i8)
-//                            over tiled weights: ordinary readers take the live image rows as
-//                            columns, routed readers the live pairs of one expert, found by a
-//                            stable scan of the ids in the same launch. D: block-dot export.
+//   mmvq_tiled_kernel<N,M>   ordinary Q4_0 x Q8_1 readers on the matrix cores
+//                            (v_mfma_i32_16x16x64_i8) over tiled weights, the live image rows as
+//                            columns; M = 2: block-dot export.
+//   mmvq_routed_kernel<N,U>  routed readers: the plan of the live pairs built in LDS by every
+//                            workgroup, then (expert, pass, tile) units streamed over full K.
 //   tile_q4_0_kernel         one-time reordering of standard Q4_0 planes into reader tiles.
 //
 // Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off (no fast-math), so every float
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
 // n+32), then the waves' K ranges in ascending wave order. The sum for one output does not
 // depend on the other columns, the live count or the tiles of the workgroup.
 //
-// Image columns (live image rows, or a routed expert's live pairs) are staged in LDS per pass of
+// Image columns (live image rows; a routed expert's live pairs) are staged in LDS per pass of
 // up to 8: codes [block][column][32], d_a and -8 s_a as f32 [block][8].
 // ---------------------------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -358,16 +359,20 @@ struct ReadArgs {
   const int32_t* ids;  // routed: [bucket][top_k]
   int32_t* ws;         // routed: plan workspace
   int32_t* sumi;       // debug: block dots of reader 0, [rows][N][Kb]
-  int32_t n_readers, RB, Kb, KC, rows, top_k, E, routed;
-  int32_t wg_per_unit;  // workgroups per expert (routed) or in total (ordinary)
+  int32_t n_readers, RB, Kb, KC, rows, top_k, E;
   int32_t tiles_total;  // tiles per expert summed over readers
   int32_t tp;           // image columns per LDS pass (8, 4, 2 or 1)
-  int32_t lds_da, lds_ms, lds_zero, lds_red, lds_cols;  // byte offsets (codes at 0)
+  int32_t lds_da, lds_ms, lds_zero, lds_red;  // byte offsets (codes at 0)
+  // routed readers
+  int32_t lds_plan;     // byte offset of the plan arrays
+  int32_t slots;        // staged (expert, pass) segments per batch
+  int32_t slot_bytes;   // LDS bytes per staged segment
+  int32_t pairs_cap;    // bucket * top_k
 };
 
 // Staging of image columns [c0, c0 + nc), blocks [b0, b1), in LDS, by one wave for the blocks
 // of its own K range (no workgroup barrier: the LDS operations of one wave complete in order).
-// Column c is image row c (ordinary) or cols[c] / top_k (routed). A batch is up to 8 codes
+// Column c is image row c. A batch is up to 8 codes
 // items (16 bytes) and 8 scale items per lane. Its loads are unconditional (in-bounds
 // addresses; padding items are zeroed at the store), so when the first batch is issued before
 // the first weight loads, its stores wait for it alone while the weights stay in flight.
@@ -376,9 +381,8 @@ struct StageBatch {
   uint32_t dsw[8];
 };
 
-template <bool ROUTED>
-__device__ __forceinline__ void stage_issue(const ReadArgs& p, const int32_t* cols, int c0, int nc,
-                                            int b0, int b1, int base, StageBatch& sb) {
+__device__ __forceinline__ void stage_issue(const ReadArgs& p, int c0, int nc, int b0, int b1,
+                                            int base, StageBatch& sb) {
   const int TP = p.tp;
   const int nitems = (b1 - b0) * TP * 2;  // (block, column, half)
   const int nds = (b1 - b0) * 8;          // (block, column slot of 8)
@@ -388,7 +392,7 @@ __device__ __forceinline__ void stage_issue(const ReadArgs& p, const int32_t* co
     const int half = i & 1, t = (i >> 1) % TP, b = b0 + (i >> 1) / TP;
     const bool ok = i < nitems && t < nc && b < p.Kb;
     const int c = c0 + (ok ? t : 0);
-    const int irow = ROUTED ? cols[c] / p.top_k : c;
+    const int irow = c;
     const uint32_t off = ok ? (uint32_t)(irow * p.RB + b) * 32u + 16u * half : 0u;
     sb.v[j] = *reinterpret_cast<const uint4*>(p.codes + off);
   }
@@ -398,7 +402,7 @@ __device__ __forceinline__ void stage_issue(const ReadArgs& p, const int32_t* co
     const int t = i & 7, b = b0 + (i >> 3);
     const bool ok = i < nds && t < nc && b < p.Kb;
     const int c = c0 + (ok ? t : 0);
-    const int irow = ROUTED ? cols[c] / p.top_k : c;
+    const int irow = c;
     sb.dsw[j] = p.ds[ok ? (uint32_t)(irow * p.RB + b) : 0u];
   }
 }
@@ -432,66 +436,7 @@ __device__ __forceinline__ void stage_store(const ReadArgs& p, unsigned char* sm
   if (lane < 4) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[lane] = 0u;  // own zero slot
 }
 
-// Stable scan of the live pairs routed to expert e: cols[0..n) = pair ids in ascending order.
-// The workgroup of tile range 0 also writes expert e's plan entries ([P3] What this changes:
-// only the first live rows' pairs are planned; padding rows' ids are never read).
-__device__ int scan_expert(const ReadArgs& p, int e, int live, int clamped, bool write_plan,
-                           int32_t* cols) {
-  __shared__ int wave_cnt[kWaves];
-  __shared__ int red_i[4];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, NW = blockDim.x >> 6;
-  const int P = live * p.top_k;
-  if (threadIdx.x < 4) red_i[threadIdx.x] = 0;
-  __syncthreads();
-  int n_lt = 0, n_valid = 0, n_bad = 0, base = 0;
-  for (int p0 = 0; p0 < P; p0 += blockDim.x) {
-    const int pi = p0 + threadIdx.x;
-    const int id = pi < P ? p.ids[pi] : -1;
-    const bool valid = pi < P && id >= 0 && id < p.E;
-    n_bad += (pi < P && !valid) ? 1 : 0;
-    n_valid += valid ? 1 : 0;
-    n_lt += (valid && id < e) ? 1 : 0;
-    const bool match = valid && id == e;
-    const unsigned long long bal = __ballot(match);
-    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_cnt[w] = __popcll(bal);
-    __syncthreads();
-    int pre = 0, tot = 0;
-    for (int i = 0; i < NW; ++i) {
-      pre += i < w ? wave_cnt[i] : 0;
-      tot += wave_cnt[i];
-    }
-    if (match) cols[base + pre + rank] = pi;
-    base += tot;
-    __syncthreads();
-  }
-  if (write_plan) {
-    atomicAdd(&red_i[0], n_lt);
-    atomicAdd(&red_i[1], n_valid);
-    atomicAdd(&red_i[2], n_bad);
-    __syncthreads();
-    const int off = red_i[0];
-    int32_t* counts = p.ws + 4;
-    int32_t* offsets = counts + p.E;
-    int32_t* members = offsets + p.E + 1;
-    if (threadIdx.x == 0) {
-      counts[e] = base;
-      offsets[e] = off;
-    }
-    for (int i = threadIdx.x; i < base; i += blockDim.x) members[off + i] = cols[i];
-    if (e == 0 && threadIdx.x == 0) {
-      p.ws[0] = (red_i[2] ? QIMG_ERR_EXPERT_RANGE : 0) | (clamped ? QIMG_ERR_LIVE_CLAMPED : 0);
-      p.ws[1] = P;
-      p.ws[2] = 0;
-      p.ws[3] = 0;
-      offsets[p.E] = red_i[1];
-    }
-  }
-  __syncthreads();
-  return base;
-}
-
-// MODE: 0 ordinary readers, 1 routed readers, 2 block-dot export (ordinary).
+// MODE: 0 ordinary readers, 2 block-dot export.
 template <int NTM, int MODE>
 __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   constexpr bool DOTS = MODE == 2;
@@ -501,18 +446,15 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   const int n = lane & 15, g = lane >> 4;
   const int KC = p.KC, TP = p.tp;
   const int cs0 = KC * w / kWaves, cs1 = KC * (w + 1) / kWaves;
-  int clamped = 0;
-  const int live = DOTS ? p.rows : clamp_live(p.live_rows, p.rows, &clamped);
-  const int unit = blockIdx.x / p.wg_per_unit;  // expert (routed) or 0
-  const int wgi = blockIdx.x % p.wg_per_unit;
-  const int t0 = (int)((int64_t)p.tiles_total * wgi / p.wg_per_unit);
-  const int t1 = (int)((int64_t)p.tiles_total * (wgi + 1) / p.wg_per_unit);
-  int32_t* cols = reinterpret_cast<int32_t*>(smem + p.lds_cols);
+  const int live = DOTS ? p.rows : clamp_live(p.live_rows, p.rows, nullptr);
+  const int wgi = blockIdx.x;
+  const int t0 = (int)((int64_t)p.tiles_total * wgi / gridDim.x);
+  const int t1 = (int)((int64_t)p.tiles_total * (wgi + 1) / gridDim.x);
   const float* daL = reinterpret_cast<const float*>(smem + p.lds_da);
   const float* msL = reinterpret_cast<const float*>(smem + p.lds_ms);
   float* red = reinterpret_cast<float*>(smem + p.lds_red);
 
-  const int ncols = MODE == 1 ? scan_expert(p, unit, live, clamped, wgi == 0, cols) : live;
+  const int ncols = live;
   if (ncols == 0 || t0 >= t1) return;
 
   for (int c0 = 0; c0 < ncols; c0 += TP) {
@@ -541,7 +483,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
         const int lt = tile - p.tile_start[ri];
         rr[t] = ri;
         rl[t] = lt * 16 + n;  // this lane's weight row in reader ri
-        const int64_t chunk0 = ((int64_t)unit * p.r[ri].tiles + lt) * KC;
+        const int64_t chunk0 = (int64_t)lt * KC;
         qp[t] = reinterpret_cast<const uint4*>(p.r[ri].qs) + chunk0 * 64 + lane;
         dp[t] = p.r[ri].d + chunk0 * 64 + lane;
       }
@@ -626,11 +568,11 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
         const int nbat = (nitems + 511) / 512 > (b1 - b0 + 63) / 64 ? (nitems + 511) / 512
                                                                     : (b1 - b0 + 63) / 64;
         StageBatch sb;
-        stage_issue<MODE == 1>(p, cols, c0, nc, b0, b1, lane, sb);
+        stage_issue(p, c0, nc, b0, b1, lane, sb);
         if (cs1 > cs0) load(qa, da_, cs0);
         stage_store(p, smem, nc, b0, b1, lane, sb);
         for (int bt = 1; bt < nbat; ++bt) {
-          stage_issue<MODE == 1>(p, cols, c0, nc, b0, b1, lane + 512 * bt, sb);
+          stage_issue(p, c0, nc, b0, b1, lane + 512 * bt, sb);
           stage_store(p, smem, nc, b0, b1, lane + 512 * bt, sb);
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // staged LDS before reads
@@ -677,14 +619,461 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
             if (row < p.r[ri].N) {
               float s = red[(t * 16 + nn) * 8 + col];
               for (int ww = 1; ww < kWaves; ++ww) s = s + red[((ww * NTM + t) * 16 + nn) * 8 + col];
-              const int orow = MODE == 1 ? cols[c0 + col] : c0 + col;
-              p.r[ri].out[(int64_t)orow * p.r[ri].ld + row] = s;
+              p.r[ri].out[(int64_t)(c0 + col) * p.r[ri].ld + row] = s;
             }
           }
         }
         __syncthreads();
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Routed readers (MUL_MAT_ID).
+//
+// Plan ([P3] What this changes: only the live rows' pairs are planned, padding ids are never
+// read). Every workgroup builds the whole plan of the live pairs in LDS: per-expert counts
+// (LDS atomics), one scan giving each expert's offset, the ascending list of active experts
+// and their work-unit offsets, then the pairs placed by expert and re-ranked by pair id within
+// the expert (stable order). Workgroup 0 also writes the plan to the workspace.
+//
+// Work. A unit is one 16-row tile (over the concatenated readers) of one active expert for one
+// pass of up to TP of its pairs; units are ordered by (expert, pass, tile), and an (expert,
+// pass) is a segment of T units, T = tiles per expert. Workgroup i takes units
+// [U i / G, U (i + 1) / G). It stages the image columns of up to `slots` of its segments at a
+// time in LDS (all K blocks), then its waves split that batch's units contiguously. A wave
+// streams groups of up to NTM consecutive tiles of one segment over the full K, KU chunks per
+// load, two loads in flight; the loads of the next group are issued before the current group
+// ends, so a wave's stream does not drain between groups. After the last chunk of a group the
+// four k-group lanes of each row are summed and the lanes store their outputs directly. The
+// sum for a pair depends only on that pair's image row and expert (chunks in K order, then the
+// fixed lane tree): not on the other pairs, the live count or the schedule.
+// ---------------------------------------------------------------------------------------------
+constexpr int kRoutedMaxSlots = 4;
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+template <int NTM, int KU>
+__global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int sh_wave[3][kWaves];
+  __shared__ int sh_misc[4];                  // bad ids, active experts A, units U, unused
+  __shared__ int sh_seg[kRoutedMaxSlots][4];  // start unit, expert, columns, first member
+  __shared__ int sh_batch[2];                 // batch end unit, segments in the batch
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int n = lane & 15, g = lane >> 4;
+  const int E = p.E, T = p.tiles_total, TP = p.tp, KC = p.KC;
+  int clamped = 0;
+  const int live = clamp_live(p.live_rows, p.rows, &clamped);
+  const int P = live * p.top_k;  // <= rows * top_k = pairs_cap
+
+  int32_t* off = reinterpret_cast<int32_t*>(smem + p.lds_plan);  // [E + 1]
+  int32_t* fill = off + E + 1;                                     // [E]
+  int32_t* act = fill + E;                                         // [E]
+  int32_t* ust = act + E;                                          // [E + 1]
+  int32_t* tmp = ust + E + 1;                                      // [pairs_cap]
+  int32_t* mem = tmp + p.pairs_cap;                                // [pairs_cap]
+
+  // ---- plan ----
+  for (int e = tid; e < E; e += blockDim.x) fill[e] = 0;
+  if (tid < 4) {
+    sh_misc[tid] = 0;
+    reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;
+  }
+  __syncthreads();
+  int nbad = 0;
+  for (int pi = tid; pi < P; pi += blockDim.x) {
+    const int id = p.ids[pi];
+    if (id >= 0 && id < E) atomicAdd(&fill[id], 1);
+    else ++nbad;
+  }
+  if (nbad) atomicAdd(&sh_misc[0], nbad);
+  __syncthreads();
+  {
+    const int per = (E + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int e0 = tid * per;
+    int lc = 0, la = 0, lu = 0;
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) {
+        const int c = fill[e];
+        lc += c;
+        la += c > 0 ? 1 : 0;
+        lu += c > 0 ? ((c + TP - 1) / TP) * T : 0;
+      }
+    }
+    const int ic = wave_incl_scan(lc, lane), ia = wave_incl_scan(la, lane),
+              iu = wave_incl_scan(lu, lane);
+    if (lane == 63) {
+      sh_wave[0][w] = ic;
+      sh_wave[1][w] = ia;
+      sh_wave[2][w] = iu;
+    }
+    __syncthreads();
+    int xc = ic - lc, xa = ia - la, xu = iu - lu;
+    for (int i = 0; i < w; ++i) {
+      xc += sh_wave[0][i];
+      xa += sh_wave[1][i];
+      xu += sh_wave[2][i];
+    }
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) {
+        const int c = fill[e];
+        off[e] = xc;
+        if (c > 0) {
+          act[xa] = e;
+          ust[xa] = xu;
+          ++xa;
+          xu += ((c + TP - 1) / TP) * T;
+        }
+        xc += c;
+      }
+    }
+    if (tid == (int)blockDim.x - 1) {  // its running sums end at the totals
+      off[E] = xc;
+      ust[xa] = xu;
+      sh_misc[1] = xa;
+      sh_misc[2] = xu;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) fill[e] = 0;
+  __syncthreads();
+  for (int pi = tid; pi < P; pi += blockDim.x) {
+    const int id = p.ids[pi];
+    if (id >= 0 && id < E) tmp[off[id] + atomicAdd(&fill[id], 1)] = pi;
+  }
+  __syncthreads();
+  const int nvalid = off[E];
+  for (int q = tid; q < nvalid; q += blockDim.x) {
+    const int v = tmp[q];
+    const int e = p.ids[v];
+    const int s0 = off[e], s1 = off[e + 1];
+    int r = 0;
+    for (int j = s0; j < s1; ++j) r += tmp[j] < v ? 1 : 0;
+    mem[s0 + r] = v;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    int32_t* counts = p.ws + 4;
+    int32_t* offsets = counts + E;
+    int32_t* members = offsets + E + 1;
+    for (int e = tid; e < E; e += blockDim.x) {
+      counts[e] = off[e + 1] - off[e];
+      offsets[e] = off[e];
+    }
+    for (int q = tid; q < nvalid; q += blockDim.x) members[q] = mem[q];
+    if (tid == 0) {
+      p.ws[0] = (sh_misc[0] ? QIMG_ERR_EXPERT_RANGE : 0) | (clamped ? QIMG_ERR_LIVE_CLAMPED : 0);
+      p.ws[1] = P;
+      p.ws[2] = 0;
+      p.ws[3] = 0;
+      offsets[E] = nvalid;
+    }
+  }
+
+  // ---- work ----
+  // values read from LDS that are the same in every lane are made wave-uniform, so that the
+  // reader descriptors they select are fetched with scalar loads (which do not wait on the
+  // weight loads in flight)
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  const int A = uni(sh_misc[1]), U = uni(sh_misc[2]);
+  const int u0 = (int)((int64_t)U * blockIdx.x / gridDim.x);
+  const int u1 = (int)((int64_t)U * (blockIdx.x + 1) / gridDim.x);
+  const int nb = 4 * KC;                 // staged blocks per segment (K padded to chunks)
+  const int code_bytes = nb * TP * 32;   // staged codes [nb][TP][32]
+  const int ncode = nb * TP * 2, nds = nb * 8;
+  for (int ub = u0; ub < u1;) {
+    if (tid == 0) {
+      int ue = ub, ns = 0;
+      while (ns < p.slots && ue < u1) {
+        int lo = 0, hi = A - 1;  // last active expert whose units start at or before ue
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (ust[mid] <= ue) lo = mid;
+          else hi = mid - 1;
+        }
+        const int e = act[lo];
+        const int pass = (ue - ust[lo]) / T;
+        const int cnt = off[e + 1] - off[e];
+        sh_seg[ns][0] = ust[lo] + pass * T;
+        sh_seg[ns][1] = e;
+        sh_seg[ns][2] = cnt - pass * TP < TP ? cnt - pass * TP : TP;
+        sh_seg[ns][3] = off[e] + pass * TP;
+        ue = sh_seg[ns][0] + T < u1 ? sh_seg[ns][0] + T : u1;
+        ++ns;
+      }
+      for (int k = ns; k < kRoutedMaxSlots; ++k) sh_seg[k][0] = 0x7fffffff;
+      sh_batch[0] = ue;
+      sh_batch[1] = ns;
+    }
+    __syncthreads();
+    const int ue = uni(sh_batch[0]);
+    const int ns = uni(sh_batch[1]);
+    // Stage the batch: codes items (slot, block, column, half) and scale items (slot, block,
+    // column slot of 8); unconditional in-bounds loads, padding items stored as zeros.
+    {
+      const int nitc = ns * ncode, nitd = ns * nds;
+      const int iters = (nitc + 4095) / 4096 > (nitd + 2047) / 2048 ? (nitc + 4095) / 4096
+                                                                     : (nitd + 2047) / 2048;
+      for (int it = 0; it < iters; ++it) {
+        uint4 v[8];
+        uint32_t dw[4];
+        bool okc[8], okd[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = tid + 512 * j + 4096 * it;
+          const int k = i / ncode, r = i - k * ncode;
+          const int half = r & 1, c = (r >> 1) % TP, b = (r >> 1) / TP;
+          const int kk = k < kRoutedMaxSlots ? k : 0;
+          okc[j] = i < nitc && c < sh_seg[kk][2] && b < p.Kb && sh_seg[kk][0] != 0x7fffffff;
+          const int irow = okc[j] ? mem[sh_seg[kk][3] + c] / p.top_k : 0;
+          const uint32_t src = okc[j] ? (uint32_t)(irow * p.RB + b) * 32u + 16u * half : 0u;
+          v[j] = *reinterpret_cast<const uint4*>(p.codes + src);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = tid + 512 * j + 2048 * it;
+          const int k = i / nds, r = i - k * nds;
+          const int c = r & 7, b = r >> 3;
+          const int kk = k < kRoutedMaxSlots ? k : 0;
+          okd[j] = i < nitd && c < sh_seg[kk][2] && b < p.Kb && sh_seg[kk][0] != 0x7fffffff;
+          const int irow = okd[j] ? mem[sh_seg[kk][3] + c] / p.top_k : 0;
+          dw[j] = p.ds[okd[j] ? (uint32_t)(irow * p.RB + b) : 0u];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = tid + 512 * j + 4096 * it;
+          const int k = i / ncode, r = i - k * ncode;
+          if (i < nitc)
+            *reinterpret_cast<uint4*>(smem + k * p.slot_bytes + r * 16) = okc[j] ? v[j] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = tid + 512 * j + 2048 * it;
+          const int k = i / nds, r = i - k * nds;
+          if (i < nitd) {
+            const uint32_t x = okd[j] ? dw[j] : 0u;
+            float* da = reinterpret_cast<float*>(smem + k * p.slot_bytes + code_bytes);
+            da[r] = h2f(x);
+            da[nds + r] = -8.0f * h2f(x >> 16);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- this wave's units [wa, wb) of the batch ----
+    const int m = ue - ub;
+    const int wa = ub + (int)((int64_t)m * w / kWaves), wb = ub + (int)((int64_t)m * (w + 1) / kWaves);
+    if (wa < wb) {
+      struct Cursor {
+        int u, nt, k, kb;
+      };
+      const uint8_t* lq[NTM];   // load cursor: tile code bases
+      const uint16_t* ld[NTM];  // and scale bases
+      int crow[NTM], cri[NTM];  // compute cursor: output row of this lane, reader
+      auto seg_of = [&](int u) {
+        int k = 0;
+        while (k + 1 < ns && u >= uni(sh_seg[k + 1][0])) ++k;
+        return k;
+      };
+      auto start = [&](int u, Cursor& c) {
+        c.u = u;
+        c.k = seg_of(u);
+        c.kb = 0;
+        const int s0 = uni(sh_seg[c.k][0]);
+        const int lim = s0 + T < wb ? s0 + T : wb;
+        c.nt = lim - u < NTM ? lim - u : NTM;
+      };
+      auto bind_load = [&](const Cursor& c) {
+        const int e = uni(sh_seg[c.k][1]);
+        const int s0 = uni(sh_seg[c.k][0]);
+#pragma unroll
+        for (int t = 0; t < NTM; ++t) {
+          const int tt = c.u - s0 + (t < c.nt ? t : c.nt - 1);
+          int ri = 0;
+          while (ri + 1 < p.n_readers && tt >= p.tile_start[ri + 1]) ++ri;
+          const int64_t chunk0 = ((int64_t)e * p.r[ri].tiles + (tt - p.tile_start[ri])) * KC;
+          lq[t] = p.r[ri].qs + (chunk0 * 64 + lane) * 16;
+          ld[t] = p.r[ri].d + chunk0 * 64 + lane;
+        }
+      };
+      auto bind_compute = [&](const Cursor& c) {
+        const int s0 = uni(sh_seg[c.k][0]);
+#pragma unroll
+        for (int t = 0; t < NTM; ++t) {
+          const int tt = c.u - s0 + (t < c.nt ? t : c.nt - 1);
+          int ri = 0;
+          while (ri + 1 < p.n_readers && tt >= p.tile_start[ri + 1]) ++ri;
+          cri[t] = ri;
+          crow[t] = (tt - p.tile_start[ri]) * 16 + n;
+        }
+      };
+      Cursor lc, cc;
+      start(wa, lc);
+      cc = lc;
+      bind_load(lc);
+      bind_compute(cc);
+      bool ldone = false;
+      auto advance_load = [&]() {
+        if (ldone) return;
+        lc.kb += KU;
+        if (lc.kb >= KC) {
+          const int nu = lc.u + lc.nt;
+          if (nu < wb) {
+            start(nu, lc);
+            bind_load(lc);
+          } else {
+            ldone = true;  // further loads repeat the last batch (in bounds, unused)
+            lc.kb -= KU;
+          }
+        }
+      };
+      float acc[NTM][8];
+#pragma unroll
+      for (int t = 0; t < NTM; ++t)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[t][v] = 0.0f;
+      int a_off[2];
+      bool a_on[2];
+      auto bind_a = [&](const Cursor& c) {
+        const int nc = uni(sh_seg[c.k][2]);
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg) {
+          const int col = 4 * tg + (n & 3);
+          a_on[tg] = (n >> 2) == g && col < nc;
+          a_off[tg] = c.k * p.slot_bytes + (g * TP + col) * 32;
+        }
+      };
+      bind_a(cc);
+
+      uint4 qa[KU][NTM], qb[KU][NTM];
+      uint32_t da_[KU][NTM], db_[KU][NTM];
+      auto load = [&](uint4 (&q)[KU][NTM], uint32_t (&d)[KU][NTM]) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          const int cs = lc.kb + u < KC ? lc.kb + u : KC - 1;
+#pragma unroll
+          for (int t = 0; t < NTM; ++t) {
+            q[u][t] = *reinterpret_cast<const uint4*>(lq[t] + (int64_t)cs * 1024);
+            d[u][t] = ld[t][(int64_t)cs * 64];
+          }
+        }
+      };
+      auto compute = [&](const uint4 (&q)[KU][NTM], const uint32_t (&d)[KU][NTM]) {
+        const unsigned char* slot = smem + cc.k * p.slot_bytes;
+        const float* daL = reinterpret_cast<const float*>(slot + code_bytes);
+        const float* msL = daL + nds;
+        const int nc = uni(sh_seg[cc.k][2]);
+        const int TG = (nc + 3) >> 2;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          const int cs = cc.kb + u;
+          if (cs >= KC) break;
+          v4i blo[NTM], bhi[NTM];
+          float dw[NTM];
+#pragma unroll
+          for (int t = 0; t < NTM; ++t) {
+            blo[t][0] = (int)(q[u][t].x & 0x0f0f0f0fu);
+            blo[t][1] = (int)(q[u][t].y & 0x0f0f0f0fu);
+            blo[t][2] = (int)(q[u][t].z & 0x0f0f0f0fu);
+            blo[t][3] = (int)(q[u][t].w & 0x0f0f0f0fu);
+            bhi[t][0] = (int)((q[u][t].x >> 4) & 0x0f0f0f0fu);
+            bhi[t][1] = (int)((q[u][t].y >> 4) & 0x0f0f0f0fu);
+            bhi[t][2] = (int)((q[u][t].z >> 4) & 0x0f0f0f0fu);
+            bhi[t][3] = (int)((q[u][t].w >> 4) & 0x0f0f0f0fu);
+            dw[t] = h2f(d[u][t]);
+          }
+          const int blk = 4 * cs + g;
+#pragma unroll
+          for (int tg = 0; tg < 2; ++tg) {
+            if (tg >= TG) break;
+            const int lo = a_on[tg] ? cs * (4 * TP * 32) + a_off[tg] : p.lds_zero;
+            const int hi = a_on[tg] ? lo + 16 : p.lds_zero;
+            const v4i alo = *reinterpret_cast<const v4i*>(smem + lo);
+            const v4i ahi = *reinterpret_cast<const v4i*>(smem + hi);
+            const float4 da4 = *reinterpret_cast<const float4*>(daL + blk * 8 + 4 * tg);
+            const float4 ms4 = *reinterpret_cast<const float4*>(msL + blk * 8 + 4 * tg);
+#pragma unroll
+            for (int t = 0; t < NTM; ++t) {
+              if (t >= cc.nt) break;
+              const v4i zero = {0, 0, 0, 0};
+              v4i dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[t], zero, 0, 0, 0);
+              dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[t], dd, 0, 0, 0);
+              acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.x, (float)dd[0], ms4.x), acc[t][4 * tg + 0]);
+              acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.y, (float)dd[1], ms4.y), acc[t][4 * tg + 1]);
+              acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.z, (float)dd[2], ms4.z), acc[t][4 * tg + 2]);
+              acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.w, (float)dd[3], ms4.w), acc[t][4 * tg + 3]);
+            }
+          }
+        }
+      };
+      // After a compute step: at the end of a group, sum the k-group lanes, store, and move
+      // the compute cursor to the next group.
+      auto finish_step = [&]() {
+        cc.kb += KU;
+        if (cc.kb < KC) return;
+        const int nc = uni(sh_seg[cc.k][2]);
+        const int mb = uni(sh_seg[cc.k][3]);
+#pragma unroll
+        for (int t = 0; t < NTM; ++t) {
+          if (t < cc.nt) {
+#pragma unroll
+            for (int v = 0; v < 8; ++v) acc[t][v] = pair_sum_halves(pair_sum_rows(acc[t][v]));
+            const int ri = cri[t], row = crow[t];
+            if (row < p.r[ri].N) {
+              const float v0 = g == 0 ? acc[t][0] : g == 1 ? acc[t][2] : g == 2 ? acc[t][4] : acc[t][6];
+              const float v1 = g == 0 ? acc[t][1] : g == 1 ? acc[t][3] : g == 2 ? acc[t][5] : acc[t][7];
+              if (2 * g < nc) p.r[ri].out[(int64_t)mem[mb + 2 * g] * p.r[ri].ld + row] = v0;
+              if (2 * g + 1 < nc) p.r[ri].out[(int64_t)mem[mb + 2 * g + 1] * p.r[ri].ld + row] = v1;
+            }
+          }
+#pragma unroll
+          for (int v = 0; v < 8; ++v) acc[t][v] = 0.0f;
+        }
+        const int nu = cc.u + cc.nt;
+        if (nu < wb) {
+          start(nu, cc);
+          bind_compute(cc);
+          bind_a(cc);
+        }
+      };
+      // steps of this wave: ceil(KC / KU) per group
+      const int per_group = (KC + KU - 1) / KU;
+      int S = 0;
+      for (Cursor c = lc; ; ) {
+        S += per_group;
+        if (c.u + c.nt >= wb) break;
+        start(c.u + c.nt, c);
+      }
+      load(qa, da_);
+      advance_load();
+      for (int st = 0; st < S; st += 2) {
+        load(qb, db_);
+        advance_load();
+        compute(qa, da_);
+        finish_step();
+        load(qa, da_);
+        advance_load();
+        if (st + 1 < S) {
+          compute(qb, db_);
+          finish_step();
+        }
+      }
+    }
+    __syncthreads();
+    ub = ue;
   }
 }
 
@@ -791,22 +1180,20 @@ struct ReadPlan {
 };
 
 // LDS layout of the reader: staged codes [4 KC][tp][32], d_a and -8 s_a [4 KC][8] f32, a
-// 16-byte zero slot, cross-wave sums [waves][ntm][16][8] f32, then the routed column list.
+// 16-byte zero slot, cross-wave sums [waves][ntm][16][8] f32.
 // tp is the widest of 8, 4, 2, 1 image columns per pass that fits.
-inline bool plan_lds(ReadArgs& a, int ntm, int max_cols, int* total) {
+inline bool plan_lds(ReadArgs& a, int ntm, int* total) {
   for (int tp : {8, 4, 2, 1}) {
     const int codes = 4 * a.KC * tp * 32;
     const int dsz = 4 * a.KC * 8 * 4;
     const int red = kWaves * ntm * 16 * 8 * 4;
-    const int cols = ((max_cols > 0 ? max_cols : 1) * 4 + 15) & ~15;
-    const int t = codes + 2 * dsz + 16 + red + cols;
+    const int t = codes + 2 * dsz + 16 + red;
     if (t <= kMaxLds) {
       a.tp = tp;
       a.lds_da = codes;
       a.lds_ms = codes + dsz;
       a.lds_zero = codes + 2 * dsz;
       a.lds_red = a.lds_zero + 16;
-      a.lds_cols = a.lds_red + red;
       *total = t;
       return true;
     }
@@ -842,25 +1229,49 @@ int run_ordinary(ReadArgs& a, hipStream_t s) {
   const int tiles = a.tile_start[a.n_readers];
   int G = cu_count();
   if (tiles < G) G = tiles;
-  a.wg_per_unit = G;
   a.tiles_total = tiles;
   const int ntm = ntm_for((tiles + G - 1) / G);
   int lds = 0;
-  if (!plan_lds(a, ntm, 0, &lds)) return QIMG_EUNSUPPORTED;
+  if (!plan_lds(a, ntm, &lds)) return QIMG_EUNSUPPORTED;
   return launch_read<MODE>(a, G, ntm, lds, s);
 }
 
-// Routed readers: E x (tile runs of about four tiles) workgroups.
-int run_routed(ReadArgs& a, int max_cols, hipStream_t s) {
+// Routed readers: one workgroup per CU over the (expert, pass, tile) units. LDS: `slots`
+// staged segments of [4 KC][tp][32] codes + [4 KC][8] d_a + [4 KC][8] -8 s_a, the zero slot,
+// then the plan arrays off[E+1], fill[E], act[E], ust[E+1], tmp[pairs], mem[pairs].
+int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   const int tiles = a.tile_start[a.n_readers];
-  const int per = tiles < 4 ? tiles : 4;
-  a.wg_per_unit = (tiles + per - 1) / per;
   a.tiles_total = tiles;
-  if ((int64_t)a.wg_per_unit * a.E > 0x7fffffff) return QIMG_EUNSUPPORTED;
-  const int ntm = ntm_for((tiles + a.wg_per_unit - 1) / a.wg_per_unit);
-  int lds = 0;
-  if (!plan_lds(a, ntm, max_cols, &lds)) return QIMG_EUNSUPPORTED;
-  return launch_read<1>(a, a.wg_per_unit * a.E, ntm, lds, s);
+  a.pairs_cap = pairs_cap;
+  if ((int64_t)(pairs_cap + a.E) * tiles > 0x7fffffff) return QIMG_EUNSUPPORTED;
+  const int plan = 4 * (4 * a.E + 2 + 2 * pairs_cap);
+  const int nb = 4 * a.KC;
+  // the widest column pass that leaves room for two staged segments, else for one
+  int lds = -1;
+  for (int need : {2, 1}) {
+    for (int tp : {8, 4, 2, 1}) {
+      const int slot = nb * tp * 32 + nb * 64;
+      int slots = (kMaxLds - 16 - plan) / slot;
+      if (slots > kRoutedMaxSlots) slots = kRoutedMaxSlots;
+      if (slots >= need) {
+        a.tp = tp;
+        a.slots = slots;
+        a.slot_bytes = slot;
+        a.lds_zero = slots * slot;
+        a.lds_plan = a.lds_zero + 16;
+        lds = a.lds_plan + plan;
+        break;
+      }
+    }
+    if (lds >= 0) break;
+  }
+  if (lds < 0) return QIMG_EUNSUPPORTED;
+  const void* fn = (const void*)mmvq_routed_kernel<2, 2>;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return QIMG_EHIP;
+  hipLaunchKernelGGL((mmvq_routed_kernel<2, 2>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
+  return launch_status();
 }
 
 }  // namespace
@@ -1027,7 +1438,6 @@ int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const voi
   a.live_rows = live_rows;
   a.n_readers = n_readers;
   a.top_k = 1;
-  a.routed = 0;
   return run_ordinary<0>(a, (hipStream_t)stream);
 }
 
@@ -1072,7 +1482,7 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
     for (int j = 0; j < i; ++j)
       if (overlap(outs[i], outs[j])) return QIMG_EALIAS;
   }
-  if (pairs > (1 << 24)) return QIMG_EUNSUPPORTED;
+  if (pairs > QIMG_MAX_ROUTED_PAIRS || E > QIMG_MAX_EXPERTS) return QIMG_EUNSUPPORTED;
   ReadArgs a{};
   int tiles = 0;
   for (int i = 0; i < n_readers; ++i) {
@@ -1091,7 +1501,6 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
   a.n_readers = n_readers;
   a.top_k = top_k;
   a.E = E;
-  a.routed = 1;
   return run_routed(a, (int)pairs, (hipStream_t)stream);
 }
 
@@ -1118,7 +1527,6 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
   a.sumi = sumi;
   a.n_readers = 1;
   a.top_k = 1;
-  a.routed = 0;
   return run_ordinary<2>(a, (hipStream_t)stream);
 }
 

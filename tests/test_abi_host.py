@@ -236,3 +236,14 @@ def test_blockdots_validation(L):
     assert L.mmvq_q4_0_q8_1_blockdots(r, D, 4, 256, C + 2, S) == qimg.EALIGN
     assert L.mmvq_q4_0_q8_1_blockdots(r, D, 4, 256, D + 64, S) == qimg.EALIAS
     assert L.mmvq_q4_0_q8_1_blockdots(r, D, 4, 256, A, S) == qimg.EALIAS
+
+
+def test_mmvq_id_limits(L):
+    r = expert_readers((A, 64, C, 64))
+    WS, IDS = B, B + (1 << 24)
+    big = qimg.workspace_bytes(4097, 1, 8)
+    assert L.mmvq_id_q4_0_q8_1(r, 1, 8, D, IDS, 4097, 1, None, 256, WS, big, S) == qimg.EUNSUPPORTED
+    assert L.mmvq_id_q4_0_q8_1(r, 1, 8, D, IDS, 1024, 5, None, 256, WS,
+                               qimg.workspace_bytes(1024, 5, 8), S) == qimg.EUNSUPPORTED
+    assert L.mmvq_id_q4_0_q8_1(r, 1, 1025, D, IDS, 8, 2, None, 256, WS,
+                               qimg.workspace_bytes(8, 2, 1025), S) == qimg.EUNSUPPORTED

@@ -374,6 +374,42 @@ def test_routed_bad_expert_ids_are_skipped_and_flagged():
     assert ws[0] & qimg.ERR_LIVE_CLAMPED and ws[1] == wl.T * wl.top_k
 
 
+@pytest.mark.parametrize("live", [128, 37])
+def test_routed_crowded_experts_and_repeated_ids(live):
+    # every live row routes to the same nine experts, so each of them has `live` pairs and needs
+    # several column passes; one row names an expert twice (two pairs, both computed)
+    print("crowded experts live", live, flush=True)
+    wl = W.make(5, live=live, small=True)
+    attach_dev_weights(wl)
+    rng = np.random.default_rng([77, live])
+    ids = np.empty_like(wl.ids)
+    for t in range(wl.T):
+        ids[t] = rng.permutation(wl.top_k) * 3
+    ids[1, 4] = ids[1, 2]
+    y, img = run_producer(wl, live=live)
+    _, img_o = check_producer(wl, y, img, live=live)
+    outs, ws = run_routed(wl, H.dev(img), ids, live=live)
+    check_plan(ws, ids, live, wl.E, wl.top_k)
+    check_routed(wl, img_o, outs, live, ids=ids)
+
+
+def test_routed_single_expert_and_all_pairs_bad():
+    wl = W.make(4, small=True)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl)
+    _, img_o = H.oracle_producer(wl)
+    ids = np.full_like(wl.ids, wl.E - 1)  # every pair on the last expert
+    outs, ws = run_routed(wl, H.dev(img), ids)
+    check_plan(ws, ids, wl.T, wl.E, wl.top_k)
+    check_routed(wl, img_o, outs, wl.T, ids=ids)
+    bad = np.full_like(wl.ids, wl.E)  # no valid pair: nothing written, plan empty, flagged
+    outs, ws = run_routed(wl, H.dev(img), bad)
+    assert ws[0] == qimg.ERR_EXPERT_RANGE and ws[1] == wl.T * wl.top_k
+    assert (ws[4:4 + 2 * wl.E + 1] == 0).all()
+    for out in outs:
+        assert (out.view(np.uint8) == H.SENTINEL_BYTE).all()
+
+
 # ---- padded bucket -------------------------------------------------------------------------------
 @pytest.mark.parametrize("live", [1, 9, 113, 114, 128])
 def test_padded_bucket(live):
