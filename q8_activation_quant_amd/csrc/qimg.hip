@@ -338,8 +338,18 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
 // up to 8: codes [block][column][32], d_a and -8 s_a as f32 [block][8].
 // ---------------------------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
+// Buffer resource word 3 for raw (untyped) buffer loads on this GPU family: 32-bit data
+// format, no swizzle, no index stride. Offsets at or past num_records read as zero.
+constexpr int kBufferFlags = 0x00020000;
+
+constexpr int kWaves = 8;  // routed readers
+#ifdef QIMG_OWAVES
+constexpr int kOrdWaves = QIMG_OWAVES;  // ordinary readers
+#else
+constexpr int kOrdWaves = 8;
+#endif
 
 struct ReaderDesc {
   const uint8_t* qs;  // tiled codes (1 KB per chunk)
@@ -362,7 +372,10 @@ struct ReadArgs {
   int32_t n_readers, RB, Kb, KC, rows, top_k, E;
   int32_t tiles_total;  // tiles per expert summed over readers
   int32_t tp;           // image columns per LDS pass (8, 4, 2 or 1)
+  int32_t tp_log2;      // log2(tp)
   int32_t lds_da, lds_ms, lds_zero, lds_red;  // byte offsets (codes at 0)
+  int32_t lds_raw;      // ordinary: raw image scale words [4 KC][tp]
+  int32_t tpd;          // ordinary: columns per row of d_a / -8 s_a (max(tp, 4))
   // routed readers
   int32_t lds_plan;     // byte offset of the plan arrays
   int32_t slots;        // staged (expert, pass) segments per batch
@@ -370,88 +383,122 @@ struct ReadArgs {
   int32_t pairs_cap;    // bucket * top_k
 };
 
-// Staging of image columns [c0, c0 + nc), blocks [b0, b1), in LDS, by one wave for the blocks
-// of its own K range (no workgroup barrier: the LDS operations of one wave complete in order).
-// Column c is image row c. A batch is up to 8 codes
-// items (16 bytes) and 8 scale items per lane. Its loads are unconditional (in-bounds
-// addresses; padding items are zeroed at the store), so when the first batch is issued before
-// the first weight loads, its stores wait for it alone while the weights stay in flight.
-struct StageBatch {
-  uint4 v[8];
-  uint32_t dsw[8];
-};
+// Staging of image columns [c0, c0 + nc) in LDS for the ordinary readers, all 4 KC blocks, by
+// direct global-to-LDS copies (no registers): codes into [4 KC][tp][32] at LDS 0 as 1 KB wave
+// instructions (16 bytes per lane), raw scale words into [4 KC][tp] at lds_raw as 256-byte
+// instructions. Wave w issues instructions w, w + 8, ... Items past the end of a region copy an
+// in-bounds image address into the region's padding; blocks past K/32 copy the row's last
+// block (their d_a and -8 s_a are set to zero, which is what makes them contribute nothing).
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-__device__ __forceinline__ void stage_issue(const ReadArgs& p, int c0, int nc, int b0, int b1,
-                                            int base, StageBatch& sb) {
+// One direct global-to-LDS copy per lane, to LDS byte address lds + lane * bytes (lds must be
+// the same in all lanes). Issued as inline assembly so that the compiler's wait-count pass does
+// not track it (it would otherwise wait for every outstanding load before each later LDS read
+// inside the streaming loop); callers issue these before any other vector memory load and
+// wait for them with an explicit vmcnt, which is exact because that counter retires in order.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)p);
+}
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ int stage_code_insts(const ReadArgs& p) { return (4 * p.KC * p.tp * 2 + 63) / 64; }
+__device__ __forceinline__ int stage_word_insts(const ReadArgs& p) { return (4 * p.KC * p.tp + 63) / 64; }
+
+__device__ __forceinline__ void stage_dma_issue(const ReadArgs& p, unsigned char* smem, int c0, int nc,
+                                                int w, int lane) {
   const int TP = p.tp;
-  const int nitems = (b1 - b0) * TP * 2;  // (block, column, half)
-  const int nds = (b1 - b0) * 8;          // (block, column slot of 8)
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = base + j * 64;
-    const int half = i & 1, t = (i >> 1) % TP, b = b0 + (i >> 1) / TP;
-    const bool ok = i < nitems && t < nc && b < p.Kb;
-    const int c = c0 + (ok ? t : 0);
-    const int irow = c;
-    const uint32_t off = ok ? (uint32_t)(irow * p.RB + b) * 32u + 16u * half : 0u;
-    sb.v[j] = *reinterpret_cast<const uint4*>(p.codes + off);
+  const int nci = stage_code_insts(p), nwi = stage_word_insts(p);
+  const int L = p.tp_log2;
+  for (int k = w; k < nci; k += kOrdWaves) {
+    const int i = 64 * k + lane;
+    const int half = i & 1, c = (i >> 1) & (TP - 1), b = i >> (1 + L);
+    const int row = c0 + (c < nc ? c : 0);
+    const int bs = b < p.Kb ? b : p.Kb - 1;
+    dma_b128(p.codes + ((int64_t)row * p.RB + bs) * 32 + 16 * half, lds_addr(smem + 1024 * k));
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = base + j * 64;
-    const int t = i & 7, b = b0 + (i >> 3);
-    const bool ok = i < nds && t < nc && b < p.Kb;
-    const int c = c0 + (ok ? t : 0);
-    const int irow = c;
-    sb.dsw[j] = p.ds[ok ? (uint32_t)(irow * p.RB + b) : 0u];
+  for (int k = w; k < nwi; k += kOrdWaves) {
+    const int i = 64 * k + lane;
+    const int c = i & (TP - 1), b = i >> L;
+    const int row = c0 + (c < nc ? c : 0);
+    const int bs = b < p.Kb ? b : p.Kb - 1;
+    dma_b32(p.ds + (int64_t)row * p.RB + bs, lds_addr(smem + p.lds_raw + 256 * k));
   }
 }
 
-__device__ __forceinline__ void stage_store(const ReadArgs& p, unsigned char* smem, int nc, int b0,
-                                            int b1, int base, const StageBatch& sb) {
-  const int TP = p.tp;
-  float* daL = reinterpret_cast<float*>(smem + p.lds_da);
-  float* msL = reinterpret_cast<float*>(smem + p.lds_ms);
-  const int nitems = (b1 - b0) * TP * 2;
-  const int nds = (b1 - b0) * 8;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = base + j * 64;
-    const int t = (i >> 1) % TP, b = b0 + (i >> 1) / TP;
-    if (i < nitems)
-      reinterpret_cast<uint4*>(smem)[b0 * TP * 2 + i] =
-          (t < nc && b < p.Kb) ? sb.v[j] : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = base + j * 64;
-    const int t = i & 7, b = b0 + (i >> 3);
-    const uint32_t w = (t < nc && b < p.Kb) ? sb.dsw[j] : 0u;
-    if (i < nds) {
-      daL[b0 * 8 + i] = h2f(w);
-      msL[b0 * 8 + i] = -8.0f * h2f(w >> 16);
+// After the wave's own copies have landed: convert the scale words it copied into d_a and
+// -8 s_a rows of tpd columns (zero for padding columns and blocks).
+__device__ __forceinline__ void stage_convert(const ReadArgs& p, unsigned char* smem, int nc, int w,
+                                              int lane) {
+  const int TP = p.tp, TPD = p.tpd, nb = 4 * p.KC;
+  const uint32_t* raw = reinterpret_cast<const uint32_t*>(smem + p.lds_raw);
+  float2* dam = reinterpret_cast<float2*>(smem + p.lds_da);  // [4 KC][tpd] (d_a, -8 s_a)
+  const int nwi = stage_word_insts(p);
+  for (int k = w; k < nwi; k += kOrdWaves) {
+    const int i = 64 * k + lane;
+    const int c = i & (TP - 1), b = i >> p.tp_log2;
+    if (b < nb) {
+      const bool ok = c < nc && b < p.Kb;
+      const uint32_t x = raw[i];
+      dam[b * TPD + c] = ok ? make_float2(h2f(x), -8.0f * h2f(x >> 16)) : make_float2(0.0f, 0.0f);
+      if (c == TP - 1)
+        for (int cc = TP; cc < TPD; ++cc) dam[b * TPD + cc] = make_float2(0.0f, 0.0f);
     }
   }
-  const int lane = threadIdx.x & 63;
-  if (lane < 4) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[lane] = 0u;  // own zero slot
+  if (lane < 8) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[lane] = 0u;
+}
+
+// s_waitcnt on the vector memory counter alone (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Weight loads in flight per wave (ring slots of one chunk of NTM tiles each).
+#ifndef QIMG_RING1
+#define QIMG_RING1 6
+#endif
+#ifndef QIMG_RING2
+#define QIMG_RING2 2
+#endif
+#ifndef QIMG_RING3
+#define QIMG_RING3 2
+#endif
+#ifndef QIMG_RING4
+#define QIMG_RING4 2
+#endif
+constexpr int ring_depth(int ntm) {
+  return ntm == 1 ? QIMG_RING1 : ntm == 2 ? QIMG_RING2 : ntm == 3 ? QIMG_RING3 : QIMG_RING4;
 }
 
 // MODE: 0 ordinary readers, 2 block-dot export.
 template <int NTM, int MODE>
-__global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
+__global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   constexpr bool DOTS = MODE == 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int KU = NTM <= 2 ? 2 : 1;  // chunks per prefetch batch (two batches in flight)
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // weight loads in flight per wave: a ring of D slots, each one chunk of NTM tiles
+  constexpr int D = ring_depth(NTM);
+#ifdef QIMG_INTERLEAVE
+  constexpr bool kInterleave = QIMG_INTERLEAVE;
+#else
+  constexpr bool kInterleave = true;
+#endif
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int n = lane & 15, g = lane >> 4;
   const int KC = p.KC, TP = p.tp;
-  const int cs0 = KC * w / kWaves, cs1 = KC * (w + 1) / kWaves;
+  const int cs0 = KC * w / kOrdWaves, cs1 = KC * (w + 1) / kOrdWaves;
   const int live = DOTS ? p.rows : clamp_live(p.live_rows, p.rows, nullptr);
   const int wgi = blockIdx.x;
   const int t0 = (int)((int64_t)p.tiles_total * wgi / gridDim.x);
   const int t1 = (int)((int64_t)p.tiles_total * (wgi + 1) / gridDim.x);
-  const float* daL = reinterpret_cast<const float*>(smem + p.lds_da);
-  const float* msL = reinterpret_cast<const float*>(smem + p.lds_ms);
   float* red = reinterpret_cast<float*>(smem + p.lds_red);
 
   const int ncols = live;
@@ -460,20 +507,28 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   for (int c0 = 0; c0 < ncols; c0 += TP) {
     const int nc = ncols - c0 < TP ? ncols - c0 : TP;
     const int TG = (nc + 3) >> 2;  // token groups of 4 columns
-    // A operand addresses (per token group and half): 16 LDS bytes, or the zero slot
-    const int m = n;  // A row of this lane
-    int a_off[2];
-    bool a_on[2];
+    // A operand of this lane (row m = n of the MFMA's A, k-group g) for token group tg: the
+    // 32 staged bytes of image column 4 tg + (m & 3), block 4 cs + g, at
+    // a_base + cs * a_step (low half, high half 16 bytes on), or the 32-byte zero slot
+    // (a_step = 0) when the row is outside the lane's k-group or past the columns.
+    const int m = n;
+    int a_base[2], a_step[2];
 #pragma unroll
     for (int tg = 0; tg < 2; ++tg) {
       const int col = 4 * tg + (m & 3);
-      a_on[tg] = (m >> 2) == g && col < nc;
-      a_off[tg] = (g * TP + col) * 32;
+      const bool on = (m >> 2) == g && col < nc;
+      a_base[tg] = on ? (g * TP + col) * 32 : p.lds_zero;
+      a_step[tg] = on ? 4 * TP * 32 : 0;
     }
+    // d_a, -8 s_a pairs of this lane's block: [block][tpd] float2, block 4 cs + g
+    const int dam_base = p.lds_da + g * p.tpd * 8, dam_step = 4 * p.tpd * 8;
     for (int tb = t0; tb < t1; tb += NTM) {
       const int nt = t1 - tb < NTM ? t1 - tb : NTM;
-      const uint4* qp[NTM];
-      const uint16_t* dp[NTM];
+      // per tile: buffer resources over its reader's code and scale planes, and the byte
+      // offsets of its first chunk (the same in every lane); the lanes add 16 * lane and
+      // 2 * lane
+      __amdgpu_buffer_rsrc_t rq[NTM], rd[NTM];
+      uint32_t oq[NTM], od[NTM];
       int rl[NTM], rr[NTM];
 #pragma unroll
       for (int t = 0; t < NTM; ++t) {
@@ -483,9 +538,14 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
         const int lt = tile - p.tile_start[ri];
         rr[t] = ri;
         rl[t] = lt * 16 + n;  // this lane's weight row in reader ri
-        const int64_t chunk0 = (int64_t)lt * KC;
-        qp[t] = reinterpret_cast<const uint4*>(p.r[ri].qs) + chunk0 * 64 + lane;
-        dp[t] = p.r[ri].d + chunk0 * 64 + lane;
+        const uint32_t chunk0 = (uint32_t)lt * (uint32_t)KC;
+        const uint32_t chunks = (uint32_t)p.r[ri].tiles * (uint32_t)KC;
+        rq[t] = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].qs, (short)0, (int)(chunks * 1024u),
+                                                  kBufferFlags);
+        rd[t] = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].d, (short)0, (int)(chunks * 128u),
+                                                  kBufferFlags);
+        oq[t] = chunk0 * 1024u;
+        od[t] = chunk0 * 128u;
       }
       float acc[NTM][8];
 #pragma unroll
@@ -493,48 +553,54 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[t][v] = 0.0f;
 
-      uint4 qa[KU][NTM], qb[KU][NTM];
-      uint32_t da_[KU][NTM], db_[KU][NTM];
-      auto load = [&](uint4 (&q)[KU][NTM], uint32_t (&d)[KU][NTM], int kb) {
+      uint4 q[D][NTM];
+      uint32_t dsc[D][NTM];
+      // chunks of this wave: with kInterleave, w, w + 8, w + 16, ... (the workgroup's waves
+      // read 8 consecutive chunks of a tile at each step); otherwise the range [cs0, cs1)
+      const int nst = kInterleave ? (KC - w + kOrdWaves - 1) / kOrdWaves : cs1 - cs0;
+      auto chunk_of = [&](int st) { return kInterleave ? w + kOrdWaves * st : cs0 + st; };
+      // Every slot is loaded unconditionally (a conditional load would keep the slot's stale
+      // value alive and defeat the exact wait counts); a slot past the wave's last chunk
+      // repeats that chunk (its lines are in flight or cached), never used. The chunk part of
+      // the address is the same in every lane.
+      const uint32_t lq = 16u * lane, ld2 = 2u * lane;
+      auto load = [&](int j, int st) {
+        const uint32_t cs = (uint32_t)chunk_of(st < nst ? st : nst - 1);
 #pragma unroll
-        for (int u = 0; u < KU; ++u) {
-          const int cs = kb + u < cs1 ? kb + u : cs1 - 1;  // past the range: repeat the last
-#pragma unroll
-          for (int t = 0; t < NTM; ++t) {
-            q[u][t] = qp[t][(int64_t)cs * 64];
-            d[u][t] = dp[t][(int64_t)cs * 64];
-          }
+        for (int t = 0; t < NTM; ++t) {
+          const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq, oq[t] + cs * 1024u, 0);
+          q[j][t] = make_uint4(x.x, x.y, x.z, x.w);
+          dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b16(rd[t], ld2, od[t] + cs * 128u, 0);
         }
       };
-      auto compute = [&](const uint4 (&q)[KU][NTM], const uint32_t (&d)[KU][NTM], int kb) {
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-          const int cs = kb + u;
-          if (cs >= cs1) break;
+      auto compute = [&](int j, int cs) {
+        {
           v4i blo[NTM], bhi[NTM];
           float dw[NTM];
 #pragma unroll
           for (int t = 0; t < NTM; ++t) {
-            blo[t][0] = (int)(q[u][t].x & 0x0f0f0f0fu);
-            blo[t][1] = (int)(q[u][t].y & 0x0f0f0f0fu);
-            blo[t][2] = (int)(q[u][t].z & 0x0f0f0f0fu);
-            blo[t][3] = (int)(q[u][t].w & 0x0f0f0f0fu);
-            bhi[t][0] = (int)((q[u][t].x >> 4) & 0x0f0f0f0fu);
-            bhi[t][1] = (int)((q[u][t].y >> 4) & 0x0f0f0f0fu);
-            bhi[t][2] = (int)((q[u][t].z >> 4) & 0x0f0f0f0fu);
-            bhi[t][3] = (int)((q[u][t].w >> 4) & 0x0f0f0f0fu);
-            dw[t] = h2f(d[u][t]);
+            blo[t][0] = (int)(q[j][t].x & 0x0f0f0f0fu);
+            blo[t][1] = (int)(q[j][t].y & 0x0f0f0f0fu);
+            blo[t][2] = (int)(q[j][t].z & 0x0f0f0f0fu);
+            blo[t][3] = (int)(q[j][t].w & 0x0f0f0f0fu);
+            bhi[t][0] = (int)((q[j][t].x >> 4) & 0x0f0f0f0fu);
+            bhi[t][1] = (int)((q[j][t].y >> 4) & 0x0f0f0f0fu);
+            bhi[t][2] = (int)((q[j][t].z >> 4) & 0x0f0f0f0fu);
+            bhi[t][3] = (int)((q[j][t].w >> 4) & 0x0f0f0f0fu);
+            dw[t] = h2f(dsc[j][t]);
           }
           const int blk = 4 * cs + g;  // this lane's block
+          const unsigned char* dam = smem + dam_base + cs * dam_step;
 #pragma unroll
           for (int tg = 0; tg < 2; ++tg) {
             if (tg >= TG) break;
-            const int lo = a_on[tg] ? cs * (4 * TP * 32) + a_off[tg] : p.lds_zero;
-            const int hi = a_on[tg] ? lo + 16 : p.lds_zero;
-            const v4i alo = *reinterpret_cast<const v4i*>(smem + lo);
-            const v4i ahi = *reinterpret_cast<const v4i*>(smem + hi);
-            const float4 da4 = *reinterpret_cast<const float4*>(daL + blk * 8 + 4 * tg);
-            const float4 ms4 = *reinterpret_cast<const float4*>(msL + blk * 8 + 4 * tg);
+            const unsigned char* ap = smem + a_base[tg] + cs * a_step[tg];
+            const v4i alo = *reinterpret_cast<const v4i*>(ap);
+            const v4i ahi = *reinterpret_cast<const v4i*>(ap + 16);
+            const float4 dm0 = *reinterpret_cast<const float4*>(dam + 32 * tg);       // cols 0, 1
+            const float4 dm1 = *reinterpret_cast<const float4*>(dam + 32 * tg + 16);  // cols 2, 3
+            const float4 da4 = make_float4(dm0.x, dm0.z, dm1.x, dm1.z);
+            const float4 ms4 = make_float4(dm0.y, dm0.w, dm1.y, dm1.w);
 #pragma unroll
             for (int t = 0; t < NTM; ++t) {
               if (t >= nt) break;
@@ -560,31 +626,31 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
           }
         }
       };
-      if (tb == t0) {
-        // Stage this wave's blocks of the image columns: the first batch's loads go out before
-        // the first weight batch and are stored while those weights are in flight.
-        const int b0 = 4 * cs0, b1 = 4 * cs1;
-        const int nitems = (b1 - b0) * TP * 2;
-        const int nbat = (nitems + 511) / 512 > (b1 - b0 + 63) / 64 ? (nitems + 511) / 512
-                                                                    : (b1 - b0 + 63) / 64;
-        StageBatch sb;
-        stage_issue(p, c0, nc, b0, b1, lane, sb);
-        if (cs1 > cs0) load(qa, da_, cs0);
-        stage_store(p, smem, nc, b0, b1, lane, sb);
-        for (int bt = 1; bt < nbat; ++bt) {
-          stage_issue(p, c0, nc, b0, b1, lane + 512 * bt, sb);
-          stage_store(p, smem, nc, b0, b1, lane + 512 * bt, sb);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // staged LDS before reads
-        __builtin_amdgcn_wave_barrier();
-      } else if (cs1 > cs0) {
-        load(qa, da_, cs0);
+      // Stage the image columns (first tile group of a column pass): the copies go out before
+      // the wave's first weight loads, and the wait below covers the copies alone.
+      const bool stage = tb == t0;
+      if (stage) {
+        if (c0 > 0) __syncthreads();  // every wave is done with the previous pass's columns
+        stage_dma_issue(p, smem, c0, nc, w, lane);
       }
-      for (int kb = cs0; kb < cs1; kb += 2 * KU) {
-        load(qb, db_, kb + KU);
-        compute(qa, da_, kb);
-        load(qa, da_, kb + 2 * KU);
-        compute(qb, db_, kb + KU);
+      if (nst > 0) {
+#pragma unroll
+        for (int j = 0; j < D - 1; ++j) load(j, j);
+        if (stage) wait_vmcnt<(D - 1) * NTM * 2>();
+      } else if (stage) {
+        wait_vmcnt<0>();
+      }
+      if (stage) {
+        stage_convert(p, smem, nc, w, lane);
+        __syncthreads();
+      }
+      for (int base = 0; base < nst; base += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          load((j + D - 1) % D, base + j + D - 1);
+          if (base + j < nst) compute(j, chunk_of(base + j));
+          __builtin_amdgcn_sched_barrier(0);  // keep each step's LDS operands local to it
+        }
       }
       if constexpr (!DOTS) {
         // the four k-group lanes of a row: (g0 + g1) + (g2 + g3)
@@ -618,7 +684,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
             const int row = (tile - p.tile_start[ri]) * 16 + nn;
             if (row < p.r[ri].N) {
               float s = red[(t * 16 + nn) * 8 + col];
-              for (int ww = 1; ww < kWaves; ++ww) s = s + red[((ww * NTM + t) * 16 + nn) * 8 + col];
+              for (int ww = 1; ww < kOrdWaves; ++ww) s = s + red[((ww * NTM + t) * 16 + nn) * 8 + col];
               p.r[ri].out[(int64_t)(c0 + col) * p.r[ri].ld + row] = s;
             }
           }
@@ -1179,21 +1245,28 @@ struct ReadPlan {
   int grid, ntm, lds;
 };
 
-// LDS layout of the reader: staged codes [4 KC][tp][32], d_a and -8 s_a [4 KC][8] f32, a
-// 16-byte zero slot, cross-wave sums [waves][ntm][16][8] f32.
-// tp is the widest of 8, 4, 2, 1 image columns per pass that fits.
+// LDS layout of the ordinary reader: staged codes [4 KC][tp][32] (padded to whole 1 KB copy
+// instructions), raw scale words [4 KC][tp] (padded to 256 B instructions), (d_a, -8 s_a)
+// pairs [4 KC][tpd] of f32, a 32-byte zero slot, cross-wave sums [waves][ntm][16][8] f32. tp
+// is the widest of 8, 4, 2, 1 image columns per pass that fits.
 inline bool plan_lds(ReadArgs& a, int ntm, int* total) {
+  const int nb = 4 * a.KC;
   for (int tp : {8, 4, 2, 1}) {
-    const int codes = 4 * a.KC * tp * 32;
-    const int dsz = 4 * a.KC * 8 * 4;
-    const int red = kWaves * ntm * 16 * 8 * 4;
-    const int t = codes + 2 * dsz + 16 + red;
+    const int tpd = tp > 4 ? tp : 4;
+    const int codes = (nb * tp * 2 + 63) / 64 * 1024;
+    const int raw = (nb * tp + 63) / 64 * 256;
+    const int dsz = nb * tpd * 8;
+    const int red = kOrdWaves * ntm * 16 * 8 * 4;
+    const int t = codes + raw + dsz + 32 + red;
     if (t <= kMaxLds) {
       a.tp = tp;
-      a.lds_da = codes;
-      a.lds_ms = codes + dsz;
-      a.lds_zero = codes + 2 * dsz;
-      a.lds_red = a.lds_zero + 16;
+      a.tp_log2 = tp == 8 ? 3 : tp == 4 ? 2 : tp == 2 ? 1 : 0;
+      a.tpd = tpd;
+      a.lds_raw = codes;
+      a.lds_da = codes + raw;
+      a.lds_ms = 0;  // unused: d_a and -8 s_a are interleaved at lds_da
+      a.lds_zero = a.lds_da + dsz;
+      a.lds_red = a.lds_zero + 32;
       *total = t;
       return true;
     }
@@ -1210,7 +1283,7 @@ int launch_read(ReadArgs& a, int grid, int ntm, int lds, hipStream_t s) {
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
-  dim3 g(grid), b(kWaves * 64);
+  dim3 g(grid), b(kOrdWaves * 64);
   if (ntm == 1) hipLaunchKernelGGL((mmvq_tiled_kernel<1, MODE>), g, b, lds, s, a);
   else if (ntm == 2) hipLaunchKernelGGL((mmvq_tiled_kernel<2, MODE>), g, b, lds, s, a);
   else if (ntm == 3) hipLaunchKernelGGL((mmvq_tiled_kernel<3, MODE>), g, b, lds, s, a);
