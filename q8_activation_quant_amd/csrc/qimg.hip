@@ -11,7 +11,7 @@
 // Kernels
 //   emit_kernel<OP,JW>       one workgroup per live row: (RMS reduction) -> f32 output -> per
 //                            32-block Q8_1 quantization, all in one pass over the row.
-//   mmvq_tiled_kernel<N,M>   ordinary Q4_0 x Q8_1 readers on the matrix cores
+//   mmvq_tiled_kernel<N,M,G> ordinary Q4_0 x Q8_1 readers on the matrix cores
 //                            (v_mfma_i32_16x16x64_i8) over tiled weights, the live image rows as
 //                            columns; M = 2: block-dot export.
 //   mmvq_routed_kernel<N,U>  routed readers: the plan of the live pairs built in LDS by every
@@ -461,6 +461,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8, each
+// with its own L2). xcd_rank renumbers them so that each XCD's workgroups take a contiguous run
+// of the work (ranks [start of XCD, next XCD)): work split by rank is then balanced across the
+// XCDs and neighbouring tiles share an L2. A bijection of [0, G).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_rank(int i, int G) {
+  const int x = i % kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + (x < r ? x : r) + i / kXcds;
+}
+
 // Weight loads in flight per wave (ring slots of one chunk of NTM tiles each).
 #ifndef QIMG_RING1
 #define QIMG_RING1 6
@@ -478,8 +488,9 @@ constexpr int ring_depth(int ntm) {
   return ntm == 1 ? QIMG_RING1 : ntm == 2 ? QIMG_RING2 : ntm == 3 ? QIMG_RING3 : QIMG_RING4;
 }
 
-// MODE: 0 ordinary readers, 2 block-dot export.
-template <int NTM, int MODE>
+// MODE: 0 ordinary readers, 2 block-dot export. NTG: token groups of 4 image columns per pass
+// (1 when a pass has at most 4 columns).
+template <int NTM, int MODE, int NTG>
 __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   constexpr bool DOTS = MODE == 2;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -496,7 +507,7 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
   const int KC = p.KC, TP = p.tp;
   const int cs0 = KC * w / kOrdWaves, cs1 = KC * (w + 1) / kOrdWaves;
   const int live = DOTS ? p.rows : clamp_live(p.live_rows, p.rows, nullptr);
-  const int wgi = blockIdx.x;
+  const int wgi = xcd_rank(blockIdx.x, gridDim.x);
   const int t0 = (int)((int64_t)p.tiles_total * wgi / gridDim.x);
   const int t1 = (int)((int64_t)p.tiles_total * (wgi + 1) / gridDim.x);
   float* red = reinterpret_cast<float*>(smem + p.lds_red);
@@ -506,7 +517,6 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 
   for (int c0 = 0; c0 < ncols; c0 += TP) {
     const int nc = ncols - c0 < TP ? ncols - c0 : TP;
-    const int TG = (nc + 3) >> 2;  // token groups of 4 columns
     // A operand of this lane (row m = n of the MFMA's A, k-group g) for token group tg: the
     // 32 staged bytes of image column 4 tg + (m & 3), block 4 cs + g, at
     // a_base + cs * a_step (low half, high half 16 bytes on), or the 32-byte zero slot
@@ -573,54 +583,63 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
           dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b16(rd[t], ld2, od[t] + cs * 128u, 0);
         }
       };
+      // One chunk of NTM tiles: all matrix-core products first (for every tile slot; an idle
+      // slot repeats the last tile and its sums are never stored), then the scaling, so no
+      // VALU instruction waits on a product issued just before it.
       auto compute = [&](int j, int cs) {
+        v4i blo[NTM], bhi[NTM];
+        float dw[NTM];
+#pragma unroll
+        for (int t = 0; t < NTM; ++t) {
+          blo[t][0] = (int)(q[j][t].x & 0x0f0f0f0fu);
+          blo[t][1] = (int)(q[j][t].y & 0x0f0f0f0fu);
+          blo[t][2] = (int)(q[j][t].z & 0x0f0f0f0fu);
+          blo[t][3] = (int)(q[j][t].w & 0x0f0f0f0fu);
+          bhi[t][0] = (int)((q[j][t].x >> 4) & 0x0f0f0f0fu);
+          bhi[t][1] = (int)((q[j][t].y >> 4) & 0x0f0f0f0fu);
+          bhi[t][2] = (int)((q[j][t].z >> 4) & 0x0f0f0f0fu);
+          bhi[t][3] = (int)((q[j][t].w >> 4) & 0x0f0f0f0fu);
+          dw[t] = h2f(dsc[j][t]);
+        }
+        const int blk = 4 * cs + g;  // this lane's block
+        const unsigned char* dam = smem + dam_base + cs * dam_step;
         {
-          v4i blo[NTM], bhi[NTM];
-          float dw[NTM];
+          v4i dd[NTG][NTM];
 #pragma unroll
-          for (int t = 0; t < NTM; ++t) {
-            blo[t][0] = (int)(q[j][t].x & 0x0f0f0f0fu);
-            blo[t][1] = (int)(q[j][t].y & 0x0f0f0f0fu);
-            blo[t][2] = (int)(q[j][t].z & 0x0f0f0f0fu);
-            blo[t][3] = (int)(q[j][t].w & 0x0f0f0f0fu);
-            bhi[t][0] = (int)((q[j][t].x >> 4) & 0x0f0f0f0fu);
-            bhi[t][1] = (int)((q[j][t].y >> 4) & 0x0f0f0f0fu);
-            bhi[t][2] = (int)((q[j][t].z >> 4) & 0x0f0f0f0fu);
-            bhi[t][3] = (int)((q[j][t].w >> 4) & 0x0f0f0f0fu);
-            dw[t] = h2f(dsc[j][t]);
-          }
-          const int blk = 4 * cs + g;  // this lane's block
-          const unsigned char* dam = smem + dam_base + cs * dam_step;
-#pragma unroll
-          for (int tg = 0; tg < 2; ++tg) {
-            if (tg >= TG) break;
+          for (int tg = 0; tg < NTG; ++tg) {
             const unsigned char* ap = smem + a_base[tg] + cs * a_step[tg];
             const v4i alo = *reinterpret_cast<const v4i*>(ap);
             const v4i ahi = *reinterpret_cast<const v4i*>(ap + 16);
+#pragma unroll
+            for (int t = 0; t < NTM; ++t) {
+              const v4i zero = {0, 0, 0, 0};
+              dd[tg][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[t], zero, 0, 0, 0);
+              dd[tg][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[t], dd[tg][t], 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int tg = 0; tg < NTG; ++tg) {
             const float4 dm0 = *reinterpret_cast<const float4*>(dam + 32 * tg);       // cols 0, 1
             const float4 dm1 = *reinterpret_cast<const float4*>(dam + 32 * tg + 16);  // cols 2, 3
             const float4 da4 = make_float4(dm0.x, dm0.z, dm1.x, dm1.z);
             const float4 ms4 = make_float4(dm0.y, dm0.w, dm1.y, dm1.w);
 #pragma unroll
             for (int t = 0; t < NTM; ++t) {
-              if (t >= nt) break;
-              const v4i zero = {0, 0, 0, 0};
-              v4i dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[t], zero, 0, 0, 0);
-              dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[t], dd, 0, 0, 0);
+              const v4i d = dd[tg][t];
               if constexpr (DOTS) {
-                if (rl[t] < p.r[0].N && blk < p.Kb) {
+                if (t < nt && rl[t] < p.r[0].N && blk < p.Kb) {
 #pragma unroll
                   for (int v = 0; v < 4; ++v) {
                     const int col = c0 + 4 * tg + v;
                     if (4 * tg + v < nc)
-                      p.sumi[((int64_t)col * p.r[0].N + rl[t]) * p.Kb + blk] = dd[v];
+                      p.sumi[((int64_t)col * p.r[0].N + rl[t]) * p.Kb + blk] = d[v];
                   }
                 }
               } else {
-                acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.x, (float)dd[0], ms4.x), acc[t][4 * tg + 0]);
-                acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.y, (float)dd[1], ms4.y), acc[t][4 * tg + 1]);
-                acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.z, (float)dd[2], ms4.z), acc[t][4 * tg + 2]);
-                acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.w, (float)dd[3], ms4.w), acc[t][4 * tg + 3]);
+                acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.x, (float)d[0], ms4.x), acc[t][4 * tg + 0]);
+                acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.y, (float)d[1], ms4.y), acc[t][4 * tg + 1]);
+                acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.z, (float)d[2], ms4.z), acc[t][4 * tg + 2]);
+                acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.w, (float)d[3], ms4.w), acc[t][4 * tg + 3]);
               }
             }
           }
@@ -854,8 +873,9 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   // weight loads in flight)
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
   const int A = uni(sh_misc[1]), U = uni(sh_misc[2]);
-  const int u0 = (int)((int64_t)U * blockIdx.x / gridDim.x);
-  const int u1 = (int)((int64_t)U * (blockIdx.x + 1) / gridDim.x);
+  const int wr = xcd_rank(blockIdx.x, gridDim.x);
+  const int u0 = (int)((int64_t)U * wr / gridDim.x);
+  const int u1 = (int)((int64_t)U * (wr + 1) / gridDim.x);
   const int nb = 4 * KC;                 // staged blocks per segment (K padded to chunks)
   const int code_bytes = nb * TP * 32;   // staged codes [nb][TP][32]
   const int ncode = nb * TP * 2, nds = nb * 8;
@@ -1274,21 +1294,29 @@ inline bool plan_lds(ReadArgs& a, int ntm, int* total) {
   return false;
 }
 
-template <int MODE>
-int launch_read(ReadArgs& a, int grid, int ntm, int lds, hipStream_t s) {
-  const void* fn = ntm == 1 ? (const void*)mmvq_tiled_kernel<1, MODE>
-                 : ntm == 2 ? (const void*)mmvq_tiled_kernel<2, MODE>
-                 : ntm == 3 ? (const void*)mmvq_tiled_kernel<3, MODE>
-                            : (const void*)mmvq_tiled_kernel<4, MODE>;
+template <int MODE, int NTG>
+int launch_read_g(ReadArgs& a, int grid, int ntm, int lds, hipStream_t s) {
+  const void* fn = ntm == 1 ? (const void*)mmvq_tiled_kernel<1, MODE, NTG>
+                 : ntm == 2 ? (const void*)mmvq_tiled_kernel<2, MODE, NTG>
+                 : ntm == 3 ? (const void*)mmvq_tiled_kernel<3, MODE, NTG>
+                            : (const void*)mmvq_tiled_kernel<4, MODE, NTG>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
   dim3 g(grid), b(kOrdWaves * 64);
-  if (ntm == 1) hipLaunchKernelGGL((mmvq_tiled_kernel<1, MODE>), g, b, lds, s, a);
-  else if (ntm == 2) hipLaunchKernelGGL((mmvq_tiled_kernel<2, MODE>), g, b, lds, s, a);
-  else if (ntm == 3) hipLaunchKernelGGL((mmvq_tiled_kernel<3, MODE>), g, b, lds, s, a);
-  else hipLaunchKernelGGL((mmvq_tiled_kernel<4, MODE>), g, b, lds, s, a);
+  if (ntm == 1) hipLaunchKernelGGL((mmvq_tiled_kernel<1, MODE, NTG>), g, b, lds, s, a);
+  else if (ntm == 2) hipLaunchKernelGGL((mmvq_tiled_kernel<2, MODE, NTG>), g, b, lds, s, a);
+  else if (ntm == 3) hipLaunchKernelGGL((mmvq_tiled_kernel<3, MODE, NTG>), g, b, lds, s, a);
+  else hipLaunchKernelGGL((mmvq_tiled_kernel<4, MODE, NTG>), g, b, lds, s, a);
   return launch_status();
+}
+
+// One token group when no pass can hold more than 4 image columns.
+template <int MODE>
+int launch_read(ReadArgs& a, int grid, int ntm, int lds, hipStream_t s) {
+  const int max_cols = a.rows < a.tp ? a.rows : a.tp;
+  return max_cols <= 4 ? launch_read_g<MODE, 1>(a, grid, ntm, lds, s)
+                       : launch_read_g<MODE, 2>(a, grid, ntm, lds, s);
 }
 
 inline int ntm_for(int64_t tiles_per_wg) {
