@@ -220,6 +220,9 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
   const int w = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
   const int C = p.K >> 2;
+  // leaves of this workgroup: the whole row (RMS, whose sum needs it), or slice blockIdx.y of
+  // W * 64 * JW leaves (the element-wise producers and the quantizer)
+  const int c_off = blockIdx.y * (W * 64 * JW);
   const float* arow = p.a + (int64_t)row * p.lda;
 
   // all input loads of the row go out at once (in bounds: leaves past K re-read leaf 0 and
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
   const float* brow = (OP == OP_SWIGLU || OP == OP_GEGLU) ? p.b + (int64_t)row * p.ldb : p.b;
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj) {
-    const int c = lane + 64 * (w * JW + jj);
+    const int c = c_off + lane + 64 * (w * JW + jj);
     const int cc = c < C ? c : 0;
     v[jj] = *reinterpret_cast<const float4*>(arow + 4 * cc);
     if (c >= C) v[jj] = make_float4(0, 0, 0, 0);
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
     const float r = 1.0f / __builtin_sqrtf(mean + p.eps);
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
-      const int c = lane + 64 * (w * JW + jj);
+      const int c = c_off + lane + 64 * (w * JW + jj);
       float4 y;
       y.x = v[jj].x * r; y.y = v[jj].y * r; y.z = v[jj].z * r; y.w = v[jj].w * r;
       if (p.b && c < C) {
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
   } else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU) {
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
-      const int c = lane + 64 * (w * JW + jj);
+      const int c = c_off + lane + 64 * (w * JW + jj);
       if (c < C) {
         const float4 uu = u[jj];
         float4 y;
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
     float* yrow = p.y + (int64_t)row * p.ldy;
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
-      const int c = lane + 64 * (w * JW + jj);
+      const int c = c_off + lane + 64 * (w * JW + jj);
       if (c < C) *reinterpret_cast<float4*>(yrow + 4 * c) = v[jj];
     }
   }
@@ -298,11 +301,11 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
   if (p.codes) {
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
-      const int blk = 8 * (w * JW + jj) + (lane >> 3);
+      const int blk = (c_off >> 3) + 8 * (w * JW + jj) + (lane >> 3);
       if (blk < p.Kb) quantize_leaf(v[jj], row, blk, lane, p);  // whole 8-lane groups agree
     }
-    // row padding blocks [Kb, RB) are zero bytes
-    const int npad = p.RB - p.Kb;
+    // row padding blocks [Kb, RB) are zero bytes (written by the row's last slice)
+    const int npad = blockIdx.y + 1 == gridDim.y ? p.RB - p.Kb : 0;
     uint32_t* cw = reinterpret_cast<uint32_t*>(p.codes) + ((int64_t)row * p.RB + p.Kb) * 8;
     for (int i = threadIdx.x; i < npad * 9; i += blockDim.x) {
       if (i < npad * 8) cw[i] = 0u;
@@ -1224,15 +1227,24 @@ inline int launch_status() {
 
 // Producer launch shape: Jp = next power of two >= ceil(K/256) leaf slots per lane;
 // W = min(16, max(1, Jp/2)) waves, JW = Jp / W slots per lane.
+// The element-wise producers and the quantizer need no row-wide value: their rows are cut into
+// slices of at most 16 waves x 64 lanes x 1 leaf (4096 elements), one workgroup each.
 int launch_emit(int op, EmitArgs& a, hipStream_t s) {
   const int J = (a.K + 255) / 256;
-  int Jp = 1;
-  while (Jp < J) Jp <<= 1;
-  int W = Jp / 2;
-  if (W < 1) W = 1;
-  if (W > 16) W = 16;
-  const int JW = Jp / W;
-  dim3 grid(a.rows), block(W * 64);
+  int W, JW, S = 1;
+  if (op == OP_RMS) {
+    int Jp = 1;
+    while (Jp < J) Jp <<= 1;
+    W = Jp / 2;
+    if (W < 1) W = 1;
+    if (W > 16) W = 16;
+    JW = Jp / W;
+  } else {
+    W = J < 16 ? J : 16;
+    JW = 1;
+    S = (J + W - 1) / W;
+  }
+  dim3 grid(a.rows, S), block(W * 64);
 #define QIMG_EMIT_CASE(OPV, JWV) \
   if (op == OPV && JW == JWV) { hipLaunchKernelGGL((emit_kernel<OPV, JWV>), grid, block, 0, s, a); return launch_status(); }
 #define QIMG_EMIT_OP(OPV) QIMG_EMIT_CASE(OPV, 1) QIMG_EMIT_CASE(OPV, 2) QIMG_EMIT_CASE(OPV, 4) QIMG_EMIT_CASE(OPV, 8)
@@ -1259,7 +1271,7 @@ inline int64_t tiled_chunks(int32_t N, int32_t K, int32_t E) {
   return (int64_t)E * tiles * KC;
 }
 
-constexpr int kMaxLds = 160 * 1024;
+constexpr int kMaxLds = 156 * 1024;  // dynamic LDS; 4 KB left for static arrays (160 KB per workgroup)
 
 struct ReadPlan {
   int grid, ntm, lds;
