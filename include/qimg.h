@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 3
+#define QIMG_ABI_VERSION 4
 
 /* status codes */
 #define QIMG_OK 0
@@ -225,6 +225,25 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
  */
 int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, int32_t rows,
                              int32_t K, int32_t* sumi, void* stream);
+
+/*
+ * Check export of the producers' activation math ([P1] Coverage: F32 SwiGLU and GeGLU-erf
+ * producers keep their formulas; the pages give no exp or erf, so the library fixes one f32
+ * operation sequence for each and the producers inline it).
+ * For i < n, out[i] = f(x_i), where x_i is the f32 whose bit pattern is first_bits + i
+ * (mod 2^32), so n = 2^32 with first_bits = 0 covers every f32 input once.
+ *   fn QIMG_MATH_EXP    : exp_q(x)            (e^x)
+ *   fn QIMG_MATH_ERFC   : erfc_q(x)           (erfc x; the producers call it with x >= 0)
+ *   fn QIMG_MATH_SWIGLU : x / (1 + exp_q(-x)) (the SwiGLU activation)
+ *   fn QIMG_MATH_GEGLU  : (0.5 x) (1 + erf(x / sqrt 2)) through erfc_q (the GeGLU-erf activation)
+ * out: device float[n], 4-byte aligned, owned by the caller. 0 <= n <= 2^32; n = 0 is a no-op.
+ * Errors: QIMG_EINVAL for a bad fn, n out of range or a null out; QIMG_EALIGN.
+ */
+#define QIMG_MATH_EXP 0
+#define QIMG_MATH_ERFC 1
+#define QIMG_MATH_SWIGLU 2
+#define QIMG_MATH_GEGLU 3
+int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream);
 
 #ifdef __cplusplus
 }

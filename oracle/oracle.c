@@ -163,6 +163,10 @@ float orc_glu_act(int op, float g) {
   }
 }
 
+void orc_glu_act_array(int op, const float* g, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_glu_act(op, g[i]);
+}
+
 void orc_glu(int op, const float* gate, int64_t ldg, const float* up, int64_t ldu, int rows, int K,
              float* y, int64_t ldy) {
   for (int i = 0; i < rows; ++i)

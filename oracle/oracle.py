@@ -49,6 +49,7 @@ def lib():
             "orc_erfc_q": (f32, [f32]),
             "orc_erfc_q_array": (None, [P, P, i64]),
             "orc_glu_act": (f32, [i32, f32]),
+            "orc_glu_act_array": (None, [i32, P, P, i64]),
             "orc_glu": (None, [i32, P, i64, P, i64, i32, i32, P, i64]),
             "orc_rms_sumsq": (f32, [P, i32]),
             "orc_rmsnorm": (None, [P, i64, P, f32, i32, i32, P, i64]),
@@ -92,17 +93,33 @@ def f16_to_f64(h: int) -> float:
     return float(lib().orc_f16_to_f64(int(h)))
 
 
-def exp_q(x) -> np.ndarray:
+def _out_like(x: np.ndarray, out: np.ndarray | None) -> np.ndarray:
+    """A result array shaped like x: a new one, or the caller's (f32, C-contiguous, same size)."""
+    if out is None:
+        return np.empty_like(x)
+    assert out.dtype == np.float32 and out.flags["C_CONTIGUOUS"] and out.size == x.size
+    return out
+
+
+def exp_q(x, out: np.ndarray | None = None) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
-    out = np.empty_like(x)
+    out = _out_like(x, out)
     lib().orc_exp_q_array(_p(x), _p(out), x.size)
     return out
 
 
-def erfc_q(z) -> np.ndarray:
+def erfc_q(z, out: np.ndarray | None = None) -> np.ndarray:
     z = np.ascontiguousarray(z, dtype=np.float32)
-    out = np.empty_like(z)
+    out = _out_like(z, out)
     lib().orc_erfc_q_array(_p(z), _p(out), z.size)
+    return out
+
+
+def glu_act(g, op: str, out: np.ndarray | None = None) -> np.ndarray:
+    """orc_glu_act element-wise: the GLU activation alone (no up factor)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    out = _out_like(g, out)
+    lib().orc_glu_act_array(GLU_OPS[op], _p(g), _p(out), g.size)
     return out
 
 

@@ -146,6 +146,26 @@ __device__ __forceinline__ float geglu_erf_act(float g) {
   return (0.5f * g) * ope;
 }
 
+// Element-wise evaluation of the activation math above over a range of f32 bit patterns:
+// out[i] = f(x) with x the float whose bits are first + i (mod 2^32). It runs the same inlined
+// device functions the producers run, so every f32 input can be compared with a host
+// evaluation of the same operation sequence.
+enum : int { MATH_EXP = 0, MATH_ERFC = 1, MATH_SWIGLU = 2, MATH_GEGLU = 3 };
+
+template <int FN>
+__global__ __launch_bounds__(256) void eval_math_kernel(uint32_t first, int64_t n, float* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const float x = __builtin_bit_cast(float, first + (uint32_t)i);
+    float v;
+    if constexpr (FN == MATH_EXP) v = exp_q(x);
+    else if constexpr (FN == MATH_ERFC) v = erfc_q(x);
+    else if constexpr (FN == MATH_SWIGLU) v = swiglu_act(x);
+    else v = geglu_erf_act(x);
+    out[i] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Producer: one workgroup per live row.
 // Element mapping: leaf c covers elements 4c..4c+3; lane l of wave w holds leaves
@@ -739,6 +759,14 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 // fixed lane tree): not on the other pairs, the live count or the schedule.
 // ---------------------------------------------------------------------------------------------
 constexpr int kRoutedMaxSlots = 4;
+// routed waves stream NTM tiles x KU chunks per load batch, two batches in flight
+#ifndef QIMG_RNTM
+#define QIMG_RNTM 1
+#endif
+#ifndef QIMG_RKU
+#define QIMG_RKU 4
+#endif
+constexpr int kRoutedNtm = QIMG_RNTM, kRoutedKu = QIMG_RKU;
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -1379,11 +1407,11 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
     if (lds >= 0) break;
   }
   if (lds < 0) return QIMG_EUNSUPPORTED;
-  const void* fn = (const void*)mmvq_routed_kernel<2, 2>;
+  const void* fn = (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
-  hipLaunchKernelGGL((mmvq_routed_kernel<2, 2>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
+  hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
   return launch_status();
 }
 
@@ -1641,6 +1669,23 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
   a.n_readers = 1;
   a.top_k = 1;
   return run_ordinary<2>(a, (hipStream_t)stream);
+}
+
+int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream) {
+  if (fn < MATH_EXP || fn > MATH_GEGLU || n < 0 || n > ((int64_t)1 << 32)) return QIMG_EINVAL;
+  if (n == 0) return QIMG_OK;
+  if (!out) return QIMG_EINVAL;
+  if (!al(out, 4)) return QIMG_EALIGN;
+  const int64_t wgs = (n + 255) / 256;
+  const dim3 grid((unsigned)(wgs < 8192 ? wgs : 8192));
+  hipStream_t s = (hipStream_t)stream;
+  switch (fn) {
+    case MATH_EXP: eval_math_kernel<MATH_EXP><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_ERFC: eval_math_kernel<MATH_ERFC><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_SWIGLU: eval_math_kernel<MATH_SWIGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    default: eval_math_kernel<MATH_GEGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+  }
+  return launch_status();
 }
 
 }  // extern "C"

@@ -18,14 +18,15 @@ GLU_SWIGLU, GLU_GEGLU_ERF = 0, 1
 GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
     "qimg_emit_rmsnorm", "qimg_emit_glu", "qimg_quantize_q8_1", "mmvq_q4_0_q8_1",
     "mmvq_id_workspace_bytes", "mmvq_id_q4_0_q8_1", "mmvq_q4_0_q8_1_blockdots",
-    "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile",
+    "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile", "qimg_eval_math",
 )
+MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3}
 
 
 class QimgError(RuntimeError):
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "mmvq_q4_0_q8_1_blockdots": (ctypes.c_int, [ctypes.POINTER(Reader), P, i32, i32, P, P]),
             "qimg_q4_0_tiled_bytes": (i64, [i32, i32, i32]),
             "qimg_q4_0_tile": (ctypes.c_int, [P, P, i32, i32, i32, P, P]),
+            "qimg_eval_math": (ctypes.c_int, [i32, ctypes.c_uint32, i64, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -187,3 +189,10 @@ def blockdots(w, N, img, rows, K, sumi, stream=None):
     r = Reader(ctypes.c_void_p(w.data_ptr()), N, 0, ctypes.c_void_p(sumi.data_ptr()), N)
     _check(lib().mmvq_q4_0_q8_1_blockdots(ctypes.byref(r), _ptr(img), rows, K, _ptr(sumi),
                                           _stream(stream)), "mmvq_q4_0_q8_1_blockdots")
+
+
+def eval_math(fn, first_bits, out, stream=None):
+    """out[i] = fn(x_i) with x_i the f32 of bit pattern first_bits + i (out: float32 device)."""
+    fn = MATH_FNS[fn] if isinstance(fn, str) else fn
+    _check(lib().qimg_eval_math(fn, ctypes.c_uint32(first_bits & 0xFFFFFFFF), out.numel(), _ptr(out),
+                                _stream(stream)), "qimg_eval_math")
