@@ -236,6 +236,8 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
  *   fn QIMG_MATH_ERFC   : erfc_q(x)           (erfc x; the producers call it with x >= 0)
  *   fn QIMG_MATH_SWIGLU : x / (1 + exp_q(-x)) (the SwiGLU activation)
  *   fn QIMG_MATH_GEGLU  : (0.5 x) (1 + erf(x / sqrt 2)) through erfc_q (the GeGLU-erf activation)
+ *   fn QIMG_MATH_RSQRT  : 1 / sqrt(x)         (the RMS scale's correctly rounded sqrt and divide)
+ *   fn QIMG_MATH_QSCALE : 1 / (x / 127)       (the quantizer's d = amax/127 and 1/d)
  * out: device float[n], 4-byte aligned, owned by the caller. 0 <= n <= 2^32; n = 0 is a no-op.
  * Errors: QIMG_EINVAL for a bad fn, n out of range or a null out; QIMG_EALIGN.
  */
@@ -243,6 +245,8 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
 #define QIMG_MATH_ERFC 1
 #define QIMG_MATH_SWIGLU 2
 #define QIMG_MATH_GEGLU 3
+#define QIMG_MATH_RSQRT 4
+#define QIMG_MATH_QSCALE 5
 int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream);
 
 #ifdef __cplusplus

@@ -217,13 +217,21 @@ float orc_rms_sumsq(const float* x, int K) {
   return pairwise_tree(lane_sum, 64);
 }
 
+/* The RMS scale from the regularised mean square v = mean + eps: 1 / sqrt(v), with the
+ * correctly rounded sqrt and division of IEEE f32. */
+float orc_rms_scale(float v) { return 1.0f / sqrtf(v); }
+
+void orc_rms_scale_array(const float* v, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_rms_scale(v[i]);
+}
+
 void orc_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps, int rows, int K,
                  float* y, int64_t ldy) {
   for (int i = 0; i < rows; ++i) {
     const float* xr = x + (int64_t)i * ldx;
     float S = orc_rms_sumsq(xr, K);
     float mean = S / (float)K;
-    float r = 1.0f / sqrtf(mean + eps);
+    float r = orc_rms_scale(mean + eps);
     for (int k = 0; k < K; ++k) {
       float t = xr[k] * r;
       y[(int64_t)i * ldy + k] = gamma ? t * gamma[k] : t;
@@ -244,6 +252,13 @@ void orc_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps, int
  * whole blocks; the padding is part of the compared image bytes). Returns the number of
  * non-finite inputs met (the producer's live rows must be finite).
  * ---------------------------------------------------------------------------------------- */
+/* The block scale d = amax / 127 and the code multiplier id = 1 / d (both correctly rounded). */
+float orc_quant_scale(float amax) { return amax / 127.0f; }
+
+void orc_quant_recip_array(const float* amax, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = 1.0f / orc_quant_scale(amax[i]);
+}
+
 int orc_row_blocks(int K) { return ((K / 32 + 15) / 16) * 16; }
 
 int orc_quantize(const float* y, int64_t ldy, int rows, int K, uint8_t* img) {
@@ -266,7 +281,7 @@ int orc_quantize(const float* y, int64_t ldy, int rows, int K, uint8_t* img) {
         if (a > amax) amax = a;
       }
       if (amax == 0.0f) continue;
-      float d = amax / 127.0f;
+      float d = orc_quant_scale(amax);
       float id = 1.0f / d;
       if (!isfinite(id)) continue;
       int sum = 0;

@@ -50,6 +50,8 @@ def lib():
             "orc_erfc_q_array": (None, [P, P, i64]),
             "orc_glu_act": (f32, [i32, f32]),
             "orc_glu_act_array": (None, [i32, P, P, i64]),
+            "orc_rms_scale_array": (None, [P, P, i64]),
+            "orc_quant_recip_array": (None, [P, P, i64]),
             "orc_glu": (None, [i32, P, i64, P, i64, i32, i32, P, i64]),
             "orc_rms_sumsq": (f32, [P, i32]),
             "orc_rmsnorm": (None, [P, i64, P, f32, i32, i32, P, i64]),
@@ -120,6 +122,22 @@ def glu_act(g, op: str, out: np.ndarray | None = None) -> np.ndarray:
     g = np.ascontiguousarray(g, dtype=np.float32)
     out = _out_like(g, out)
     lib().orc_glu_act_array(GLU_OPS[op], _p(g), _p(out), g.size)
+    return out
+
+
+def rms_scale(v, out: np.ndarray | None = None) -> np.ndarray:
+    """orc_rms_scale element-wise: 1 / sqrt(v)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = _out_like(v, out)
+    lib().orc_rms_scale_array(_p(v), _p(out), v.size)
+    return out
+
+
+def quant_recip(amax, out: np.ndarray | None = None) -> np.ndarray:
+    """1 / (amax / 127) element-wise: the quantizer's code multiplier."""
+    amax = np.ascontiguousarray(amax, dtype=np.float32)
+    out = _out_like(amax, out)
+    lib().orc_quant_recip_array(_p(amax), _p(out), amax.size)
     return out
 
 

@@ -150,7 +150,10 @@ __device__ __forceinline__ float geglu_erf_act(float g) {
 // out[i] = f(x) with x the float whose bits are first + i (mod 2^32). It runs the same inlined
 // device functions the producers run, so every f32 input can be compared with a host
 // evaluation of the same operation sequence.
-enum : int { MATH_EXP = 0, MATH_ERFC = 1, MATH_SWIGLU = 2, MATH_GEGLU = 3 };
+// Two more functions cover the correctly rounded divisions and square root the producers rely
+// on: 1/sqrt(x) (the RMS scale) and 1/(x/127) (the quantizer's scale and its reciprocal).
+enum : int { MATH_EXP = 0, MATH_ERFC = 1, MATH_SWIGLU = 2, MATH_GEGLU = 3, MATH_RSQRT = 4,
+             MATH_QSCALE = 5 };
 
 template <int FN>
 __global__ __launch_bounds__(256) void eval_math_kernel(uint32_t first, int64_t n, float* out) {
@@ -161,7 +164,9 @@ __global__ __launch_bounds__(256) void eval_math_kernel(uint32_t first, int64_t 
     if constexpr (FN == MATH_EXP) v = exp_q(x);
     else if constexpr (FN == MATH_ERFC) v = erfc_q(x);
     else if constexpr (FN == MATH_SWIGLU) v = swiglu_act(x);
-    else v = geglu_erf_act(x);
+    else if constexpr (FN == MATH_GEGLU) v = geglu_erf_act(x);
+    else if constexpr (FN == MATH_RSQRT) v = 1.0f / __builtin_sqrtf(x);
+    else v = 1.0f / (x / 127.0f);
     out[i] = v;
   }
 }
@@ -1672,7 +1677,7 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
 }
 
 int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream) {
-  if (fn < MATH_EXP || fn > MATH_GEGLU || n < 0 || n > ((int64_t)1 << 32)) return QIMG_EINVAL;
+  if (fn < MATH_EXP || fn > MATH_QSCALE || n < 0 || n > ((int64_t)1 << 32)) return QIMG_EINVAL;
   if (n == 0) return QIMG_OK;
   if (!out) return QIMG_EINVAL;
   if (!al(out, 4)) return QIMG_EALIGN;
@@ -1683,7 +1688,9 @@ int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void*
     case MATH_EXP: eval_math_kernel<MATH_EXP><<<grid, 256, 0, s>>>(first_bits, n, out); break;
     case MATH_ERFC: eval_math_kernel<MATH_ERFC><<<grid, 256, 0, s>>>(first_bits, n, out); break;
     case MATH_SWIGLU: eval_math_kernel<MATH_SWIGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
-    default: eval_math_kernel<MATH_GEGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_GEGLU: eval_math_kernel<MATH_GEGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_RSQRT: eval_math_kernel<MATH_RSQRT><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    default: eval_math_kernel<MATH_QSCALE><<<grid, 256, 0, s>>>(first_bits, n, out); break;
   }
   return launch_status();
 }

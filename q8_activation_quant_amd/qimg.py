@@ -26,7 +26,7 @@ EXPORTS = (
     "mmvq_id_workspace_bytes", "mmvq_id_q4_0_q8_1", "mmvq_q4_0_q8_1_blockdots",
     "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile", "qimg_eval_math",
 )
-MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3}
+MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5}
 
 
 class QimgError(RuntimeError):

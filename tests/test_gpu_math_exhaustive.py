@@ -1,7 +1,8 @@
-"""Exhaustive equality of the activation math: every one of the 2^32 f32 inputs.
+"""Exhaustive equality of the producers' scalar math: every one of the 2^32 f32 inputs.
 
 The GLU producers inline fixed f32 operation sequences for e^x and erfc (the pages give the
-activation formulas, SwiGLU and GeGLU-erf, but no exp or erf). Bit-exact producer parity on
+activation formulas, SwiGLU and GeGLU-erf, but no exp or erf); the RMS producer and the
+quantizer rely on correctly rounded f32 square root and division. Bit-exact producer parity on
 sampled workloads does not show that the device and the host oracle agree on every input, so
 here the device evaluates each function on all 2^32 bit patterns (qimg_eval_math, chunk by
 chunk) and the host compares each chunk with the oracle's evaluation, bit for bit; a NaN
@@ -17,8 +18,6 @@ import helpers as H
 from oracle import oracle as O
 from q8_activation_quant_amd import qimg
 
-pytestmark = pytest.mark.gpu
-
 CHUNK = 1 << 27
 THREADS = 16 if (os.cpu_count() or 1) >= 16 else 8  # divides CHUNK
 
@@ -27,6 +26,8 @@ ORACLE = {
     "erfc": lambda x, out: O.erfc_q(x, out),
     "swiglu": lambda x, out: O.glu_act(x, "swiglu", out),
     "geglu_erf": lambda x, out: O.glu_act(x, "geglu_erf", out),
+    "rsqrt": lambda x, out: O.rms_scale(x, out),
+    "qscale": lambda x, out: O.quant_recip(x, out),
 }
 
 
@@ -52,7 +53,22 @@ class _Slot:
         return idx.size, [(int(self.x[i]), int(wb[i]), int(got_bits[i])) for i in idx[:4]]
 
 
-@pytest.mark.parametrize("fn", ["exp", "erfc", "swiglu", "geglu_erf"])
+def test_chunk_compare_finds_planted_mismatches():
+    """Host side only: one flipped bit is found, a different NaN payload is not a mismatch."""
+    n, first = 4096, 0x7F7FF800  # runs from finite values through +inf into NaN patterns
+    slot = _Slot(n)
+    x = (np.arange(n, dtype=np.uint32) + np.uint32(first)).view(np.float32)
+    got = O.glu_act(x, "swiglu").view(np.uint32).copy()
+    assert slot.compare("swiglu", first, got) == (0, [])
+    nan_at = int(np.flatnonzero(np.isnan(got.view(np.float32)))[0])
+    got[nan_at] ^= 1  # another quiet NaN
+    got[17] ^= 1 << 3
+    nb, cases = slot.compare("swiglu", first, got)
+    assert nb == 1 and cases[0][0] == first + 17
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("fn", list(ORACLE))
 def test_activation_math_all_f32_inputs(fn):
     torch = H.torch()
     assert torch.cuda.is_available(), "GPU tests need a GPU"
@@ -77,11 +93,12 @@ def test_activation_math_all_f32_inputs(fn):
         fn, total_bad, [tuple(hex(v) for v in c) for c in examples[:8]])
 
 
+@pytest.mark.gpu
 def test_eval_math_rejects_bad_arguments():
     torch = H.torch()
     out = torch.empty(16, dtype=torch.float32, device="cuda")
     with pytest.raises(qimg.QimgError):
-        qimg.eval_math(4, 0, out)
+        qimg.eval_math(6, 0, out)
     st = qimg.lib().qimg_eval_math(0, 0, (1 << 32) + 1, qimg._ptr(out), None)
     assert st == qimg.EINVAL
     assert qimg.lib().qimg_eval_math(0, 0, 0, None, None) == qimg.OK
