@@ -384,15 +384,19 @@ int orc_plan(const int32_t* ids, int live, int top_k, int E, int32_t* counts, in
 }
 
 /* Routed reader: out[p][n] for live pairs p < live*top_k whose expert is in range; expert e's
- * weights are qs + e*N*Kb*16, d + e*N*Kb; image row = p / top_k. Pairs with a bad expert
- * are not written. */
-void orc_mmvq_id(const uint8_t* qs, const uint16_t* d, int E, int N, int K, const uint8_t* img,
-                 int img_rows, const int32_t* ids, int live, int top_k, double* out) {
+ * weights are qs + e*N*Kb*16, d + e*N*Kb. The image row of pair p = (t, slot) is t for an
+ * image of the tokens (one image shared by every slot), or p itself for a per-slot image (one
+ * image row per pair, as a GLU producer over the routed gate/up outputs emits it for the down
+ * projection: "Share temporary Q8_1 activation images", Overview and Coverage, per-slot
+ * routed projections). Pairs with a bad expert are not written. */
+static void mmvq_id_rows(const uint8_t* qs, const uint16_t* d, int E, int N, int K,
+                         const uint8_t* img, int img_rows, const int32_t* ids, int live,
+                         int top_k, int per_slot, double* out) {
   int Kb = K / 32, RB = orc_row_blocks(K);
   const int8_t* codes = (const int8_t*)img;
   const uint32_t* ds = (const uint32_t*)(img + (size_t)img_rows * RB * 32);
   for (int p = 0; p < live * top_k; ++p) {
-    int e = ids[p], t = p / top_k;
+    int e = ids[p], t = per_slot ? p : p / top_k;
     if (e < 0 || e >= E) continue;
     const uint8_t* qe = qs + (size_t)e * N * Kb * 16;
     const uint16_t* de = d + (size_t)e * N * Kb;
@@ -400,4 +404,39 @@ void orc_mmvq_id(const uint8_t* qs, const uint16_t* d, int E, int N, int K, cons
       out[(size_t)p * N + n] = reader_row(qe + (size_t)n * Kb * 16, de + (size_t)n * Kb, Kb,
                                           codes + (size_t)t * RB * 32, ds + (size_t)t * RB);
   }
+}
+
+void orc_mmvq_id(const uint8_t* qs, const uint16_t* d, int E, int N, int K, const uint8_t* img,
+                 int img_rows, const int32_t* ids, int live, int top_k, double* out) {
+  mmvq_id_rows(qs, d, E, N, K, img, img_rows, ids, live, top_k, 0, out);
+}
+
+void orc_mmvq_id_per_slot(const uint8_t* qs, const uint16_t* d, int E, int N, int K,
+                          const uint8_t* img, int img_rows, const int32_t* ids, int live,
+                          int top_k, double* out) {
+  mmvq_id_rows(qs, d, E, N, K, img, img_rows, ids, live, top_k, 1, out);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * MoE combine of the routed expert outputs with the routing weights, for live rows only
+ * ("qwen3_5 CUDA: a captured bucket's padding rows no longer go through the routed experts",
+ * What this changes: padding rows get no combine work and their output rows stay unwritten).
+ * out[t][n] = sum over slots s = 0 .. top_k-1 whose expert ids[t][s] is in [0, E) of
+ * w[t][s] * x[t][s][n]. The pages fix no arithmetic for the sum; the reading taken here is one
+ * f32 fused multiply-add per slot in ascending slot order, from +0:
+ *   acc = +0; acc = fmaf(w[t][s], x[t][s][n], acc).
+ * x is [rows][top_k][ld_pair] f32, w and ids are [rows][top_k]. Rows t >= live are not touched.
+ * ---------------------------------------------------------------------------------------- */
+void orc_moe_combine(const float* x, int64_t ld_pair, const float* w, const int32_t* ids, int E,
+                     int live, int top_k, int N, float* out, int64_t ldo) {
+  for (int t = 0; t < live; ++t)
+    for (int n = 0; n < N; ++n) {
+      float acc = 0.0f;
+      for (int s = 0; s < top_k; ++s) {
+        int p = t * top_k + s;
+        if (ids[p] < 0 || ids[p] >= E) continue;
+        acc = fmaf(w[p], x[(int64_t)p * ld_pair + n], acc);
+      }
+      out[(int64_t)t * ldo + n] = acc;
+    }
 }

@@ -51,6 +51,8 @@ def lib():
             "orc_glu_act": (f32, [i32, f32]),
             "orc_glu_act_array": (None, [i32, P, P, i64]),
             "orc_rms_scale_array": (None, [P, P, i64]),
+            "orc_mmvq_id_per_slot": (None, [P, P, i32, i32, i32, P, i32, P, i32, i32, P]),
+            "orc_moe_combine": (None, [P, i64, P, P, i32, i32, i32, i32, P, i64]),
             "orc_quant_recip_array": (None, [P, P, i64]),
             "orc_glu": (None, [i32, P, i64, P, i64, i32, i32, P, i64]),
             "orc_rms_sumsq": (f32, [P, i32]),
@@ -239,8 +241,9 @@ def plan(ids: np.ndarray, live: int, E: int):
 
 
 def mmvq_id(qs: np.ndarray, d16: np.ndarray, E: int, K: int, img: np.ndarray, img_rows: int,
-            ids: np.ndarray, live: int) -> np.ndarray:
-    """orc_mmvq_id: float64 out [live*top_k][N]; pairs with a bad expert stay NaN."""
+            ids: np.ndarray, live: int, per_slot: bool = False) -> np.ndarray:
+    """orc_mmvq_id (image row = token) or orc_mmvq_id_per_slot (image row = pair):
+    float64 out [live*top_k][N]; pairs with a bad expert stay NaN."""
     qs = np.ascontiguousarray(qs, dtype=np.uint8)
     d16 = np.ascontiguousarray(d16, dtype=np.uint16)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -249,5 +252,17 @@ def mmvq_id(qs: np.ndarray, d16: np.ndarray, E: int, K: int, img: np.ndarray, im
     N = qs.size // (E * Kb * 16)
     out = np.full((live * top_k, N), np.nan, dtype=np.float64)
     img = np.ascontiguousarray(img, dtype=np.uint8)
-    lib().orc_mmvq_id(_p(qs), _p(d16), E, N, K, _p(img), img_rows, _p(ids), live, top_k, _p(out))
+    fn = lib().orc_mmvq_id_per_slot if per_slot else lib().orc_mmvq_id
+    fn(_p(qs), _p(d16), E, N, K, _p(img), img_rows, _p(ids), live, top_k, _p(out))
+    return out
+
+
+def moe_combine(x: np.ndarray, w: np.ndarray, ids: np.ndarray, E: int, live: int) -> np.ndarray:
+    """orc_moe_combine over x [rows][top_k][N] f32: out [live][N] f32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    rows, top_k, N = x.shape
+    out = np.zeros((live, N), dtype=np.float32)
+    lib().orc_moe_combine(_p(x), N, _p(w), _p(ids), E, live, top_k, N, _p(out), N)
     return out

@@ -16,6 +16,12 @@ Workloads (sizes and distributions of the pages' component graphs, chosen per wo
                     top-9, Q4_0 expert weights [256, 512, 2048]; padding rows poisoned
 Q4_0 weights: 4-bit codes uniform on 0..15 (uniform random bytes), fp16 block scales uniform
 on [1e-3, 1e-2]. Gamma ~ N(1, 0.1), eps = 1e-6.
+
+MoE FFN extension of the routed workloads (moe=True): the per-slot SwiGLU over the gate/up
+outputs, a Q4_0 down projection per (token, slot) with expert weights [E, K, n_ff] (workload
+4: n_ff 768; workload 5: n_ff 512), then the combine with the routing weights. Stage inputs
+for checking each step on its own: pair_gu ~ N(0,1) [T*top_k][2*n_ff] (packed gate|up per
+pair) and pair_x ~ N(0,1) [T][top_k][K] (expert outputs for the combine).
 """
 from __future__ import annotations
 
@@ -25,7 +31,9 @@ import numpy as np
 
 # tensor ids of the seeded streams
 T_X, T_GAMMA, T_OUTLIER, T_GU, T_LOGITS, T_STALE_IDS, T_EXTRA = 0, 1, 2, 3, 4, 5, 6
+T_PAIR_GU, T_PAIR_X = 7, 8
 T_READER0 = 10  # reader r uses T_READER0 + r
+T_DOWN = 20     # MoE down projection
 
 EPS = 1e-6
 
@@ -81,6 +89,10 @@ class Workload:
     route_w: np.ndarray | None = None   # [T][top_k]
     live: int | None = None
     extra_v: np.ndarray | None = None   # f32 vector for the extra f32 reader of workload 3
+    n_ff: int = 0                       # MoE: expert hidden width (gate/up rows, down K)
+    down: Q4Weights | None = None       # MoE: down projection [E, K, n_ff]
+    pair_gu: np.ndarray | None = None   # MoE stage input [T*top_k][2*n_ff]
+    pair_x: np.ndarray | None = None    # MoE stage input [T][top_k][K]
 
     @property
     def routed(self) -> bool:
@@ -91,9 +103,24 @@ class Workload:
         return [w.d.shape[-2] for w in self.readers]
 
 
-def make(config: int, *, live: int | None = None, glu_op: str = "swiglu", small: bool = False) -> Workload:
+def make(config: int, *, live: int | None = None, glu_op: str = "swiglu", small: bool = False,
+         moe: bool = False) -> Workload:
     """Build workload `config` (1..5). `small=True` shrinks the weight row counts (not K or T)
-    so the CPU oracle can check every output of a GPU run in well under a second."""
+    so the CPU oracle can check every output of a GPU run in well under a second. `moe=True`
+    (workloads 4 and 5) adds the down projection and the MoE stage inputs."""
+    wl = _make(config, live, glu_op, small, moe)
+    if moe:
+        if not wl.routed:
+            raise ValueError("the MoE extension needs a routed workload (4 or 5)")
+        c = wl.config
+        wl.down = q4_0_weights(rng(c, T_DOWN), (wl.E, wl.K if not small else 80), wl.n_ff)
+        wl.pair_gu = rng(c, T_PAIR_GU).standard_normal((wl.T * wl.top_k, 2 * wl.n_ff)).astype(np.float32)
+        wl.pair_x = rng(c, T_PAIR_X).standard_normal((wl.T, wl.top_k, wl.K)).astype(np.float32)
+        wl.name += " moe-ffn n_ff%d" % wl.n_ff
+    return wl
+
+
+def _make(config, live, glu_op, small, moe):
     if config == 1:
         K, T = 2560, 1
         x = rng(1, T_X).standard_normal((T, K)).astype(np.float32)
@@ -123,25 +150,27 @@ def make(config: int, *, live: int | None = None, glu_op: str = "swiglu", small:
         K, T, E, k = 2560, 8, 128, 8
         x = rng(4, T_X).standard_normal((T, K)).astype(np.float32)
         gamma = rng(4, T_GAMMA).normal(1.0, 0.1, K).astype(np.float32)
-        N = 768 if not small else 48
+        N = 768 if not small else (64 if moe else 48)
         readers = [q4_0_weights(rng(4, T_READER0 + r), (E, N), K) for r in range(2)]
         ids, w = topk_ids(rng(4, T_LOGITS), T, E, k)
         return Workload(4, "routed T8 K2560 E128 top8", T, K, "rmsnorm", x=x, gamma=gamma,
-                        readers=readers, E=E, top_k=k, ids=ids, route_w=w)
+                        readers=readers, E=E, top_k=k, ids=ids, route_w=w, n_ff=N)
     if config == 5:
         K, B, E, k = 2048, 128, 256, 9
         live = 128 if live is None else live
         x = rng(5, T_X).standard_normal((B, K)).astype(np.float32)
         gamma = rng(5, T_GAMMA).normal(1.0, 0.1, K).astype(np.float32)
-        N = 512 if not small else 40
+        N = 512 if not small else (64 if moe else 40)
         readers = [q4_0_weights(rng(5, T_READER0), (E, N), K)]
+        if moe:  # gate and up experts, as in workload 4
+            readers.append(q4_0_weights(rng(5, T_READER0 + 1), (E, N), K))
         ids, w = topk_ids(rng(5, T_LOGITS), B, E, k)
         stale, _ = topk_ids(rng(5, T_STALE_IDS), B, E, k)
         ids[live:] = stale[live:]
         poison_rows(x, live)
         return Workload(5, "padded bucket B128 K2048 E256 top9 live%d" % live, B, K, "rmsnorm",
                         x=x, gamma=gamma, readers=readers, E=E, top_k=k, ids=ids, route_w=w,
-                        live=live)
+                        live=live, n_ff=N)
     raise ValueError("config must be 1..5")
 
 

@@ -179,3 +179,68 @@ def test_routed_reduces_to_ordinary_reader():
         diff = 8.0 * (_f16(d16[t, :Kb]) * codes[t, :Kb].sum(-1) - _f16(s16[t, :Kb]))
         ref = np.einsum("nbj,bj->n", wd, ad) + _f16(w.d[e]) @ diff
         assert np.allclose(out[p], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_per_slot_routed_reader_uses_the_pair_image_row():
+    """Per-slot image (one row per (token, slot) pair): the routed reader of pair p equals the
+    brute-force float64 dequantize-and-dot of expert ids[p] with image row p; bad ids stay NaN."""
+    g = np.random.default_rng(6)
+    E, N, K, B, k, live = 5, 3, 96, 4, 3, 3
+    w = W.q4_0_weights(g, (E, N), K)
+    ids, _ = W.topk_ids(g, B, E, k)
+    ids[1, 2] = E  # out of range: skipped
+    y, img = _random_image(g, B * k, K)
+    out = O.mmvq_id(w.qs, w.d, E, K, img, B * k, ids, live, per_slot=True)
+    tok = O.mmvq_id(w.qs, w.d, E, K, img, B * k, ids, live)  # token rows: a different answer
+    codes, d16, s16 = O.image_planes(img, B * k, K)
+    Kb = K // 32
+    for p in range(live * k):
+        e = ids.reshape(-1)[p]
+        if e >= E:
+            assert np.isnan(out[p]).all()
+            continue
+        wd = (_unpack_weights(w.qs[e]).astype(np.float64) - 8.0) * _f16(w.d[e])[..., None]
+        ad = codes[p, :Kb].astype(np.float64) * _f16(d16[p, :Kb])[..., None]
+        diff = 8.0 * (_f16(d16[p, :Kb]) * codes[p, :Kb].sum(-1) - _f16(s16[p, :Kb]))
+        ref = np.einsum("nbj,bj->n", wd, ad) + _f16(w.d[e]) @ diff
+        assert np.allclose(out[p], ref, rtol=1e-12, atol=1e-14)
+    assert not np.allclose(out[k:2 * k], tok[k:2 * k], equal_nan=True)
+
+
+def test_moe_combine_against_float64():
+    """fma chain over the slots: within top_k roundings of the exact float64 weighted sum."""
+    wl = W.make(4, moe=True)
+    x, w, ids = wl.pair_x, wl.route_w, wl.ids
+    out = O.moe_combine(x, w, ids, wl.E, wl.T)
+    prod = w.astype(np.float64)[:, :, None] * x.astype(np.float64)
+    exact = prod.sum(axis=1)
+    bound = wl.top_k * 2.0 ** -24 * np.abs(prod).sum(axis=1)
+    assert (np.abs(out - exact) <= bound).all()
+    assert np.abs(out - exact).max() > 0  # f32 rounding is visible: not a float64 sum
+
+
+def test_moe_combine_closed_forms():
+    g = np.random.default_rng(7)
+    rows, k, N, E = 3, 4, 64, 6
+    x = g.standard_normal((rows, k, N)).astype(np.float32)
+    ids = np.array([[0, 1, 2, 3], [4, 5, 0, 1], [2, 3, 4, 5]], np.int32)
+    # one-hot weights give that slot's row exactly
+    for s in range(k):
+        w = np.zeros((rows, k), np.float32)
+        w[:, s] = 1.0
+        assert np.array_equal(O.moe_combine(x, w, ids, E, rows), x[:, s])
+    # small integers: every product and partial sum is exact
+    xi = g.integers(-50, 50, size=(rows, k, N)).astype(np.float32)
+    wi = g.integers(-8, 8, size=(rows, k)).astype(np.float32)
+    want = (wi[:, :, None].astype(np.int64) * xi.astype(np.int64)).sum(axis=1)
+    assert np.array_equal(O.moe_combine(xi, wi, ids, E, rows), want.astype(np.float32))
+    # a pair whose expert is out of range contributes nothing, as a zero weight would
+    bad = ids.copy()
+    bad[1, 2] = E
+    bad[2, 0] = -1
+    wz = wi.copy()
+    wz[1, 2] = 0.0
+    wz[2, 0] = 0.0
+    assert np.array_equal(O.moe_combine(xi, wi, bad, E, rows), O.moe_combine(xi, wz, ids, E, rows))
+    # live rows only
+    assert O.moe_combine(x, wi, ids, E, 2).shape == (2, N)
