@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 4
+#define QIMG_ABI_VERSION 5
 
 /* status codes */
 #define QIMG_OK 0
@@ -218,6 +218,43 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * The rest of a routed MoE FFN after the gate and up projections ([P1] Coverage: GLU
+ * producers emit images, routed MUL_MAT_ID readers on MMVQ, per-slot routed projections;
+ * [P3] What this changes: padding rows get no expert work and no combine, their outputs stay
+ * unwritten). Rows are (token, slot) pairs p = row*top_k + slot; the pairs of live tokens
+ * (row < *live_rows, clamped to [0, bucket]) are live.
+ *
+ * qimg_emit_glu_per_slot: the GLU producer of qimg_emit_glu over bucket*top_k pair rows,
+ *   usually gate = the gate reader's out, up = the up reader's out, ldg = ldu = ld_pair.
+ *   Writes y and the image rows of live pairs only; img holds bucket*top_k rows
+ *   (qimg_image_bytes(bucket*top_k, K)). Rows of a live pair whose expert was out of range
+ *   hold whatever the gate/up outputs held (the routed readers skip such pairs).
+ *   bucket*top_k <= QIMG_MAX_ROUTED_PAIRS.
+ * mmvq_id_q4_0_q8_1_per_slot: mmvq_id_q4_0_q8_1 over a per-slot image: live pair p reads
+ *   image row p (not its token's row); img has bucket*top_k rows. Same workspace, plan and
+ *   errors as mmvq_id_q4_0_q8_1.
+ * qimg_moe_combine: for live rows t and n < N,
+ *   out[t*ldo + n] = sum over slots s = 0..top_k-1 with ids[t*top_k+s] in [0, E) of
+ *                    weights[t*top_k+s] * x[(t*top_k+s)*ld_pair + n],
+ *   accumulated in f32 as acc = fma(w, x, acc) from +0 in ascending slot order (the pages fix
+ *   no order; this one makes the result independent of the launch shape).
+ *   x: f32 [bucket*top_k][ld_pair] (the down reader's out), 16-byte aligned, ld_pair % 4 == 0;
+ *   weights: f32 [bucket][top_k] routing weights; ids: int32 [bucket][top_k];
+ *   out: f32 [bucket][ldo], 16-byte aligned, ldo % 4 == 0, must not overlap any input.
+ *   N % 4 == 0 (QIMG_EUNSUPPORTED otherwise). Padding rows of out are not written.
+ */
+int qimg_emit_glu_per_slot(int32_t op, const float* gate, int64_t ldg, const float* up,
+                           int64_t ldu, int32_t bucket, int32_t top_k, const int32_t* live_rows,
+                           int32_t K, float* y, int64_t ldy, void* img, void* stream);
+int mmvq_id_q4_0_q8_1_per_slot(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
+                               int32_t E, const void* img, const int32_t* ids, int32_t bucket,
+                               int32_t top_k, const int32_t* live_rows, int32_t K,
+                               void* workspace, size_t workspace_bytes, void* stream);
+int qimg_moe_combine(const float* x, int64_t ld_pair, const float* weights, const int32_t* ids,
+                     int32_t E, int32_t bucket, int32_t top_k, const int32_t* live_rows,
+                     int32_t N, float* out, int64_t ldo, void* stream);
+
+/*
  * Debug export of the per-block integer dot products of one ordinary reader, computed by the
  * same device code the readers run (the matrix-core dot of each weight block with each image
  * row): sumi[t][n][b] (int32, [rows][N][K/32]) for all image rows t < rows. sumi must not
@@ -238,6 +275,9 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
  *   fn QIMG_MATH_GEGLU  : (0.5 x) (1 + erf(x / sqrt 2)) through erfc_q (the GeGLU-erf activation)
  *   fn QIMG_MATH_RSQRT  : 1 / sqrt(x)         (the RMS scale's correctly rounded sqrt and divide)
  *   fn QIMG_MATH_QSCALE : 1 / (x / 127)       (the quantizer's d = amax/127 and 1/d)
+ *   fn QIMG_MATH_QDIV   : x / 127             (the quantizer's block scale d alone)
+ *   fn QIMG_MATH_F2H    : fp16 bits of x (round to nearest even) in the low half of the
+ *                         output word, high half zero (the image's stored d and s)
  * out: device float[n], 4-byte aligned, owned by the caller. 0 <= n <= 2^32; n = 0 is a no-op.
  * Errors: QIMG_EINVAL for a bad fn, n out of range or a null out; QIMG_EALIGN.
  */
@@ -247,6 +287,8 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
 #define QIMG_MATH_GEGLU 3
 #define QIMG_MATH_RSQRT 4
 #define QIMG_MATH_QSCALE 5
+#define QIMG_MATH_QDIV 6
+#define QIMG_MATH_F2H 7
 int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream);
 
 #ifdef __cplusplus

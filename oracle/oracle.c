@@ -259,6 +259,15 @@ void orc_quant_recip_array(const float* amax, float* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = 1.0f / orc_quant_scale(amax[i]);
 }
 
+void orc_quant_scale_array(const float* amax, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_quant_scale(amax[i]);
+}
+
+/* f32 -> binary16 bits, widened to a 32-bit word (high half zero). */
+void orc_f32_to_f16_word_array(const float* x, uint32_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(x[i]);
+}
+
 int orc_row_blocks(int K) { return ((K / 32 + 15) / 16) * 16; }
 
 int orc_quantize(const float* y, int64_t ldy, int rows, int K, uint8_t* img) {

@@ -54,6 +54,8 @@ def lib():
             "orc_mmvq_id_per_slot": (None, [P, P, i32, i32, i32, P, i32, P, i32, i32, P]),
             "orc_moe_combine": (None, [P, i64, P, P, i32, i32, i32, i32, P, i64]),
             "orc_quant_recip_array": (None, [P, P, i64]),
+            "orc_quant_scale_array": (None, [P, P, i64]),
+            "orc_f32_to_f16_word_array": (None, [P, P, i64]),
             "orc_glu": (None, [i32, P, i64, P, i64, i32, i32, P, i64]),
             "orc_rms_sumsq": (f32, [P, i32]),
             "orc_rmsnorm": (None, [P, i64, P, f32, i32, i32, P, i64]),
@@ -140,6 +142,22 @@ def quant_recip(amax, out: np.ndarray | None = None) -> np.ndarray:
     amax = np.ascontiguousarray(amax, dtype=np.float32)
     out = _out_like(amax, out)
     lib().orc_quant_recip_array(_p(amax), _p(out), amax.size)
+    return out
+
+
+def quant_scale(amax, out: np.ndarray | None = None) -> np.ndarray:
+    """amax / 127 element-wise: the quantizer's block scale d."""
+    amax = np.ascontiguousarray(amax, dtype=np.float32)
+    out = _out_like(amax, out)
+    lib().orc_quant_scale_array(_p(amax), _p(out), amax.size)
+    return out
+
+
+def f32_to_f16_words(x, out: np.ndarray | None = None) -> np.ndarray:
+    """f32 -> binary16 bits in the low half of a 32-bit word, returned as float32 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = _out_like(x, out)
+    lib().orc_f32_to_f16_word_array(_p(x), _p(out), x.size)
     return out
 
 

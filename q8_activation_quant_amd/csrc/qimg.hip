@@ -36,7 +36,13 @@ namespace {
 __device__ __forceinline__ float h2f(uint32_t h) {
   return __half2float(__ushort_as_half((unsigned short)(h & 0xffffu)));
 }
-__device__ __forceinline__ uint32_t f2h(float f) {  // round-to-nearest-even, subnormals kept
+// f32 -> fp16, round-to-nearest-even, subnormals kept. The empty asm makes f an opaque f32
+// register: without it the compiler folds a conversion of a product, fp16(a * b), into one
+// mixed-precision multiply-add (v_fma_mix) that rounds the exact product once, straight to
+// fp16, instead of rounding it to f32 first; the two differ when the f32 product is an fp16
+// tie (the image's s = fp16(f32(sum * d)) is specified with both roundings).
+__device__ __forceinline__ uint32_t f2h(float f) {
+  asm volatile("" : "+v"(f));
   return (uint32_t)__half_as_ushort(__float2half_rn(f));
 }
 
@@ -152,8 +158,10 @@ __device__ __forceinline__ float geglu_erf_act(float g) {
 // evaluation of the same operation sequence.
 // Two more functions cover the correctly rounded divisions and square root the producers rely
 // on: 1/sqrt(x) (the RMS scale) and 1/(x/127) (the quantizer's scale and its reciprocal).
+// The quantizer's block scale d = x/127 on its own and the f32 -> fp16 conversion of its
+// stored halves (result bits in the low 16 bits of the output word) are the last two.
 enum : int { MATH_EXP = 0, MATH_ERFC = 1, MATH_SWIGLU = 2, MATH_GEGLU = 3, MATH_RSQRT = 4,
-             MATH_QSCALE = 5 };
+             MATH_QSCALE = 5, MATH_QDIV = 6, MATH_F2H = 7 };
 
 template <int FN>
 __global__ __launch_bounds__(256) void eval_math_kernel(uint32_t first, int64_t n, float* out) {
@@ -166,9 +174,55 @@ __global__ __launch_bounds__(256) void eval_math_kernel(uint32_t first, int64_t 
     else if constexpr (FN == MATH_SWIGLU) v = swiglu_act(x);
     else if constexpr (FN == MATH_GEGLU) v = geglu_erf_act(x);
     else if constexpr (FN == MATH_RSQRT) v = 1.0f / __builtin_sqrtf(x);
-    else v = 1.0f / (x / 127.0f);
+    else if constexpr (FN == MATH_QSCALE) v = 1.0f / (x / 127.0f);
+    else if constexpr (FN == MATH_QDIV) v = x / 127.0f;
+    else v = __builtin_bit_cast(float, f2h(x));
     out[i] = v;
   }
+}
+
+// MoE combine ("qwen3_5 CUDA: a captured bucket's padding rows no longer go through the
+// routed experts", What this changes: only live rows are combined, padding output rows stay
+// unwritten). out[t][n] = sum over slots s (ascending) whose expert id is in [0, E) of
+// w[t][s] * x[t][s][n], one f32 fma per slot from +0. Grid (ceil(N/1024), bucket); a thread
+// owns 4 consecutive n. The x rows of up to 8 slots are loaded before any is used.
+struct CombineArgs {
+  const float* x;          // [bucket][top_k][ld_pair]
+  int64_t ld_pair;
+  const float* w;          // [bucket][top_k]
+  const int32_t* ids;      // [bucket][top_k]
+  const int32_t* live_rows;
+  float* out;              // [bucket][ldo]
+  int64_t ldo;
+  int32_t rows, top_k, E, N;
+};
+
+__global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs c) {
+  const int t = blockIdx.y;
+  if (t >= clamp_live(c.live_rows, c.rows, nullptr)) return;
+  const int n4 = blockIdx.x * 256 + threadIdx.x;
+  if (4 * n4 >= c.N) return;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s0 = 0; s0 < c.top_k; s0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // slots past top_k re-read the last slot (unused)
+      const int s = s0 + j < c.top_k ? s0 + j : c.top_k - 1;
+      v[j] = *reinterpret_cast<const float4*>(c.x + (int64_t)(t * c.top_k + s) * c.ld_pair + 4 * n4);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = t * c.top_k + s0 + j;
+      if (s0 + j < c.top_k && c.ids[p] >= 0 && c.ids[p] < c.E) {
+        const float wp = c.w[p];
+        acc.x = __builtin_fmaf(wp, v[j].x, acc.x);
+        acc.y = __builtin_fmaf(wp, v[j].y, acc.y);
+        acc.z = __builtin_fmaf(wp, v[j].z, acc.z);
+        acc.w = __builtin_fmaf(wp, v[j].w, acc.w);
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(c.out + (int64_t)t * c.ldo + 4 * n4) = acc;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -194,6 +248,7 @@ struct EmitArgs {
   uint32_t* ds;        // image ds plane
   const int32_t* live_rows;
   int32_t rows, K, Kb, RB;
+  int32_t live_mul;    // rows per live count unit: 1, or top_k for per-slot (pair) rows
   float eps;
 };
 
@@ -240,7 +295,8 @@ __device__ __forceinline__ void quantize_leaf(const float4 y, int row, int blk, 
 template <int OP, int JW>
 __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
   const int row = blockIdx.x;
-  if (row >= clamp_live(p.live_rows, p.rows, nullptr)) return;  // padding rows: untouched
+  // padding rows (past the live count, in units of live_mul rows) stay untouched
+  if (row >= clamp_live(p.live_rows, p.rows / p.live_mul, nullptr) * p.live_mul) return;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -398,6 +454,7 @@ struct ReadArgs {
   int32_t* ws;         // routed: plan workspace
   int32_t* sumi;       // debug: block dots of reader 0, [rows][N][Kb]
   int32_t n_readers, RB, Kb, KC, rows, top_k, E;
+  int32_t img_div;      // routed: image row of pair p is p / img_div (top_k: token rows; 1: per slot)
   int32_t tiles_total;  // tiles per expert summed over readers
   int32_t tp;           // image columns per LDS pass (8, 4, 2 or 1)
   int32_t tp_log2;      // log2(tp)
@@ -959,7 +1016,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           const int half = r & 1, c = (r >> 1) % TP, b = (r >> 1) / TP;
           const int kk = k < kRoutedMaxSlots ? k : 0;
           okc[j] = i < nitc && c < sh_seg[kk][2] && b < p.Kb && sh_seg[kk][0] != 0x7fffffff;
-          const int irow = okc[j] ? mem[sh_seg[kk][3] + c] / p.top_k : 0;
+          const int irow = okc[j] ? mem[sh_seg[kk][3] + c] / p.img_div : 0;
           const uint32_t src = okc[j] ? (uint32_t)(irow * p.RB + b) * 32u + 16u * half : 0u;
           v[j] = *reinterpret_cast<const uint4*>(p.codes + src);
         }
@@ -970,7 +1027,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           const int c = r & 7, b = r >> 3;
           const int kk = k < kRoutedMaxSlots ? k : 0;
           okd[j] = i < nitd && c < sh_seg[kk][2] && b < p.Kb && sh_seg[kk][0] != 0x7fffffff;
-          const int irow = okd[j] ? mem[sh_seg[kk][3] + c] / p.top_k : 0;
+          const int irow = okd[j] ? mem[sh_seg[kk][3] + c] / p.img_div : 0;
           dw[j] = p.ds[okd[j] ? (uint32_t)(irow * p.RB + b) : 0u];
         }
 #pragma unroll
@@ -1451,7 +1508,7 @@ int64_t qimg_image_bytes(int32_t rows, int32_t K) {
 
 static int emit_common(int op, const float* a, int64_t lda, const float* b, int64_t ldb,
                        int b_rows, float eps, int32_t rows, const int32_t* live_rows, int32_t K,
-                       float* y, int64_t ldy, void* img, void* stream) {
+                       float* y, int64_t ldy, void* img, void* stream, int32_t live_mul = 1) {
   int st = check_k(K);
   if (st) return st;
   if (rows < 0) return QIMG_EINVAL;
@@ -1479,6 +1536,7 @@ static int emit_common(int op, const float* a, int64_t lda, const float* b, int6
   e.codes = (uint8_t*)img;
   e.ds = img ? (uint32_t*)((uint8_t*)img + (size_t)rows * RB * 32) : nullptr;
   e.live_rows = live_rows; e.rows = rows; e.K = K; e.Kb = K / 32; e.RB = RB; e.eps = eps;
+  e.live_mul = live_mul;
   return launch_emit(op, e, (hipStream_t)stream);
 }
 
@@ -1496,6 +1554,17 @@ int qimg_emit_glu(int32_t op, const float* gate, int64_t ldg, const float* up, i
   // gate and up may be the two halves of one packed row (they must not overlap each other's
   // elements, which packed halves do not)
   return emit_common(kop, gate, ldg, up, ldu, 2, 0.0f, rows, live_rows, K, y, ldy, img, stream);
+}
+
+int qimg_emit_glu_per_slot(int32_t op, const float* gate, int64_t ldg, const float* up,
+                           int64_t ldu, int32_t bucket, int32_t top_k, const int32_t* live_rows,
+                           int32_t K, float* y, int64_t ldy, void* img, void* stream) {
+  if (op != QIMG_GLU_SWIGLU && op != QIMG_GLU_GEGLU_ERF) return QIMG_EINVAL;
+  if (bucket < 0 || top_k <= 0) return QIMG_EINVAL;
+  if ((int64_t)bucket * top_k > QIMG_MAX_ROUTED_PAIRS) return QIMG_EUNSUPPORTED;
+  const int kop = op == QIMG_GLU_SWIGLU ? OP_SWIGLU : OP_GEGLU;
+  return emit_common(kop, gate, ldg, up, ldu, 2, 0.0f, bucket * top_k, live_rows, K, y, ldy, img,
+                     stream, top_k);
 }
 
 int qimg_quantize_q8_1(const float* y, int64_t ldy, int32_t rows, const int32_t* live_rows,
@@ -1593,10 +1662,12 @@ size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E) {
   return (words * 4 + 255) & ~(size_t)255;
 }
 
-int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
-                      const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
-                      const int32_t* live_rows, int32_t K, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+// per_slot = 0: the image holds one row per token (pair p reads row p / top_k);
+// per_slot = 1: one row per (token, slot) pair (pair p reads row p).
+static int routed_common(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
+                         const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
+                         const int32_t* live_rows, int32_t K, void* workspace,
+                         size_t workspace_bytes, int per_slot, void* stream) {
   int st = check_k(K);
   if (st) return st;
   if (!readers || n_readers < 1 || n_readers > QIMG_MAX_READERS || E <= 0 || bucket < 0 ||
@@ -1608,7 +1679,9 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
     return QIMG_EWORKSPACE;
   if (!al16(workspace) || !al(ids, 4) || (live_rows && !al(live_rows, 4))) return QIMG_EALIGN;
   const int64_t pairs = (int64_t)bucket * top_k;
-  const Span si = span(img, qimg_image_bytes(bucket, K));
+  if (pairs > QIMG_MAX_ROUTED_PAIRS || E > QIMG_MAX_EXPERTS) return QIMG_EUNSUPPORTED;
+  const int32_t img_rows = per_slot ? (int32_t)pairs : bucket;
+  const Span si = span(img, qimg_image_bytes(img_rows, K));
   const Span sids = span(ids, pairs * 4);
   const Span sl = live_rows ? span(live_rows, 4) : Span{0, 0};
   const Span sw = span(workspace, (int64_t)mmvq_id_workspace_bytes(bucket, top_k, E));
@@ -1628,7 +1701,6 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
     for (int j = 0; j < i; ++j)
       if (overlap(outs[i], outs[j])) return QIMG_EALIAS;
   }
-  if (pairs > QIMG_MAX_ROUTED_PAIRS || E > QIMG_MAX_EXPERTS) return QIMG_EUNSUPPORTED;
   ReadArgs a{};
   int tiles = 0;
   for (int i = 0; i < n_readers; ++i) {
@@ -1640,14 +1712,54 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
     tiles += (r.N + 15) / 16;
   }
   a.tile_start[n_readers] = tiles;
-  fill_common(a, img, bucket, K);
+  fill_common(a, img, img_rows, K);
+  a.rows = bucket;
   a.live_rows = live_rows;
   a.ids = ids;
   a.ws = (int32_t*)workspace;
   a.n_readers = n_readers;
   a.top_k = top_k;
+  a.img_div = per_slot ? 1 : top_k;
   a.E = E;
   return run_routed(a, (int)pairs, (hipStream_t)stream);
+}
+
+int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
+                      const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
+                      const int32_t* live_rows, int32_t K, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return routed_common(readers, n_readers, E, img, ids, bucket, top_k, live_rows, K, workspace,
+                       workspace_bytes, 0, stream);
+}
+
+int mmvq_id_q4_0_q8_1_per_slot(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
+                               int32_t E, const void* img, const int32_t* ids, int32_t bucket,
+                               int32_t top_k, const int32_t* live_rows, int32_t K,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return routed_common(readers, n_readers, E, img, ids, bucket, top_k, live_rows, K, workspace,
+                       workspace_bytes, 1, stream);
+}
+
+int qimg_moe_combine(const float* x, int64_t ld_pair, const float* weights, const int32_t* ids,
+                     int32_t E, int32_t bucket, int32_t top_k, const int32_t* live_rows,
+                     int32_t N, float* out, int64_t ldo, void* stream) {
+  if (bucket < 0 || top_k <= 0 || E <= 0 || N <= 0 || !x || !weights || !ids || !out ||
+      ld_pair < N || ldo < N)
+    return QIMG_EINVAL;
+  if (bucket == 0) return QIMG_OK;
+  if (N % 4) return QIMG_EUNSUPPORTED;
+  if (!al16(x) || ld_pair % 4 || !al16(out) || ldo % 4 || !al(weights, 4) || !al(ids, 4) ||
+      (live_rows && !al(live_rows, 4)))
+    return QIMG_EALIGN;
+  const int64_t pairs = (int64_t)bucket * top_k;
+  const Span so = span(out, rows_extent(bucket, ldo, N, 4));
+  if (overlap(so, span(x, rows_extent(pairs, ld_pair, N, 4))) || overlap(so, span(weights, pairs * 4)) ||
+      overlap(so, span(ids, pairs * 4)) || (live_rows && overlap(so, span(live_rows, 4))))
+    return QIMG_EALIAS;
+  CombineArgs c{x, ld_pair, weights, ids, live_rows, out, ldo, bucket, top_k, E, N};
+  const dim3 grid((unsigned)((N / 4 + 255) / 256), (unsigned)bucket);
+  hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, (hipStream_t)stream, c);
+  return launch_status();
 }
 
 int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, int32_t rows,
@@ -1677,7 +1789,7 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
 }
 
 int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream) {
-  if (fn < MATH_EXP || fn > MATH_QSCALE || n < 0 || n > ((int64_t)1 << 32)) return QIMG_EINVAL;
+  if (fn < MATH_EXP || fn > MATH_F2H || n < 0 || n > ((int64_t)1 << 32)) return QIMG_EINVAL;
   if (n == 0) return QIMG_OK;
   if (!out) return QIMG_EINVAL;
   if (!al(out, 4)) return QIMG_EALIGN;
@@ -1690,7 +1802,9 @@ int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void*
     case MATH_SWIGLU: eval_math_kernel<MATH_SWIGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
     case MATH_GEGLU: eval_math_kernel<MATH_GEGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
     case MATH_RSQRT: eval_math_kernel<MATH_RSQRT><<<grid, 256, 0, s>>>(first_bits, n, out); break;
-    default: eval_math_kernel<MATH_QSCALE><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_QSCALE: eval_math_kernel<MATH_QSCALE><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_QDIV: eval_math_kernel<MATH_QDIV><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    default: eval_math_kernel<MATH_F2H><<<grid, 256, 0, s>>>(first_bits, n, out); break;
   }
   return launch_status();
 }

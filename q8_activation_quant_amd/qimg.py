@@ -18,15 +18,16 @@ GLU_SWIGLU, GLU_GEGLU_ERF = 0, 1
 GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
     "qimg_emit_rmsnorm", "qimg_emit_glu", "qimg_quantize_q8_1", "mmvq_q4_0_q8_1",
     "mmvq_id_workspace_bytes", "mmvq_id_q4_0_q8_1", "mmvq_q4_0_q8_1_blockdots",
     "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile", "qimg_eval_math",
+    "qimg_emit_glu_per_slot", "mmvq_id_q4_0_q8_1_per_slot", "qimg_moe_combine",
 )
-MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5}
+MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7}
 
 
 class QimgError(RuntimeError):
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
             "qimg_q4_0_tiled_bytes": (i64, [i32, i32, i32]),
             "qimg_q4_0_tile": (ctypes.c_int, [P, P, i32, i32, i32, P, P]),
             "qimg_eval_math": (ctypes.c_int, [i32, ctypes.c_uint32, i64, P, P]),
+            "qimg_emit_glu_per_slot": (ctypes.c_int, [i32, P, i64, P, i64, i32, i32, P, i32, P, i64, P, P]),
+            "mmvq_id_q4_0_q8_1_per_slot": (ctypes.c_int, [ctypes.POINTER(ExpertReader), i32, i32, P, P,
+                                                          i32, i32, P, i32, P, ctypes.c_size_t, P]),
+            "qimg_moe_combine": (ctypes.c_int, [P, i64, P, P, i32, i32, i32, P, i32, P, i64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -182,6 +187,42 @@ def mmvq_id(readers, E, img, ids, live_rows, K, workspace, stream=None):
     _check(lib().mmvq_id_q4_0_q8_1(arr, len(readers), E, _ptr(img), _ptr(ids), bucket, top_k,
                                    _ptr(live_rows), K, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "mmvq_id_q4_0_q8_1")
+
+
+def _pair_ld(t):
+    """Row stride of the (token, slot) pair rows of a [bucket, top_k, width] tensor."""
+    assert t.dim() == 3 and t.stride(2) == 1 and t.stride(0) == t.shape[1] * t.stride(1), \
+        "pair tensors are [bucket, top_k, width] with evenly spaced pair rows"
+    return t.stride(1)
+
+
+def mmvq_id_per_slot(readers, E, img, ids, live_rows, K, workspace, stream=None):
+    """Routed readers over a per-slot image (image row = pair): as mmvq_id, img has
+    bucket*top_k rows."""
+    bucket, top_k = ids.shape
+    arr = _readers(readers, ExpertReader)
+    _check(lib().mmvq_id_q4_0_q8_1_per_slot(arr, len(readers), E, _ptr(img), _ptr(ids), bucket, top_k,
+                                            _ptr(live_rows), K, _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream)),
+           "mmvq_id_q4_0_q8_1_per_slot")
+
+
+def emit_glu_per_slot(op, gate, up, y, img=None, live_rows=None, stream=None):
+    """y [bucket, top_k, K] = act(gate) * up over the pair rows of live tokens; gate and up are
+    [bucket, top_k, K] views (e.g. the routed gate and up readers' outputs)."""
+    op = GLU_OPS[op] if isinstance(op, str) else op
+    bucket, top_k, K = gate.shape
+    _check(lib().qimg_emit_glu_per_slot(op, _ptr(gate), _pair_ld(gate), _ptr(up), _pair_ld(up), bucket,
+                                        top_k, _ptr(live_rows), K, _ptr(y), _pair_ld(y), _ptr(img),
+                                        _stream(stream)), "qimg_emit_glu_per_slot")
+
+
+def moe_combine(x, weights, ids, E, out, live_rows=None, stream=None):
+    """out [bucket, N] = routing-weighted sum over the slots of x [bucket, top_k, N] (live rows)."""
+    bucket, top_k, N = x.shape
+    _check(lib().qimg_moe_combine(_ptr(x), _pair_ld(x), _ptr(weights), _ptr(ids), E, bucket, top_k,
+                                  _ptr(live_rows), N, _ptr(out), _ld(out), _stream(stream)),
+           "qimg_moe_combine")
 
 
 def blockdots(w, N, img, rows, K, sumi, stream=None):

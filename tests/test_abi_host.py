@@ -247,3 +247,63 @@ def test_mmvq_id_limits(L):
                                qimg.workspace_bytes(1024, 5, 8), S) == qimg.EUNSUPPORTED
     assert L.mmvq_id_q4_0_q8_1(r, 1, 1025, D, IDS, 8, 2, None, 256, WS,
                                qimg.workspace_bytes(8, 2, 1025), S) == qimg.EUNSUPPORTED
+
+
+def test_per_slot_routed_validation(L):
+    """The per-slot image has bucket*top_k rows: an image that overlaps an output within that
+    extent (but past a token-row image) is an alias only for the per-slot reader."""
+    E, bucket, k, K = 8, 16, 4, 256
+    ws_bytes = qimg.workspace_bytes(bucket, k, E)
+    WS, IDS = B, B + (1 << 20)
+    out = D + qimg.image_bytes(bucket, K) + 256  # just past a token-row image
+    r = expert_readers((A, 64, out, 64))
+    per = L.mmvq_id_q4_0_q8_1_per_slot
+    args = lambda f, **kw: f(kw.get("r", r), 1, E, D, IDS, kw.get("bucket", bucket), k, None, K, WS,
+                             ws_bytes, S)
+    assert args(per) == qimg.EALIAS
+    assert args(per, bucket=0) == qimg.OK
+    assert per(r, 1, E, D, IDS, bucket, k, None, 100, WS, ws_bytes, S) == qimg.EINVAL
+    assert per(r, 1, E, D, IDS, 1024, 5, None, K, WS, qimg.workspace_bytes(1024, 5, E), S) == qimg.EUNSUPPORTED
+
+
+def test_emit_glu_per_slot_validation(L):
+    def glu(op=0, g=A, ldg=512, u=A + 1024, ldu=512, bucket=4, k=2, K=256, y=C, ldy=256, img=D):
+        return L.qimg_emit_glu_per_slot(op, g, ldg, u, ldu, bucket, k, None, K, y, ldy, img, S)
+
+    assert glu(op=2) == qimg.EINVAL
+    assert glu(k=0) == qimg.EINVAL
+    assert glu(bucket=-1) == qimg.EINVAL
+    assert glu(bucket=0) == qimg.OK
+    assert glu(bucket=1025, k=4) == qimg.EUNSUPPORTED
+    assert glu(K=48) == qimg.EINVAL
+    assert glu(u=A + 1028) == qimg.EALIGN
+    # the image spans bucket*top_k rows: 8 rows here
+    assert glu(img=C - qimg.image_bytes(8, 256) + 16) == qimg.EALIAS
+
+
+def test_moe_combine_validation(L):
+    def comb(x=A, ldp=256, w=B, ids=B + 4096, E=8, bucket=4, k=2, live=None, N=256, out=C, ldo=256):
+        return L.qimg_moe_combine(x, ldp, w, ids, E, bucket, k, live, N, out, ldo, S)
+
+    assert comb(x=None) == qimg.EINVAL
+    assert comb(w=None) == qimg.EINVAL
+    assert comb(ids=None) == qimg.EINVAL
+    assert comb(out=None) == qimg.EINVAL
+    assert comb(E=0) == qimg.EINVAL
+    assert comb(k=0) == qimg.EINVAL
+    assert comb(N=0) == qimg.EINVAL
+    assert comb(ldp=128) == qimg.EINVAL
+    assert comb(ldo=128) == qimg.EINVAL
+    assert comb(bucket=-1) == qimg.EINVAL
+    assert comb(bucket=0) == qimg.OK
+    assert comb(N=250, ldp=256, ldo=256) == qimg.EUNSUPPORTED
+    assert comb(x=A + 4) == qimg.EALIGN
+    assert comb(out=C + 8) == qimg.EALIGN
+    assert comb(ldo=258) == qimg.EALIGN
+    assert comb(ldp=258) == qimg.EALIGN
+    assert comb(w=B + 2) == qimg.EALIGN
+    assert comb(live=B + 8192 + 2) == qimg.EALIGN
+    assert comb(out=A + 1024) == qimg.EALIAS
+    assert comb(out=B) == qimg.EALIAS
+    assert comb(out=B + 4096) == qimg.EALIAS
+    assert comb(live=C + 64) == qimg.EALIAS

@@ -28,7 +28,16 @@ ORACLE = {
     "geglu_erf": lambda x, out: O.glu_act(x, "geglu_erf", out),
     "rsqrt": lambda x, out: O.rms_scale(x, out),
     "qscale": lambda x, out: O.quant_recip(x, out),
+    "qdiv": lambda x, out: O.quant_scale(x, out),
+    "f2h": lambda x, out: O.f32_to_f16_words(x, out),
 }
+
+
+def _is_nan(fn, bits):
+    """NaN results (any payload): f32 NaNs, or binary16 NaNs for the f16 conversion."""
+    if fn == "f2h":
+        return ((bits & 0x7C00) == 0x7C00) & ((bits & 0x3FF) != 0)
+    return np.isnan(bits.view(np.float32))
 
 
 class _Slot:
@@ -48,7 +57,7 @@ class _Slot:
         np.not_equal(wb, got_bits, out=self.bad)
         if not self.bad.any():
             return 0, []
-        self.bad &= ~(np.isnan(self.want) & np.isnan(got_bits.view(np.float32)))
+        self.bad &= ~(_is_nan(fn, wb) & _is_nan(fn, got_bits))
         idx = np.flatnonzero(self.bad)
         return idx.size, [(int(self.x[i]), int(wb[i]), int(got_bits[i])) for i in idx[:4]]
 
@@ -98,7 +107,7 @@ def test_eval_math_rejects_bad_arguments():
     torch = H.torch()
     out = torch.empty(16, dtype=torch.float32, device="cuda")
     with pytest.raises(qimg.QimgError):
-        qimg.eval_math(6, 0, out)
+        qimg.eval_math(8, 0, out)
     st = qimg.lib().qimg_eval_math(0, 0, (1 << 32) + 1, qimg._ptr(out), None)
     assert st == qimg.EINVAL
     assert qimg.lib().qimg_eval_math(0, 0, 0, None, None) == qimg.OK

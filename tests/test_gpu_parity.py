@@ -147,6 +147,36 @@ def test_quantizer_golden_and_special_blocks():
     assert np.array_equal(H.host(img), O.quantize(y))
 
 
+def fp16_double_rounding_blocks(y):
+    """Blocks whose stored sum s16 = fp16(f32(sum * d)) differs from a single rounding of the
+    exact product to fp16: the f32 product is an exact fp16 tie and the exact product is not.
+    Found from the oracle's image (codes and d of each block)."""
+    rows, K = y.shape
+    img = O.quantize(y)
+    codes, d16, s16 = O.image_planes(img, rows, K)
+    Kb = K // 32
+    blocks = y.reshape(rows, Kb, 32)
+    d = (np.abs(blocks).max(-1) / np.float32(127.0)).astype(np.float32)
+    csum = codes[:, :Kb].astype(np.int64).sum(-1)
+    p32 = (csum.astype(np.float32) * d).astype(np.float32)
+    bits = p32.view(np.uint32)
+    tie = ((bits & 0x1FFF) == 0x1000) & (np.abs(p32) >= 2.0 ** -14) & (np.abs(p32) < 65504)
+    inexact = csum.astype(np.float64) * d.astype(np.float64) != p32.astype(np.float64)
+    return img, np.argwhere(tie & inexact)
+
+
+def test_quantizer_sum_is_rounded_to_f32_then_fp16():
+    # regression: fp16(a * b) must not become one mixed-precision multiply-add (a single rounding)
+    g = np.random.default_rng(17)
+    y = g.standard_normal((4096, 512)).astype(np.float32)
+    img_o, ties = fp16_double_rounding_blocks(y)
+    assert len(ties) >= 3, "the sample should hold a few fp16 double-rounding blocks"
+    img = H.sentinel_u8(qimg.image_bytes(4096, 512))
+    qimg.quantize_q8_1(H.dev(y), img)
+    sync()
+    assert np.array_equal(H.host(img), img_o)
+
+
 # ---- block dots ----------------------------------------------------------------------------------
 @pytest.mark.parametrize("K,T", [(32, 3), (2592, 13), (8192, 8), (14336, 5)])
 def test_blockdots_bit_exact(K, T):
