@@ -6,8 +6,10 @@ three readers N=8192/1024/1024 (the ordinary K8192/T8 component graph).
 
 Timing: a HIP graph holds R instances of the step, each with its own copy of every tensor,
 with R x weights >= 1 GiB so replays stream weights from HBM rather than from the 256 MB
-Infinity Cache. W warmup steps, then exactly K timed steps, bracketed by synchronisation.
-The reader kernel is also timed alone (a graph of R reader launches) for the roofline line.
+Infinity Cache (the instances repeat in order until the graph holds at least 32 steps). W
+warmup steps, then exactly K timed steps, bracketed by synchronisation. The reader kernel is
+also timed alone (a graph of reader launches over the same instances) for the roofline line.
+--moe times the whole routed MoE FFN of the routed workloads the same way.
 The CPU baseline is the plain oracle on the host, single-threaded, on a bounded sample.
 
 Prints one JSON line.
@@ -119,6 +121,102 @@ def algorithmic_bytes(wl):
             "reader_kernel": img + w + out + ids}
 
 
+class MoeInstance:
+    """Device tensors of one routed MoE FFN: RMS producer + image -> gate/up experts -> per-slot
+    SwiGLU + image -> per-slot down experts -> combine with the routing weights."""
+
+    def __init__(self, wl):
+        from q8_activation_quant_amd import qimg
+        torch = _t()
+        self.wl = wl
+        B, k, K, F = wl.T, wl.top_k, wl.K, wl.n_ff
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+        self.x, self.gamma = dev(wl.x), dev(wl.gamma)
+        self.ids, self.w = dev(wl.ids), dev(wl.route_w)
+        self.live = torch.tensor([wl.live if wl.live is not None else B], dtype=torch.int32, device="cuda")
+        f32 = lambda *sh: torch.empty(*sh, dtype=torch.float32, device="cuda")
+        self.y, self.img = f32(B, K), torch.empty(qimg.image_bytes(B, K), dtype=torch.uint8, device="cuda")
+        self.gate, self.up, self.h = f32(B, k, F), f32(B, k, F), f32(B, k, F)
+        self.himg = torch.empty(qimg.image_bytes(B * k, F), dtype=torch.uint8, device="cuda")
+        self.down, self.out = f32(B, k, K), f32(B, K)
+        ws = qimg.workspace_bytes(B, k, wl.E) // 4
+        self.ws1 = torch.empty(ws, dtype=torch.int32, device="cuda")
+        self.ws2 = torch.empty(ws, dtype=torch.int32, device="cuda")
+        self.wg = qimg.tile_q4_0(dev(wl.readers[0].qs), dev(wl.readers[0].d), K)
+        self.wu = qimg.tile_q4_0(dev(wl.readers[1].qs), dev(wl.readers[1].d), K)
+        self.wd = qimg.tile_q4_0(dev(wl.down.qs), dev(wl.down.d), F)
+
+    def produce(self):
+        from q8_activation_quant_amd import qimg
+        qimg.emit_rmsnorm(self.x, self.gamma, 1e-6, self.y, self.img, self.live)
+
+    def gate_up(self):
+        from q8_activation_quant_amd import qimg
+        wl = self.wl
+        qimg.mmvq_id([(self.wg, wl.n_ff, self.gate), (self.wu, wl.n_ff, self.up)], wl.E, self.img, self.ids,
+                     self.live, wl.K, self.ws1)
+
+    def glu(self):
+        from q8_activation_quant_amd import qimg
+        qimg.emit_glu_per_slot("swiglu", self.gate, self.up, self.h, self.himg, self.live)
+
+    def down_proj(self):
+        from q8_activation_quant_amd import qimg
+        wl = self.wl
+        qimg.mmvq_id_per_slot([(self.wd, wl.K, self.down)], wl.E, self.himg, self.ids, self.live, wl.n_ff,
+                              self.ws2)
+
+    def combine(self):
+        from q8_activation_quant_amd import qimg
+        qimg.moe_combine(self.down, self.w, self.ids, self.wl.E, self.out, self.live)
+
+    def step(self):
+        self.produce()
+        self.gate_up()
+        self.glu()
+        self.down_proj()
+        self.combine()
+
+
+def moe_bytes(wl):
+    """Algorithmic bytes of one MoE FFN (live rows L, pairs P = L top_k, distinct experts U):
+    x, gamma read, y written, token image written and read; gate/up weights of U experts; ids
+    read by both routed launches; gate/up outputs written and read by the GLU; h written; the
+    per-slot image written and read; down weights of U experts; down outputs written and read
+    by the combine; routing weights and ids read by the combine; the output written."""
+    B, k, K, F = wl.T, wl.top_k, wl.K, wl.n_ff
+    L = wl.live if wl.live is not None else B
+    P = L * k
+    U = len(np.unique(wl.ids[:L].reshape(-1)))
+    img_tok = L * (K // 32) * 36
+    img_pair = P * (F // 32) * 36
+    parts = {
+        "producer": L * K * 4 + K * 4 + L * K * 4 + img_tok,
+        "gate_up": img_tok + U * 2 * F * (K // 32) * 18 + P * 4 + 2 * P * F * 4,
+        "glu": 2 * P * F * 4 + P * F * 4 + img_pair,
+        "down": img_pair + U * K * (F // 32) * 18 + P * 4 + P * K * 4,
+        "combine": P * K * 4 + 2 * P * 4 + L * K * 4,
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def run_moe(config, steps, warmup, live=None):
+    torch = _t()
+    from q8_activation_quant_amd import workloads as W
+    wl = W.make(config, live=live, moe=True)
+    wbytes = sum(r.nbytes for r in wl.readers) + wl.down.nbytes
+    R = max(1, int(np.ceil(ROT_BYTES / wbytes)))
+    insts = [MoeInstance(wl) for _ in range(R)]
+    res = {"wl": wl, "R": R, "bytes": moe_bytes(wl)}
+    res["us"] = time_graph([i.step for i in insts], steps, warmup)
+    for part in ("produce", "gate_up", "glu", "down_proj", "combine"):
+        res[part] = float(np.median(time_graph([getattr(i, part) for i in insts], steps, warmup)))
+    del insts
+    torch.cuda.empty_cache()
+    return res
+
+
 def weight_bytes(wl):
     return sum(r.qs.nbytes + r.d.nbytes for r in wl.readers)
 
@@ -128,11 +226,16 @@ def make_instances(wl, rot_bytes=ROT_BYTES):
     return [Instance(wl) for _ in range(R)]
 
 
+MIN_GRAPH_CALLS = 32
+
+
 def time_graph(fns, steps, warmup, runs=3):
-    """Capture fns (one call per instance) in one graph; replay to cover `warmup` then exactly
-    `steps` calls (a remainder graph covers steps not divisible by the instance count).
-    Returns the per-call microseconds of each run."""
+    """Capture fns (one call per instance, repeated in order until the graph holds at least
+    MIN_GRAPH_CALLS calls, so a replay's fixed launch cost is spread over many calls) in one
+    graph; replay to cover `warmup` then exactly `steps` calls (a remainder graph covers steps
+    not divisible by the graph's call count). Returns the per-call microseconds of each run."""
     torch = _t()
+    fns = list(fns) * max(1, -(-MIN_GRAPH_CALLS // len(fns)))
     R = len(fns)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -262,6 +365,8 @@ def main():
     ap.add_argument("--glu", default="swiglu", choices=["swiglu", "geglu_erf"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print one extra line per workload")
+    ap.add_argument("--moe", action="store_true",
+                    help="time the whole routed MoE FFN of workload 4 (or 5 with --config 5) instead")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="counter-collection run: one reader launch per rotated instance of the "
                          "workload, then a plain 256 MiB device copy (the calibration kernel)")
@@ -275,6 +380,31 @@ def main():
     from q8_activation_quant_amd import qimg
     qimg.lib()
 
+    if args.moe:
+        cfg = args.config if args.config in (4, 5) else 4
+        r = run_moe(cfg, args.steps, args.warmup, live=args.live)
+        wl, nb = r["wl"], r["bytes"]
+        us = float(np.median(r["us"]))
+        down_gbs = nb["down"] / (r["down_proj"] * 1e-6) / 1e9
+        print(json.dumps({
+            "metric": "us per routed MoE FFN + achieved HBM GB/s (% of peak), 1 MI355X",
+            "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(us / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int8xu4->int32 dots, f32 producers, accumulation and combine",
+            "data": "synthetic (seeded numpy PCG64; shapes/distributions of the workload)",
+            "config": {"workload": wl.name, "T": wl.T, "K": wl.K, "E": wl.E, "top_k": wl.top_k,
+                       "n_ff": wl.n_ff, "live_rows": wl.live, "graph_instances": r["R"]},
+            "us_range": [round(min(r["us"]), 3), round(max(r["us"]), 3)],
+            "algorithmic_bytes": nb,
+            "achieved_GBs": round(nb["total"] / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * nb["total"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "launch_us": {p: round(r[p], 3) for p in ("produce", "gate_up", "glu", "down_proj", "combine")},
+            "roofline": {"bound": "hbm", "kernel": "mmvq_routed_kernel (per-slot down projection)",
+                         "achieved": round(down_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(down_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_launch": nb["down"], "avg_launch_us": round(r["down_proj"], 3)},
+        }), flush=True)
+        return
     if args.pmc_probe:
         from q8_activation_quant_amd import workloads as W
         wl = W.make(args.config, live=args.live, glu_op=args.glu)
