@@ -151,16 +151,52 @@ void orc_erfc_q_array(const float* z, float* out, int64_t n) {
  *   GeGLU-erf : act(g) = g * Phi(g) = 0.5 * g * (1 + erf(g / sqrt 2))
  * with 1 + erf(z) = erfc(-z) for z < 0 and 2 - erfc(z) for z >= 0. y = act(g) * u.
  * ---------------------------------------------------------------------------------------- */
+/* g * sigmoid(c g) = g / (1 + exp(-c g)), the shape shared by SwiGLU (c = 1), GeGLU-quick
+ * (c = 1.702) and SwiGLU-OAI (c = alpha). */
+static float g_sigmoid(float g, float c) {
+  float e = orc_exp_q(-(c * g));
+  float den = 1.0f + e;
+  return g / den;
+}
+
 float orc_glu_act(int op, float g) {
   if (op == 0) {
     float e = orc_exp_q(-g);
     float den = 1.0f + e;
     return g / den;
-  } else {
+  } else if (op == 1) {
     float z = g * (float)M_SQRT1_2;
     float ope = (z < 0.0f) ? orc_erfc_q(-z) : 2.0f - orc_erfc_q(z);
     return (0.5f * g) * ope;
+  } else if (op == 2) {
+    /* ReGLU: relu(g) */
+    return g > 0.0f ? g : 0.0f;
+  } else if (op == 3) {
+    /* GeGLU, tanh form: 0.5 g (1 + tanh(z)), z = sqrt(2/pi) (g + 0.044715 g^3). With
+     * 0.5 (1 + tanh z) = 1 / (1 + exp(-2z)) it is g / (1 + exp(-c2 (g + 0.044715 g^3))),
+     * c2 = 2 sqrt(2/pi) rounded to f32 (no cancellation for either sign of g). */
+    float g3 = (g * g) * g;
+    float inner = g + 0.044715f * g3;
+    float e = orc_exp_q(-((float)(2.0 * sqrt(2.0 / M_PI)) * inner));
+    float den = 1.0f + e;
+    return g / den;
+  } else {
+    /* GeGLU-quick: g sigmoid(1.702 g) */
+    return g_sigmoid(g, 1.702f);
   }
+}
+
+/* The GLU family with the gate/up clamps of the OpenAI-style SwiGLU:
+ *   op 5 SwiGLU-OAI  : g' = min(g, limit), u' = clamp(u, -limit, limit),
+ *                      y = g' sigmoid(alpha g') * (u' + 1)
+ *   op 6 SwiGLU-clamp: g' = min(g, limit), u' = clamp(u, -limit, limit), y = silu(g') * u'
+ * ops 0..4: y = act(g) * u with orc_glu_act. alpha and limit are used by ops 5 and 6 only. */
+float orc_glu_pair(int op, float alpha, float limit, float g, float u) {
+  if (op < 5) return orc_glu_act(op, g) * u;
+  float gg = g < limit ? g : limit;
+  float uu = u < -limit ? -limit : (u > limit ? limit : u);
+  if (op == 5) return g_sigmoid(gg, alpha) * (uu + 1.0f);
+  return orc_glu_act(0, gg) * uu;
 }
 
 void orc_glu_act_array(int op, const float* g, float* out, int64_t n) {
@@ -174,6 +210,18 @@ void orc_glu(int op, const float* gate, int64_t ldg, const float* up, int64_t ld
       float act = orc_glu_act(op, gate[(int64_t)i * ldg + k]);
       y[(int64_t)i * ldy + k] = act * up[(int64_t)i * ldu + k];
     }
+}
+
+/* Every GLU variant of "Share temporary Q8_1 activation images", Coverage (F32 ReGLU, GeGLU,
+ * SwiGLU, GeGLU-erf, GeGLU-quick, SwiGLU-OAI and SwiGLU-clamp producers keep their formulas
+ * and alpha/limit parameters; separate, packed and packed-swapped inputs keep independent
+ * row strides): y[i][k] = orc_glu_pair(op, alpha, limit, gate[i][k], up[i][k]). */
+void orc_glu_ex(int op, float alpha, float limit, const float* gate, int64_t ldg, const float* up,
+                int64_t ldu, int rows, int K, float* y, int64_t ldy) {
+  for (int i = 0; i < rows; ++i)
+    for (int k = 0; k < K; ++k)
+      y[(int64_t)i * ldy + k] =
+          orc_glu_pair(op, alpha, limit, gate[(int64_t)i * ldg + k], up[(int64_t)i * ldu + k]);
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -235,6 +283,26 @@ void orc_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps, int
     for (int k = 0; k < K; ++k) {
       float t = xr[k] * r;
       y[(int64_t)i * ldy + k] = gamma ? t * gamma[k] : t;
+    }
+  }
+}
+
+/* The RMS+MUL+ADD and RMS+SCALE producers ("Share temporary Q8_1 activation images",
+ * Coverage: RMS-alone, RMS+MUL, RMS+MUL+ADD and RMS+SCALE producers emit images):
+ *   t = x * r; if gamma: t = t * gamma; if beta: t = t + beta; y = t * scale,
+ * each one f32 rounding, in that order (scale = 1 leaves t unchanged). */
+void orc_rmsnorm_ex(const float* x, int64_t ldx, const float* gamma, const float* beta,
+                    float scale, float eps, int rows, int K, float* y, int64_t ldy) {
+  for (int i = 0; i < rows; ++i) {
+    const float* xr = x + (int64_t)i * ldx;
+    float S = orc_rms_sumsq(xr, K);
+    float mean = S / (float)K;
+    float r = orc_rms_scale(mean + eps);
+    for (int k = 0; k < K; ++k) {
+      float t = xr[k] * r;
+      if (gamma) t = t * gamma[k];
+      if (beta) t = t + beta[k];
+      y[(int64_t)i * ldy + k] = t * scale;
     }
   }
 }

@@ -50,6 +50,8 @@ def lib():
             "orc_erfc_q_array": (None, [P, P, i64]),
             "orc_glu_act": (f32, [i32, f32]),
             "orc_glu_act_array": (None, [i32, P, P, i64]),
+            "orc_glu_ex": (None, [i32, f32, f32, P, i64, P, i64, i32, i32, P, i64]),
+            "orc_rmsnorm_ex": (None, [P, i64, P, P, f32, f32, i32, i32, P, i64]),
             "orc_rms_scale_array": (None, [P, P, i64]),
             "orc_mmvq_id_per_slot": (None, [P, P, i32, i32, i32, P, i32, P, i32, i32, P]),
             "orc_moe_combine": (None, [P, i64, P, P, i32, i32, i32, i32, P, i64]),
@@ -178,7 +180,9 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray | None, eps: float, rows: int | Non
     return y
 
 
-GLU_OPS = {"swiglu": 0, "geglu_erf": 1}
+GLU_OPS = {"swiglu": 0, "geglu_erf": 1, "reglu": 2, "geglu": 3, "geglu_quick": 4, "swiglu_oai": 5,
+           "swiglu_clamp": 6}
+OAI_ALPHA, OAI_LIMIT = 1.702, 7.0  # the OpenAI-style SwiGLU defaults
 
 
 def glu(gu: np.ndarray, op: str, rows: int | None = None) -> np.ndarray:
@@ -191,6 +195,34 @@ def glu(gu: np.ndarray, op: str, rows: int | None = None) -> np.ndarray:
     base = gu.ctypes.data
     lib().orc_glu(GLU_OPS[op], ctypes.c_void_p(base), K2, ctypes.c_void_p(base + 4 * K), K2,
                   rows, K, _p(y), K)
+    return y
+
+
+def glu_ex(gate: np.ndarray, up: np.ndarray, op: str, alpha: float = OAI_ALPHA, limit: float = OAI_LIMIT,
+           rows: int | None = None) -> np.ndarray:
+    """orc_glu_ex over separate gate [R][K] and up [R][K] views (any row strides); y [rows][K]."""
+    gate = np.asarray(gate, dtype=np.float32)
+    up = np.asarray(up, dtype=np.float32)
+    assert gate.strides[1] == 4 and up.strides[1] == 4 and gate.shape == up.shape
+    R, K = gate.shape
+    rows = R if rows is None else rows
+    y = np.zeros((rows, K), dtype=np.float32)
+    lib().orc_glu_ex(GLU_OPS[op], ctypes.c_float(alpha), ctypes.c_float(limit),
+                     ctypes.c_void_p(gate.ctypes.data), gate.strides[0] // 4,
+                     ctypes.c_void_p(up.ctypes.data), up.strides[0] // 4, rows, K, _p(y), K)
+    return y
+
+
+def rmsnorm_ex(x: np.ndarray, gamma, beta, scale: float, eps: float, rows: int | None = None) -> np.ndarray:
+    """orc_rmsnorm_ex: RMS (x gamma) (+ beta) (x scale) over the first rows of x [R][K]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, K = x.shape
+    rows = R if rows is None else rows
+    y = np.zeros((rows, K), dtype=np.float32)
+    gm = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
+    bt = None if beta is None else np.ascontiguousarray(beta, dtype=np.float32)
+    lib().orc_rmsnorm_ex(_p(x), K, None if gm is None else _p(gm), None if bt is None else _p(bt),
+                         ctypes.c_float(scale), ctypes.c_float(eps), rows, K, _p(y), K)
     return y
 
 

@@ -199,3 +199,105 @@ def test_rms_sumsq_is_exact_for_integer_rows():
     # integers with exact squares summing below 2^24: every order gives the exact sum
     x = np.random.default_rng(8).integers(-60, 61, 8192).astype(np.float32)
     assert O.rms_sumsq(x) == np.float32(np.sum(x.astype(np.int64) ** 2))
+
+
+# ---- remaining GLU variants and RMS+ADD / RMS+SCALE ------------------------------------------
+def _glu_variant_f64(g, u, op, alpha=O.OAI_ALPHA, limit=O.OAI_LIMIT):
+    g = g.astype(np.float64)
+    u = u.astype(np.float64)
+    sig = lambda z: 1.0 / (1.0 + np.exp(-z))
+    if op == "reglu":
+        return np.maximum(g, 0.0) * u
+    if op == "geglu":
+        # 0.5 (1 + tanh z) = expit(2 z): scipy's logistic keeps the far negative tail, where
+        # 1 + tanh(z) cancels to zero in float64 (the tanh form itself is checked for |g| < 3)
+        z = math.sqrt(2.0 / math.pi) * (g + 0.044715 * g ** 3)
+        tanh_form = 0.5 * g * (1.0 + np.tanh(z)) * u
+        logistic = g * scipy.special.expit(2.0 * z) * u
+        near = np.abs(g) < 3
+        assert np.allclose(tanh_form[near], logistic[near], rtol=1e-10, atol=0)
+        return logistic
+    if op == "geglu_quick":
+        return g * sig(float(np.float32(1.702)) * g) * u
+    gg = np.minimum(g, limit)
+    uu = np.clip(u, -limit, limit)
+    if op == "swiglu_oai":
+        return gg * sig(float(np.float32(alpha)) * gg) * (uu + 1.0)
+    return gg * sig(gg) * uu
+
+
+@pytest.mark.parametrize("op", ["reglu", "geglu", "geglu_quick", "swiglu_oai", "swiglu_clamp"])
+def test_glu_variants_against_float64_textbook(op):
+    rng = np.random.default_rng(21)
+    K = 4096
+    gu = (rng.standard_normal((3, 2 * K)) * np.array([1.0, 3.0, 8.0])[:, None]).astype(np.float32)
+    g, u = gu[:, :K], gu[:, K:]
+    y = O.glu_ex(g, u, op).astype(np.float64)
+    ref = _glu_variant_f64(g, u, op)
+    gd = g.astype(np.float64)
+    if op == "reglu":
+        rel = U  # one rounding: the product
+    elif op == "geglu":
+        # g^3 and the inner sum (4 roundings), the f32 constant, exp_q (2 ulp) of an argument
+        # known to a few ulps of its size, then 1+e, g/den and *u
+        arg = np.abs(1.5957691216057308 * (gd + 0.044715 * gd ** 3))
+        rel = (12.0 + 6.0 * arg) * U
+    else:
+        gg = np.minimum(gd, O.OAI_LIMIT) if op.startswith("swiglu") else gd
+        c = 1.702 if op in ("geglu_quick", "swiglu_oai") else 1.0
+        rel = (12.0 + 3.0 * c * np.abs(gg)) * U
+    absf = 1e-36 * np.abs(gd * u.astype(np.float64)) + 1e-36
+    assert (np.abs(y - ref) <= rel * np.abs(ref) + absf).all()
+
+
+def test_glu_variant_closed_forms():
+    rng = np.random.default_rng(22)
+    K = 512
+    g = (rng.standard_normal((2, K)) * 5).astype(np.float32)
+    u = (rng.standard_normal((2, K)) * 5).astype(np.float32)
+    # ReGLU: gate <= 0 gives a zero, gate > 0 the rounded product
+    y = O.glu_ex(g, u, "reglu")
+    assert (y[g <= 0] == 0).all() and np.array_equal(y[g > 0], (g * u)[g > 0])
+    # the gate clamp: any gate at or above the limit acts as the limit itself
+    big = np.full_like(g, 100.0)
+    lim = np.full_like(g, np.float32(O.OAI_LIMIT))
+    for op in ("swiglu_oai", "swiglu_clamp"):
+        assert np.array_equal(O.glu_ex(big, u, op), O.glu_ex(lim, u, op))
+        # the up clamp: |u| beyond the limit acts as +-limit
+        assert np.array_equal(O.glu_ex(g, u * 1e6, op), O.glu_ex(g, np.sign(u) * lim, op))
+    # SwiGLU-OAI at u = -1 multiplies by (u + 1) = 0
+    assert (O.glu_ex(g, -np.ones_like(u), "swiglu_oai") == 0).all()
+    # limits that never bind reduce the clamped forms to plain SwiGLU (a different code path:
+    # the packed-row GLU with the up values as given, or shifted by the exact + 1)
+    gu = np.concatenate([g, u], axis=1)
+    assert np.array_equal(O.glu_ex(g, u, "swiglu_clamp", limit=3e38), O.glu(gu, "swiglu"))
+    gu1 = np.concatenate([g, (u + np.float32(1.0)).astype(np.float32)], axis=1)
+    assert np.array_equal(O.glu_ex(g, u, "swiglu_oai", alpha=1.0, limit=3e38), O.glu(gu1, "swiglu"))
+    # the two original ops through the general entry
+    for op in ("swiglu", "geglu_erf"):
+        assert np.array_equal(O.glu_ex(g, u, op), O.glu(gu, op))
+    # packed-swapped input (up half first) with independent strides
+    ug = np.concatenate([u, g], axis=1)
+    assert np.array_equal(O.glu_ex(ug[:, K:], ug[:, :K], "geglu"), O.glu_ex(g, u, "geglu"))
+
+
+def test_rmsnorm_add_and_scale():
+    rng = np.random.default_rng(23)
+    K = 2048
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    gamma = rng.normal(1.0, 0.1, K).astype(np.float32)
+    beta = rng.normal(0.0, 0.5, K).astype(np.float32)
+    base = O.rmsnorm(x, gamma, 1e-6)
+    # beta = -0 and scale = 1 leave every value (signed zeros included) unchanged
+    assert np.array_equal(O.rmsnorm_ex(x, gamma, np.full(K, -0.0, np.float32), 1.0, 1e-6).view(np.uint32),
+                          base.view(np.uint32))
+    assert np.array_equal(O.rmsnorm_ex(x, None, None, 1.0, 1e-6), O.rmsnorm(x, None, 1e-6))
+    # a power-of-two scale is exact
+    assert np.array_equal(O.rmsnorm_ex(x, None, None, 0.25, 1e-6), O.rmsnorm(x, None, 1e-6) * np.float32(0.25))
+    # against float64: (x r gamma + beta) * c
+    c = 0.7
+    y = O.rmsnorm_ex(x, gamma, beta, c, 1e-6).astype(np.float64)
+    t = _rms_f64(x, gamma, 1e-6)
+    ref = (t + beta.astype(np.float64)) * float(np.float32(c))
+    bound = 26 * U * (np.abs(t) + np.abs(beta)) * abs(c)
+    assert (np.abs(y - ref) <= bound + 1e-38).all()
