@@ -72,7 +72,7 @@ class Instance:
             qimg.emit_rmsnorm(self.x, self.gamma, 1e-6, self.y, img, live)
         else:
             K = wl.K
-            qimg.emit_glu(wl.producer, self.gu[:, :K], self.gu[:, K:], self.y, img, live)
+            qimg.emit_glu_ex(wl.producer, self.gu[:, :K], self.gu[:, K:], self.y, img, live)
 
     def quantize(self):
         from q8_activation_quant_amd import qimg
@@ -285,7 +285,7 @@ def cpu_baseline(wl, budget_s=20.0):
         if wl.producer == "rmsnorm":
             y = O.rmsnorm(wl.x[:L], wl.gamma, 1e-6)
         else:
-            y = O.glu(wl.gu[:L], wl.producer)
+            y = O.glu_ex(wl.gu[:L, :K], wl.gu[:L, K:], wl.producer)
         img = O.quantize(y, img_rows=T)
         for r in wl.readers:
             if wl.routed:
@@ -362,7 +362,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=460)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--live", type=int, default=None)
-    ap.add_argument("--glu", default="swiglu", choices=["swiglu", "geglu_erf"])
+    ap.add_argument("--glu", default="swiglu", choices=["swiglu", "geglu_erf", "reglu", "geglu", "geglu_quick",
+                                                        "swiglu_oai", "swiglu_clamp"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print one extra line per workload")
     ap.add_argument("--moe", action="store_true",
@@ -441,7 +442,9 @@ def main():
         "vs_baseline": None,
         "dtype": "int8xu4->int32 dots, f32 producer and accumulation",
         "data": "synthetic (seeded numpy PCG64; shapes/distributions of the workload)",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "T": wl.T, "K": wl.K,
+        "config": {"workload": WORKLOAD_NAMES[args.config] + ("" if wl.producer in ("rmsnorm", "swiglu")
+                                                              else " (producer %s)" % wl.producer),
+                   "T": wl.T, "K": wl.K,
                    "readers_N": wl.reader_rows, "producer": wl.producer, "arm": "fused",
                    "graph_instances": r["R"], "live_rows": wl.live},
         "achieved_GBs": round(nb["total"] / (us * 1e-6) / 1e9, 1),

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 5
+#define QIMG_ABI_VERSION 6
 
 /* status codes */
 #define QIMG_OK 0
@@ -81,9 +81,16 @@ extern "C" {
 #define QIMG_MAX_EXPERTS 1024       /* routed readers: E */
 #define QIMG_MAX_ROUTED_PAIRS 4096  /* routed readers: bucket * top_k */
 
-/* GLU producer formulas ([P1] Coverage: F32 SwiGLU and GeGLU-erf producers) */
-#define QIMG_GLU_SWIGLU 0    /* y = g / (1 + exp(-g)) * u                      */
-#define QIMG_GLU_GEGLU_ERF 1 /* y = 0.5 * g * (1 + erf(g / sqrt(2))) * u       */
+/* GLU producer formulas ([P1] Coverage: F32 ReGLU, GeGLU, SwiGLU, GeGLU-erf, GeGLU-quick,
+ * SwiGLU-OAI and SwiGLU-clamp producers). g = gate, u = up; the last two take alpha and limit
+ * (qimg_emit_glu_ex) and clamp g' = min(g, limit), u' = clamp(u, -limit, limit). */
+#define QIMG_GLU_SWIGLU 0       /* y = g / (1 + exp(-g)) * u                                  */
+#define QIMG_GLU_GEGLU_ERF 1    /* y = 0.5 * g * (1 + erf(g / sqrt(2))) * u                   */
+#define QIMG_GLU_REGLU 2        /* y = max(g, 0) * u                                          */
+#define QIMG_GLU_GEGLU 3        /* y = 0.5 * g * (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u */
+#define QIMG_GLU_GEGLU_QUICK 4  /* y = g / (1 + exp(-1.702 g)) * u                            */
+#define QIMG_GLU_SWIGLU_OAI 5   /* y = g' / (1 + exp(-alpha g')) * (u' + 1)                   */
+#define QIMG_GLU_SWIGLU_CLAMP 6 /* y = g' / (1 + exp(-g')) * u'                               */
 
 /* Routed workspace error-word bits (set on the device, read by the caller after sync). */
 #define QIMG_ERR_EXPERT_RANGE 1 /* a live pair named an expert outside [0, E); it was skipped */
@@ -122,6 +129,19 @@ int qimg_emit_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps
                       void* stream);
 
 /*
+ * RMS+MUL+ADD and RMS+SCALE producers ([P1] Coverage: RMS+MUL+ADD and RMS+SCALE producers
+ * emit images): as qimg_emit_rmsnorm with
+ *   t = x * r; t = t * gamma[k] (gamma != NULL); t = t + beta[k] (beta != NULL);
+ *   y[i][k] = t * scale
+ * each one f32 rounding in that order (scale = 1 and beta = NULL give qimg_emit_rmsnorm).
+ *   beta  : f32 [K], 16-byte aligned, or NULL; must not overlap y or img
+ *   scale : finite (QIMG_EINVAL otherwise)
+ */
+int qimg_emit_rmsnorm_ex(const float* x, int64_t ldx, const float* gamma, const float* beta,
+                         float scale, float eps, int32_t rows, const int32_t* live_rows,
+                         int32_t K, float* y, int64_t ldy, void* img, void* stream);
+
+/*
  * GLU producer ([P1] Coverage: F32 SwiGLU and GeGLU-erf producers with separate or packed
  * inputs emit images; original F32 outputs remain). For live rows i and k < K:
  *   g = gate[i*ldg + k], u = up[i*ldu + k], y[i][k] = act(g) * u
@@ -132,6 +152,16 @@ int qimg_emit_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps
 int qimg_emit_glu(int32_t op, const float* gate, int64_t ldg, const float* up, int64_t ldu,
                   int32_t rows, const int32_t* live_rows, int32_t K, float* y, int64_t ldy,
                   void* img, void* stream);
+
+/*
+ * Every GLU producer (QIMG_GLU_* 0..6) with its parameters: as qimg_emit_glu, y = the op's
+ * formula of (gate, up). alpha and limit are used by QIMG_GLU_SWIGLU_OAI and
+ * QIMG_GLU_SWIGLU_CLAMP only (alpha finite, limit >= 0, else QIMG_EINVAL); qimg_emit_glu
+ * rejects those two ops. Packed-swapped input (up half first): gate = gu + K, up = gu.
+ */
+int qimg_emit_glu_ex(int32_t op, float alpha, float limit, const float* gate, int64_t ldg,
+                     const float* up, int64_t ldu, int32_t rows, const int32_t* live_rows,
+                     int32_t K, float* y, int64_t ldy, void* img, void* stream);
 
 /*
  * The separate activation quantizer: the launch the fused producers remove ([P1] Overview),

@@ -180,10 +180,11 @@ float orc_glu_act(int op, float g) {
     float e = orc_exp_q(-((float)(2.0 * sqrt(2.0 / M_PI)) * inner));
     float den = 1.0f + e;
     return g / den;
-  } else {
+  } else if (op == 4) {
     /* GeGLU-quick: g sigmoid(1.702 g) */
     return g_sigmoid(g, 1.702f);
   }
+  return NAN; /* ops 5 and 6 need their up value and parameters: orc_glu_pair */
 }
 
 /* The GLU family with the gate/up clamps of the OpenAI-style SwiGLU:
@@ -197,6 +198,11 @@ float orc_glu_pair(int op, float alpha, float limit, float g, float u) {
   float uu = u < -limit ? -limit : (u > limit ? limit : u);
   if (op == 5) return g_sigmoid(gg, alpha) * (uu + 1.0f);
   return orc_glu_act(0, gg) * uu;
+}
+
+void orc_glu_pair_array(int op, float alpha, float limit, const float* g, float u, float* out,
+                        int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_glu_pair(op, alpha, limit, g[i], u);
 }
 
 void orc_glu_act_array(int op, const float* g, float* out, int64_t n) {

@@ -51,6 +51,7 @@ def lib():
             "orc_glu_act": (f32, [i32, f32]),
             "orc_glu_act_array": (None, [i32, P, P, i64]),
             "orc_glu_ex": (None, [i32, f32, f32, P, i64, P, i64, i32, i32, P, i64]),
+            "orc_glu_pair_array": (None, [i32, f32, f32, P, f32, P, i64]),
             "orc_rmsnorm_ex": (None, [P, i64, P, P, f32, f32, i32, i32, P, i64]),
             "orc_rms_scale_array": (None, [P, P, i64]),
             "orc_mmvq_id_per_slot": (None, [P, P, i32, i32, i32, P, i32, P, i32, i32, P]),
@@ -186,7 +187,9 @@ OAI_ALPHA, OAI_LIMIT = 1.702, 7.0  # the OpenAI-style SwiGLU defaults
 
 
 def glu(gu: np.ndarray, op: str, rows: int | None = None) -> np.ndarray:
-    """orc_glu over packed gate|up rows gu [R][2K] (gate half first); returns y [rows][K]."""
+    """orc_glu over packed gate|up rows gu [R][2K] (gate half first); returns y [rows][K].
+    Ops without parameters only (the clamped SwiGLU forms go through glu_ex)."""
+    assert GLU_OPS[op] < 5, "use glu_ex for the ops with alpha/limit"
     gu = np.ascontiguousarray(gu, dtype=np.float32)
     R, K2 = gu.shape
     K = K2 // 2
@@ -196,6 +199,16 @@ def glu(gu: np.ndarray, op: str, rows: int | None = None) -> np.ndarray:
     lib().orc_glu(GLU_OPS[op], ctypes.c_void_p(base), K2, ctypes.c_void_p(base + 4 * K), K2,
                   rows, K, _p(y), K)
     return y
+
+
+def glu_pair(g, op: str, u: float, alpha: float = OAI_ALPHA, limit: float = OAI_LIMIT,
+             out: np.ndarray | None = None) -> np.ndarray:
+    """orc_glu_pair element-wise over gates g with one up value u."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    out = _out_like(g, out)
+    lib().orc_glu_pair_array(GLU_OPS[op], ctypes.c_float(alpha), ctypes.c_float(limit), _p(g),
+                             ctypes.c_float(u), _p(out), g.size)
+    return out
 
 
 def glu_ex(gate: np.ndarray, up: np.ndarray, op: str, alpha: float = OAI_ALPHA, limit: float = OAI_LIMIT,

@@ -152,35 +152,6 @@ __device__ __forceinline__ float geglu_erf_act(float g) {
   return (0.5f * g) * ope;
 }
 
-// Element-wise evaluation of the activation math above over a range of f32 bit patterns:
-// out[i] = f(x) with x the float whose bits are first + i (mod 2^32). It runs the same inlined
-// device functions the producers run, so every f32 input can be compared with a host
-// evaluation of the same operation sequence.
-// Two more functions cover the correctly rounded divisions and square root the producers rely
-// on: 1/sqrt(x) (the RMS scale) and 1/(x/127) (the quantizer's scale and its reciprocal).
-// The quantizer's block scale d = x/127 on its own and the f32 -> fp16 conversion of its
-// stored halves (result bits in the low 16 bits of the output word) are the last two.
-enum : int { MATH_EXP = 0, MATH_ERFC = 1, MATH_SWIGLU = 2, MATH_GEGLU = 3, MATH_RSQRT = 4,
-             MATH_QSCALE = 5, MATH_QDIV = 6, MATH_F2H = 7 };
-
-template <int FN>
-__global__ __launch_bounds__(256) void eval_math_kernel(uint32_t first, int64_t n, float* out) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
-    const float x = __builtin_bit_cast(float, first + (uint32_t)i);
-    float v;
-    if constexpr (FN == MATH_EXP) v = exp_q(x);
-    else if constexpr (FN == MATH_ERFC) v = erfc_q(x);
-    else if constexpr (FN == MATH_SWIGLU) v = swiglu_act(x);
-    else if constexpr (FN == MATH_GEGLU) v = geglu_erf_act(x);
-    else if constexpr (FN == MATH_RSQRT) v = 1.0f / __builtin_sqrtf(x);
-    else if constexpr (FN == MATH_QSCALE) v = 1.0f / (x / 127.0f);
-    else if constexpr (FN == MATH_QDIV) v = x / 127.0f;
-    else v = __builtin_bit_cast(float, f2h(x));
-    out[i] = v;
-  }
-}
-
 // MoE combine ("qwen3_5 CUDA: a captured bucket's padding rows no longer go through the
 // routed experts", What this changes: only live rows are combined, padding output rows stay
 // unwritten). out[t][n] = sum over slots s (ascending) whose expert id is in [0, E) of
@@ -225,6 +196,34 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs c) {
   *reinterpret_cast<float4*>(c.out + (int64_t)t * c.ldo + 4 * n4) = acc;
 }
 
+// The other GLU variants ([P1] Coverage: F32 ReGLU, GeGLU, GeGLU-quick, SwiGLU-OAI and
+// SwiGLU-clamp producers keep their formulas and alpha/limit parameters).
+//   ReGLU        act(g) = max(g, 0)  (g > 0 ? g : 0)
+//   GeGLU        act(g) = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), evaluated through
+//                0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)) as g / (1 + exp_q(-c2 (g + 0.044715 g^3))),
+//                c2 = 2 sqrt(2/pi) (no cancellation for either sign of g)
+//   GeGLU-quick  act(g) = g sigmoid(1.702 g)
+//   SwiGLU-OAI   g' = min(g, limit), u' = clamp(u, -limit, limit), y = g' sigmoid(alpha g') (u' + 1)
+//   SwiGLU-clamp g' = min(g, limit), u' = clamp(u, -limit, limit), y = silu(g') u'
+__device__ __forceinline__ float g_sigmoid(float g, float c) {
+  const float e = exp_q(-(c * g));
+  const float den = 1.0f + e;
+  return g / den;
+}
+__device__ __forceinline__ float reglu_act(float g) { return g > 0.0f ? g : 0.0f; }
+__device__ __forceinline__ float geglu_tanh_act(float g) {
+  constexpr float kC2 = 0x1.988454p+0f;      // 2 sqrt(2/pi) rounded to f32
+  constexpr float kCubic = 0x1.6e4e26p-5f;   // 0.044715 rounded to f32
+  const float g3 = (g * g) * g;
+  const float inner = g + kCubic * g3;
+  const float e = exp_q(-(kC2 * inner));
+  const float den = 1.0f + e;
+  return g / den;
+}
+__device__ __forceinline__ float geglu_quick_act(float g) {
+  return g_sigmoid(g, 0x1.b3b646p+0f);  // 1.702 rounded to f32
+}
+
 // ---------------------------------------------------------------------------------------------
 // Producer: one workgroup per live row.
 // Element mapping: leaf c covers elements 4c..4c+3; lane l of wave w holds leaves
@@ -235,7 +234,63 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(CombineArgs c) {
 // to a power of two Jp with zeros), whose top levels are taken across waves through LDS; then
 // a balanced pairwise tree over the 64 lanes (xor butterfly, masks 1..32).
 // ---------------------------------------------------------------------------------------------
-enum : int { OP_RMS = 0, OP_SWIGLU = 1, OP_GEGLU = 2, OP_QUANT = 3 };
+enum : int {
+  OP_RMS = 0, OP_SWIGLU = 1, OP_GEGLU = 2, OP_QUANT = 3,
+  OP_REGLU = 4, OP_GEGLU_TANH = 5, OP_GEGLU_QUICK = 6, OP_SWIGLU_OAI = 7, OP_SWIGLU_CLAMP = 8
+};
+constexpr bool is_glu(int op) { return op != OP_RMS && op != OP_QUANT; }
+
+// y for one element of a GLU producer: act(g) * u, or the clamped forms
+template <int OP>
+__device__ __forceinline__ float glu_pair(float g, float u, float alpha, float limit) {
+  if constexpr (OP == OP_SWIGLU) return swiglu_act(g) * u;
+  else if constexpr (OP == OP_GEGLU) return geglu_erf_act(g) * u;
+  else if constexpr (OP == OP_REGLU) return reglu_act(g) * u;
+  else if constexpr (OP == OP_GEGLU_TANH) return geglu_tanh_act(g) * u;
+  else if constexpr (OP == OP_GEGLU_QUICK) return geglu_quick_act(g) * u;
+  else {
+    const float gg = g < limit ? g : limit;
+    const float uu = u < -limit ? -limit : (u > limit ? limit : u);
+    if constexpr (OP == OP_SWIGLU_OAI) return g_sigmoid(gg, alpha) * (uu + 1.0f);
+    else return swiglu_act(gg) * uu;
+  }
+}
+
+// Element-wise evaluation of the activation math above over a range of f32 bit patterns:
+// out[i] = f(x) with x the float whose bits are first + i (mod 2^32). It runs the same inlined
+// device functions the producers run, so every f32 input can be compared with a host
+// evaluation of the same operation sequence.
+// Two more functions cover the correctly rounded divisions and square root the producers rely
+// on: 1/sqrt(x) (the RMS scale) and 1/(x/127) (the quantizer's scale and its reciprocal).
+// The quantizer's block scale d = x/127 on its own and the f32 -> fp16 conversion of its
+// stored halves (result bits in the low 16 bits of the output word) are the last two.
+// Then the other GLU activations: ReGLU, GeGLU (tanh form), GeGLU-quick and the gate factor
+// of SwiGLU-OAI at alpha 1.702, limit 7 (its output times (0 + 1)).
+enum : int { MATH_EXP = 0, MATH_ERFC = 1, MATH_SWIGLU = 2, MATH_GEGLU = 3, MATH_RSQRT = 4,
+             MATH_QSCALE = 5, MATH_QDIV = 6, MATH_F2H = 7, MATH_REGLU = 8, MATH_GEGLU_TANH = 9,
+             MATH_GEGLU_QUICK = 10, MATH_OAI_GATE = 11 };
+
+template <int FN>
+__global__ __launch_bounds__(256) void eval_math_kernel(uint32_t first, int64_t n, float* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const float x = __builtin_bit_cast(float, first + (uint32_t)i);
+    float v;
+    if constexpr (FN == MATH_EXP) v = exp_q(x);
+    else if constexpr (FN == MATH_ERFC) v = erfc_q(x);
+    else if constexpr (FN == MATH_SWIGLU) v = swiglu_act(x);
+    else if constexpr (FN == MATH_GEGLU) v = geglu_erf_act(x);
+    else if constexpr (FN == MATH_RSQRT) v = 1.0f / __builtin_sqrtf(x);
+    else if constexpr (FN == MATH_QSCALE) v = 1.0f / (x / 127.0f);
+    else if constexpr (FN == MATH_QDIV) v = x / 127.0f;
+    else if constexpr (FN == MATH_F2H) v = __builtin_bit_cast(float, f2h(x));
+    else if constexpr (FN == MATH_REGLU) v = reglu_act(x);
+    else if constexpr (FN == MATH_GEGLU_TANH) v = geglu_tanh_act(x);
+    else if constexpr (FN == MATH_GEGLU_QUICK) v = geglu_quick_act(x);
+    else v = glu_pair<OP_SWIGLU_OAI>(x, 0.0f, 1.702f, 7.0f);
+    out[i] = v;
+  }
+}
 
 struct EmitArgs {
   const float* a;      // rms: x; glu: gate; quant: y
@@ -250,6 +305,9 @@ struct EmitArgs {
   int32_t rows, K, Kb, RB;
   int32_t live_mul;    // rows per live count unit: 1, or top_k for per-slot (pair) rows
   float eps;
+  const float* beta;   // rms: added after gamma (may be null)
+  float scale;         // rms: final factor (1 keeps the value)
+  float alpha, limit;  // SwiGLU-OAI / SwiGLU-clamp parameters
 };
 
 template <int JW>
@@ -308,8 +366,8 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
 
   // all input loads of the row go out at once (in bounds: leaves past K re-read leaf 0 and
   // are zeroed): x (or gate, or y) and gamma (or up)
-  float4 v[JW], u[JW];
-  const float* brow = (OP == OP_SWIGLU || OP == OP_GEGLU) ? p.b + (int64_t)row * p.ldb : p.b;
+  float4 v[JW], u[JW], bt[JW];
+  const float* brow = is_glu(OP) ? p.b + (int64_t)row * p.ldb : p.b;
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj) {
     const int c = c_off + lane + 64 * (w * JW + jj);
@@ -317,6 +375,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
     v[jj] = *reinterpret_cast<const float4*>(arow + 4 * cc);
     if (c >= C) v[jj] = make_float4(0, 0, 0, 0);
     if (OP != OP_QUANT && brow) u[jj] = *reinterpret_cast<const float4*>(brow + 4 * cc);
+    if (OP == OP_RMS && p.beta) bt[jj] = *reinterpret_cast<const float4*>(p.beta + 4 * cc);
   }
 
   if constexpr (OP == OP_RMS) {
@@ -348,22 +407,25 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
         const float4 g = u[jj];
         y.x = y.x * g.x; y.y = y.y * g.y; y.z = y.z * g.z; y.w = y.w * g.w;
       }
+      if (p.beta && c < C) {  // RMS+MUL+ADD
+        const float4 b = bt[jj];
+        y.x = y.x + b.x; y.y = y.y + b.y; y.z = y.z + b.z; y.w = y.w + b.w;
+      }
+      // RMS+SCALE (a scale of 1 leaves every value unchanged)
+      y.x = y.x * p.scale; y.y = y.y * p.scale; y.z = y.z * p.scale; y.w = y.w * p.scale;
       v[jj] = y;
     }
-  } else if constexpr (OP == OP_SWIGLU || OP == OP_GEGLU) {
+  } else if constexpr (is_glu(OP)) {
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
       const int c = c_off + lane + 64 * (w * JW + jj);
       if (c < C) {
         const float4 uu = u[jj];
         float4 y;
-        if constexpr (OP == OP_SWIGLU) {
-          y.x = swiglu_act(v[jj].x) * uu.x; y.y = swiglu_act(v[jj].y) * uu.y;
-          y.z = swiglu_act(v[jj].z) * uu.z; y.w = swiglu_act(v[jj].w) * uu.w;
-        } else {
-          y.x = geglu_erf_act(v[jj].x) * uu.x; y.y = geglu_erf_act(v[jj].y) * uu.y;
-          y.z = geglu_erf_act(v[jj].z) * uu.z; y.w = geglu_erf_act(v[jj].w) * uu.w;
-        }
+        y.x = glu_pair<OP>(v[jj].x, uu.x, p.alpha, p.limit);
+        y.y = glu_pair<OP>(v[jj].y, uu.y, p.alpha, p.limit);
+        y.z = glu_pair<OP>(v[jj].z, uu.z, p.alpha, p.limit);
+        y.w = glu_pair<OP>(v[jj].w, uu.w, p.alpha, p.limit);
         v[jj] = y;
       }
     }
@@ -1337,12 +1399,16 @@ int launch_emit(int op, EmitArgs& a, hipStream_t s) {
   dim3 grid(a.rows, S), block(W * 64);
 #define QIMG_EMIT_CASE(OPV, JWV) \
   if (op == OPV && JW == JWV) { hipLaunchKernelGGL((emit_kernel<OPV, JWV>), grid, block, 0, s, a); return launch_status(); }
-#define QIMG_EMIT_OP(OPV) QIMG_EMIT_CASE(OPV, 1) QIMG_EMIT_CASE(OPV, 2) QIMG_EMIT_CASE(OPV, 4) QIMG_EMIT_CASE(OPV, 8)
-  QIMG_EMIT_OP(OP_RMS)
-  QIMG_EMIT_OP(OP_SWIGLU)
-  QIMG_EMIT_OP(OP_GEGLU)
-  QIMG_EMIT_OP(OP_QUANT)
-#undef QIMG_EMIT_OP
+  // RMS rows are whole rows (JW leaves per lane); the element-wise ops use slices with JW = 1
+  QIMG_EMIT_CASE(OP_RMS, 1) QIMG_EMIT_CASE(OP_RMS, 2) QIMG_EMIT_CASE(OP_RMS, 4) QIMG_EMIT_CASE(OP_RMS, 8)
+  QIMG_EMIT_CASE(OP_SWIGLU, 1)
+  QIMG_EMIT_CASE(OP_GEGLU, 1)
+  QIMG_EMIT_CASE(OP_QUANT, 1)
+  QIMG_EMIT_CASE(OP_REGLU, 1)
+  QIMG_EMIT_CASE(OP_GEGLU_TANH, 1)
+  QIMG_EMIT_CASE(OP_GEGLU_QUICK, 1)
+  QIMG_EMIT_CASE(OP_SWIGLU_OAI, 1)
+  QIMG_EMIT_CASE(OP_SWIGLU_CLAMP, 1)
 #undef QIMG_EMIT_CASE
   return QIMG_EUNSUPPORTED;
 }
@@ -1506,18 +1572,25 @@ int64_t qimg_image_bytes(int32_t rows, int32_t K) {
   return (int64_t)rows * row_blocks(K) * 36;
 }
 
+struct EmitExtra {  // producer parameters beyond the common ones
+  const float* beta = nullptr;
+  float scale = 1.0f, alpha = 0.0f, limit = 0.0f;
+};
+
 static int emit_common(int op, const float* a, int64_t lda, const float* b, int64_t ldb,
                        int b_rows, float eps, int32_t rows, const int32_t* live_rows, int32_t K,
-                       float* y, int64_t ldy, void* img, void* stream, int32_t live_mul = 1) {
+                       float* y, int64_t ldy, void* img, void* stream, int32_t live_mul = 1,
+                       EmitExtra ex = EmitExtra{}) {
   int st = check_k(K);
   if (st) return st;
   if (rows < 0) return QIMG_EINVAL;
   if (rows == 0) return QIMG_OK;
   if (!a || (op != OP_QUANT && !y) || (op == OP_QUANT && !img)) return QIMG_EINVAL;
-  if ((op == OP_SWIGLU || op == OP_GEGLU) && !b) return QIMG_EINVAL;
+  if (is_glu(op) && !b) return QIMG_EINVAL;
   if (lda < K || (op != OP_QUANT && ldy < K) || (b && b_rows > 1 && ldb < K)) return QIMG_EINVAL;
   if (!al16(a) || lda % 4 || (b && (!al16(b) || (b_rows > 1 && ldb % 4))) ||
-      (y && (!al16(y) || ldy % 4)) || (img && !al16(img)) || (live_rows && !al(live_rows, 4)))
+      (y && (!al16(y) || ldy % 4)) || (img && !al16(img)) || (live_rows && !al(live_rows, 4)) ||
+      (ex.beta && !al16(ex.beta)))
     return QIMG_EALIGN;
   const int64_t ib = qimg_image_bytes(rows, K);
   const Span sa = span(a, rows_extent(rows, lda, K, 4));
@@ -1525,8 +1598,10 @@ static int emit_common(int op, const float* a, int64_t lda, const float* b, int6
   const Span sy = y ? span(y, rows_extent(rows, ldy, K, 4)) : Span{0, 0};
   const Span si = img ? span(img, ib) : Span{0, 0};
   const Span sl = live_rows ? span(live_rows, 4) : Span{0, 0};
+  const Span sbeta = ex.beta ? span(ex.beta, (int64_t)K * 4) : Span{0, 0};
   for (Span out : {sy, si}) {
-    if (overlap(out, sa) || overlap(out, sb) || overlap(out, sl)) return QIMG_EALIAS;
+    if (overlap(out, sa) || overlap(out, sb) || overlap(out, sl) || overlap(out, sbeta))
+      return QIMG_EALIAS;
   }
   if (overlap(sy, si)) return QIMG_EALIAS;
 
@@ -1537,6 +1612,7 @@ static int emit_common(int op, const float* a, int64_t lda, const float* b, int6
   e.ds = img ? (uint32_t*)((uint8_t*)img + (size_t)rows * RB * 32) : nullptr;
   e.live_rows = live_rows; e.rows = rows; e.K = K; e.Kb = K / 32; e.RB = RB; e.eps = eps;
   e.live_mul = live_mul;
+  e.beta = ex.beta; e.scale = ex.scale; e.alpha = ex.alpha; e.limit = ex.limit;
   return launch_emit(op, e, (hipStream_t)stream);
 }
 
@@ -1546,11 +1622,50 @@ int qimg_emit_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps
   return emit_common(OP_RMS, x, ldx, gamma, 0, 1, eps, rows, live_rows, K, y, ldy, img, stream);
 }
 
+// kernel op of a public GLU op; params: whether the op takes alpha/limit. -1: unknown op.
+static int glu_kop(int32_t op, bool* params) {
+  *params = false;
+  switch (op) {
+    case QIMG_GLU_SWIGLU: return OP_SWIGLU;
+    case QIMG_GLU_GEGLU_ERF: return OP_GEGLU;
+    case QIMG_GLU_REGLU: return OP_REGLU;
+    case QIMG_GLU_GEGLU: return OP_GEGLU_TANH;
+    case QIMG_GLU_GEGLU_QUICK: return OP_GEGLU_QUICK;
+    case QIMG_GLU_SWIGLU_OAI: *params = true; return OP_SWIGLU_OAI;
+    case QIMG_GLU_SWIGLU_CLAMP: *params = true; return OP_SWIGLU_CLAMP;
+    default: return -1;
+  }
+}
+
+int qimg_emit_rmsnorm_ex(const float* x, int64_t ldx, const float* gamma, const float* beta,
+                         float scale, float eps, int32_t rows, const int32_t* live_rows,
+                         int32_t K, float* y, int64_t ldy, void* img, void* stream) {
+  if (!(scale == scale) || __builtin_isinf(scale)) return QIMG_EINVAL;
+  EmitExtra ex;
+  ex.beta = beta;
+  ex.scale = scale;
+  return emit_common(OP_RMS, x, ldx, gamma, 0, 1, eps, rows, live_rows, K, y, ldy, img, stream, 1, ex);
+}
+
+int qimg_emit_glu_ex(int32_t op, float alpha, float limit, const float* gate, int64_t ldg,
+                     const float* up, int64_t ldu, int32_t rows, const int32_t* live_rows,
+                     int32_t K, float* y, int64_t ldy, void* img, void* stream) {
+  bool params;
+  const int kop = glu_kop(op, &params);
+  if (kop < 0) return QIMG_EINVAL;
+  if (params && (!(alpha == alpha) || __builtin_isinf(alpha) || !(limit >= 0.0f))) return QIMG_EINVAL;
+  EmitExtra ex;
+  ex.alpha = alpha;
+  ex.limit = limit;
+  return emit_common(kop, gate, ldg, up, ldu, 2, 0.0f, rows, live_rows, K, y, ldy, img, stream, 1, ex);
+}
+
 int qimg_emit_glu(int32_t op, const float* gate, int64_t ldg, const float* up, int64_t ldu,
                   int32_t rows, const int32_t* live_rows, int32_t K, float* y, int64_t ldy,
                   void* img, void* stream) {
-  if (op != QIMG_GLU_SWIGLU && op != QIMG_GLU_GEGLU_ERF) return QIMG_EINVAL;
-  const int kop = op == QIMG_GLU_SWIGLU ? OP_SWIGLU : OP_GEGLU;
+  bool params;
+  const int kop = glu_kop(op, &params);
+  if (kop < 0 || params) return QIMG_EINVAL;
   // gate and up may be the two halves of one packed row (they must not overlap each other's
   // elements, which packed halves do not)
   return emit_common(kop, gate, ldg, up, ldu, 2, 0.0f, rows, live_rows, K, y, ldy, img, stream);
@@ -1559,10 +1674,11 @@ int qimg_emit_glu(int32_t op, const float* gate, int64_t ldg, const float* up, i
 int qimg_emit_glu_per_slot(int32_t op, const float* gate, int64_t ldg, const float* up,
                            int64_t ldu, int32_t bucket, int32_t top_k, const int32_t* live_rows,
                            int32_t K, float* y, int64_t ldy, void* img, void* stream) {
-  if (op != QIMG_GLU_SWIGLU && op != QIMG_GLU_GEGLU_ERF) return QIMG_EINVAL;
+  bool params;
+  const int kop = glu_kop(op, &params);
+  if (kop < 0 || params) return QIMG_EINVAL;
   if (bucket < 0 || top_k <= 0) return QIMG_EINVAL;
   if ((int64_t)bucket * top_k > QIMG_MAX_ROUTED_PAIRS) return QIMG_EUNSUPPORTED;
-  const int kop = op == QIMG_GLU_SWIGLU ? OP_SWIGLU : OP_GEGLU;
   return emit_common(kop, gate, ldg, up, ldu, 2, 0.0f, bucket * top_k, live_rows, K, y, ldy, img,
                      stream, top_k);
 }
@@ -1789,7 +1905,7 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
 }
 
 int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream) {
-  if (fn < MATH_EXP || fn > MATH_F2H || n < 0 || n > ((int64_t)1 << 32)) return QIMG_EINVAL;
+  if (fn < MATH_EXP || fn > MATH_OAI_GATE || n < 0 || n > ((int64_t)1 << 32)) return QIMG_EINVAL;
   if (n == 0) return QIMG_OK;
   if (!out) return QIMG_EINVAL;
   if (!al(out, 4)) return QIMG_EALIGN;
@@ -1804,7 +1920,11 @@ int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void*
     case MATH_RSQRT: eval_math_kernel<MATH_RSQRT><<<grid, 256, 0, s>>>(first_bits, n, out); break;
     case MATH_QSCALE: eval_math_kernel<MATH_QSCALE><<<grid, 256, 0, s>>>(first_bits, n, out); break;
     case MATH_QDIV: eval_math_kernel<MATH_QDIV><<<grid, 256, 0, s>>>(first_bits, n, out); break;
-    default: eval_math_kernel<MATH_F2H><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_F2H: eval_math_kernel<MATH_F2H><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_REGLU: eval_math_kernel<MATH_REGLU><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_GEGLU_TANH: eval_math_kernel<MATH_GEGLU_TANH><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    case MATH_GEGLU_QUICK: eval_math_kernel<MATH_GEGLU_QUICK><<<grid, 256, 0, s>>>(first_bits, n, out); break;
+    default: eval_math_kernel<MATH_OAI_GATE><<<grid, 256, 0, s>>>(first_bits, n, out); break;
   }
   return launch_status();
 }

@@ -14,11 +14,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqimg.so")
 
 OK, EINVAL, EALIGN, EALIAS, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
-GLU_SWIGLU, GLU_GEGLU_ERF = 0, 1
-GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF}
+GLU_SWIGLU, GLU_GEGLU_ERF, GLU_REGLU, GLU_GEGLU, GLU_GEGLU_QUICK, GLU_SWIGLU_OAI, GLU_SWIGLU_CLAMP = range(7)
+GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF, "reglu": GLU_REGLU, "geglu": GLU_GEGLU,
+           "geglu_quick": GLU_GEGLU_QUICK, "swiglu_oai": GLU_SWIGLU_OAI, "swiglu_clamp": GLU_SWIGLU_CLAMP}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
@@ -26,8 +27,10 @@ EXPORTS = (
     "mmvq_id_workspace_bytes", "mmvq_id_q4_0_q8_1", "mmvq_q4_0_q8_1_blockdots",
     "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile", "qimg_eval_math",
     "qimg_emit_glu_per_slot", "mmvq_id_q4_0_q8_1_per_slot", "qimg_moe_combine",
+    "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex",
 )
-MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7}
+MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7, "reglu": 8,
+            "geglu": 9, "geglu_quick": 10, "swiglu_oai_gate": 11}
 
 
 class QimgError(RuntimeError):
@@ -77,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "mmvq_id_q4_0_q8_1_per_slot": (ctypes.c_int, [ctypes.POINTER(ExpertReader), i32, i32, P, P,
                                                           i32, i32, P, i32, P, ctypes.c_size_t, P]),
             "qimg_moe_combine": (ctypes.c_int, [P, i64, P, P, i32, i32, i32, P, i32, P, i64, P]),
+            "qimg_emit_rmsnorm_ex": (ctypes.c_int, [P, i64, P, P, f32, f32, i32, P, i32, P, i64, P, P]),
+            "qimg_emit_glu_ex": (ctypes.c_int, [i32, f32, f32, P, i64, P, i64, i32, P, i32, P, i64, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -141,6 +146,23 @@ def emit_glu(op, gate, up, y, img=None, live_rows=None, stream=None):
     rows, K = gate.shape
     _check(lib().qimg_emit_glu(op, _ptr(gate), _ld(gate), _ptr(up), _ld(up), rows, _ptr(live_rows),
                                K, _ptr(y), _ld(y), _ptr(img), _stream(stream)), "qimg_emit_glu")
+
+
+def emit_rmsnorm_ex(x, gamma, beta, scale, eps, y, img=None, live_rows=None, stream=None):
+    """y = ((rmsnorm(x) * gamma) + beta) * scale (gamma, beta may be None)."""
+    rows, K = x.shape
+    _check(lib().qimg_emit_rmsnorm_ex(_ptr(x), _ld(x), _ptr(gamma), _ptr(beta), ctypes.c_float(scale),
+                                      ctypes.c_float(eps), rows, _ptr(live_rows), K, _ptr(y), _ld(y),
+                                      _ptr(img), _stream(stream)), "qimg_emit_rmsnorm_ex")
+
+
+def emit_glu_ex(op, gate, up, y, img=None, live_rows=None, alpha=1.702, limit=7.0, stream=None):
+    """Any GLU variant; gate and up are [rows, K] views with their own row strides."""
+    op = GLU_OPS[op] if isinstance(op, str) else op
+    rows, K = gate.shape
+    _check(lib().qimg_emit_glu_ex(op, ctypes.c_float(alpha), ctypes.c_float(limit), _ptr(gate), _ld(gate),
+                                  _ptr(up), _ld(up), rows, _ptr(live_rows), K, _ptr(y), _ld(y), _ptr(img),
+                                  _stream(stream)), "qimg_emit_glu_ex")
 
 
 def quantize_q8_1(y, img, live_rows=None, stream=None):

@@ -57,7 +57,7 @@ def oracle_producer(wl: W.Workload, live=None):
     if wl.producer == "rmsnorm":
         y = O.rmsnorm(wl.x[:live], wl.gamma, W.EPS)
     else:
-        y = O.glu(wl.gu[:live], wl.producer)
+        y = O.glu_ex(wl.gu[:live, :wl.K], wl.gu[:live, wl.K:], wl.producer)
     img = O.quantize(y, img_rows=wl.T)
     return y, img
 

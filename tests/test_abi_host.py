@@ -127,8 +127,11 @@ def test_emit_glu_validation(L):
     def glu(op=0, g=A, ldg=512, u=A + 1024, ldu=512, rows=4, K=256, y=C, ldy=256, img=D):
         return L.qimg_emit_glu(op, g, ldg, u, ldu, rows, None, K, y, ldy, img, S)
 
-    assert glu(op=2) == qimg.EINVAL
+    assert glu(op=7) == qimg.EINVAL
     assert glu(op=-1) == qimg.EINVAL
+    # the clamped forms need alpha and limit: only through qimg_emit_glu_ex
+    assert glu(op=qimg.GLU_SWIGLU_OAI) == qimg.EINVAL
+    assert glu(op=qimg.GLU_SWIGLU_CLAMP) == qimg.EINVAL
     assert glu(u=None) == qimg.EINVAL
     assert glu(ldu=128) == qimg.EINVAL
     assert glu(u=A + 1028) == qimg.EALIGN
@@ -270,7 +273,8 @@ def test_emit_glu_per_slot_validation(L):
     def glu(op=0, g=A, ldg=512, u=A + 1024, ldu=512, bucket=4, k=2, K=256, y=C, ldy=256, img=D):
         return L.qimg_emit_glu_per_slot(op, g, ldg, u, ldu, bucket, k, None, K, y, ldy, img, S)
 
-    assert glu(op=2) == qimg.EINVAL
+    assert glu(op=7) == qimg.EINVAL
+    assert glu(op=qimg.GLU_SWIGLU_OAI) == qimg.EINVAL
     assert glu(k=0) == qimg.EINVAL
     assert glu(bucket=-1) == qimg.EINVAL
     assert glu(bucket=0) == qimg.OK
@@ -307,3 +311,36 @@ def test_moe_combine_validation(L):
     assert comb(out=B) == qimg.EALIAS
     assert comb(out=B + 4096) == qimg.EALIAS
     assert comb(live=C + 64) == qimg.EALIAS
+
+
+def test_emit_glu_ex_validation(L):
+    inf, nan = float("inf"), float("nan")
+
+    def glu(op=5, alpha=1.702, limit=7.0, g=A, ldg=512, u=A + 1024, ldu=512, rows=4, K=256, y=C,
+            ldy=256, img=D):
+        return L.qimg_emit_glu_ex(op, ctypes.c_float(alpha), ctypes.c_float(limit), g, ldg, u, ldu, rows,
+                                  None, K, y, ldy, img, S)
+
+    assert glu(op=7) == qimg.EINVAL
+    assert glu(alpha=nan) == qimg.EINVAL
+    assert glu(alpha=inf) == qimg.EINVAL
+    assert glu(limit=-1.0) == qimg.EINVAL
+    assert glu(limit=nan) == qimg.EINVAL
+    assert glu(op=6, limit=-0.5) == qimg.EINVAL
+    assert glu(rows=0) == qimg.OK
+    assert glu(u=None) == qimg.EINVAL
+    assert glu(g=A + 4) == qimg.EALIGN
+    assert glu(y=A + 1024) == qimg.EALIAS
+
+
+def test_emit_rmsnorm_ex_validation(L):
+    def rms(beta=B + 4096, scale=1.0, x=A, gamma=B, y=C, img=D):
+        return L.qimg_emit_rmsnorm_ex(x, 256, gamma, beta, ctypes.c_float(scale), ctypes.c_float(1e-6), 4,
+                                      None, 256, y, 256, img, S)
+
+    assert rms(scale=float("nan")) == qimg.EINVAL
+    assert rms(scale=float("inf")) == qimg.EINVAL
+    assert rms(beta=B + 4100) == qimg.EALIGN
+    assert rms(y=B + 4096) == qimg.EALIAS
+    assert rms(img=B + 4096 - 64) == qimg.EALIAS
+    assert rms(x=None) == qimg.EINVAL

@@ -30,6 +30,10 @@ ORACLE = {
     "qscale": lambda x, out: O.quant_recip(x, out),
     "qdiv": lambda x, out: O.quant_scale(x, out),
     "f2h": lambda x, out: O.f32_to_f16_words(x, out),
+    "reglu": lambda x, out: O.glu_act(x, "reglu", out),
+    "geglu": lambda x, out: O.glu_act(x, "geglu", out),
+    "geglu_quick": lambda x, out: O.glu_act(x, "geglu_quick", out),
+    "swiglu_oai_gate": lambda x, out: O.glu_pair(x, "swiglu_oai", 0.0, out=out),
 }
 
 
@@ -107,7 +111,7 @@ def test_eval_math_rejects_bad_arguments():
     torch = H.torch()
     out = torch.empty(16, dtype=torch.float32, device="cuda")
     with pytest.raises(qimg.QimgError):
-        qimg.eval_math(8, 0, out)
+        qimg.eval_math(12, 0, out)
     st = qimg.lib().qimg_eval_math(0, 0, (1 << 32) + 1, qimg._ptr(out), None)
     assert st == qimg.EINVAL
     assert qimg.lib().qimg_eval_math(0, 0, 0, None, None) == qimg.OK
