@@ -501,6 +501,73 @@ void orc_mmvq_id_per_slot(const uint8_t* qs, const uint16_t* d, int E, int N, in
 }
 
 /* ------------------------------------------------------------------------------------------
+ * Device router and top-k with live-row guards ("qwen3_5 CUDA: a captured bucket's padding rows
+ * no longer go through the routed experts", What this changes: the router and the top-k read
+ * the live count and skip the padding rows, which get no picks; Receipt: router, top-k, plan,
+ * experts, combine as one routed chain).
+ *
+ * Router: logits[t][e] = sum_k x[t][k] * W[e][k] for live rows t, in a fixed order (the pages
+ * give none): leaf c (c < K/4) = fma(x3,w3, fma(x2,w2, fma(x1,w1, x0*w0))) over elements
+ * 4c..4c+3; lane l in [0,64) owns leaves c = l + 64 j and adds them in ascending j from +0;
+ * the 64 lane sums are combined by a balanced pairwise tree over l.
+ * ---------------------------------------------------------------------------------------- */
+float orc_router_dot(const float* x, const float* w, int K) {
+  int C = K / 4;
+  float lane_sum[64];
+  for (int l = 0; l < 64; ++l) {
+    float acc = 0.0f;
+    for (int c = l; c < C; c += 64) {
+      const float* a = x + 4 * c;
+      const float* b = w + 4 * c;
+      acc = acc + fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], a[0] * b[0])));
+    }
+    lane_sum[l] = acc;
+  }
+  return pairwise_tree(lane_sum, 64);
+}
+
+void orc_moe_router(const float* x, int64_t ldx, const float* w, int E, int live, int K,
+                    float* logits, int64_t ldl) {
+  for (int t = 0; t < live; ++t)
+    for (int e = 0; e < E; ++e)
+      logits[(int64_t)t * ldl + e] = orc_router_dot(x + (int64_t)t * ldx, w + (int64_t)e * K, K);
+}
+
+/* Top-k: for each live row, the k largest logits in descending order, a tie going to the lower
+ * expert id (selection: each round takes the best expert not yet taken). Routing weights are
+ * the softmax over the selected logits, in f32 with exp_q:
+ *   m = l_0 (the largest), e_r = exp_q(l_r - m), s = e_0 + e_1 + ... (ascending r, from +0),
+ *   w_r = e_r / s.
+ * Logits of live rows must not be NaN. weights may be NULL. */
+void orc_moe_topk(const float* logits, int64_t ldl, int E, int live, int k, int32_t* ids,
+                  float* weights) {
+  unsigned char* taken = (unsigned char*)malloc((size_t)E);
+  float* ev = (float*)malloc(sizeof(float) * (size_t)k);
+  for (int t = 0; t < live; ++t) {
+    const float* l = logits + (int64_t)t * ldl;
+    memset(taken, 0, (size_t)E);
+    for (int r = 0; r < k; ++r) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+      taken[best] = 1;
+      ids[(int64_t)t * k + r] = best;
+    }
+    if (weights) {
+      float m = l[ids[(int64_t)t * k]];
+      float sum = 0.0f;
+      for (int r = 0; r < k; ++r) {
+        ev[r] = orc_exp_q(l[ids[(int64_t)t * k + r]] - m);
+        sum = sum + ev[r];
+      }
+      for (int r = 0; r < k; ++r) weights[(int64_t)t * k + r] = ev[r] / sum;
+    }
+  }
+  free(ev);
+  free(taken);
+}
+
+/* ------------------------------------------------------------------------------------------
  * MoE combine of the routed expert outputs with the routing weights, for live rows only
  * ("qwen3_5 CUDA: a captured bucket's padding rows no longer go through the routed experts",
  * What this changes: padding rows get no combine work and their output rows stay unwritten).

@@ -56,6 +56,8 @@ def lib():
             "orc_rms_scale_array": (None, [P, P, i64]),
             "orc_mmvq_id_per_slot": (None, [P, P, i32, i32, i32, P, i32, P, i32, i32, P]),
             "orc_moe_combine": (None, [P, i64, P, P, i32, i32, i32, i32, P, i64]),
+            "orc_moe_router": (None, [P, i64, P, i32, i32, i32, P, i64]),
+            "orc_moe_topk": (None, [P, i64, i32, i32, i32, P, P]),
             "orc_quant_recip_array": (None, [P, P, i64]),
             "orc_quant_scale_array": (None, [P, P, i64]),
             "orc_f32_to_f16_word_array": (None, [P, P, i64]),
@@ -329,3 +331,24 @@ def moe_combine(x: np.ndarray, w: np.ndarray, ids: np.ndarray, E: int, live: int
     out = np.zeros((live, N), dtype=np.float32)
     lib().orc_moe_combine(_p(x), N, _p(w), _p(ids), E, live, top_k, N, _p(out), N)
     return out
+
+
+def moe_router(x: np.ndarray, w: np.ndarray, live: int) -> np.ndarray:
+    """orc_moe_router: logits [live][E] of x [R][K] against router weights w [E][K]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    E, K = w.shape
+    out = np.zeros((live, E), dtype=np.float32)
+    lib().orc_moe_router(_p(x), x.shape[1], _p(w), E, live, K, _p(out), E)
+    return out
+
+
+def moe_topk(logits: np.ndarray, k: int, live: int | None = None):
+    """orc_moe_topk: (ids [live][k] int32, weights [live][k] f32)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    R, E = logits.shape
+    live = R if live is None else live
+    ids = np.zeros((live, k), dtype=np.int32)
+    w = np.zeros((live, k), dtype=np.float32)
+    lib().orc_moe_topk(_p(logits), E, E, live, k, _p(ids), _p(w))
+    return ids, w

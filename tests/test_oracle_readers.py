@@ -244,3 +244,56 @@ def test_moe_combine_closed_forms():
     assert np.array_equal(O.moe_combine(xi, wi, bad, E, rows), O.moe_combine(xi, wz, ids, E, rows))
     # live rows only
     assert O.moe_combine(x, wi, ids, E, 2).shape == (2, N)
+
+
+# ---- device router and top-k ------------------------------------------------------------------
+@pytest.mark.parametrize("K", [256, 2560, 2592])
+def test_router_against_float64(K):
+    g = np.random.default_rng(K)
+    x = g.standard_normal((5, K)).astype(np.float32)
+    w = (g.standard_normal((40, K)) * 0.05).astype(np.float32)
+    got = O.moe_router(x, w, 5).astype(np.float64)
+    prod = np.abs(x.astype(np.float64))[:, None, :] * np.abs(w.astype(np.float64))[None, :, :]
+    J = -(-K // 256)
+    bound = (J + 3 + 6) * 2.0 ** -24 * prod.sum(-1)  # leaf fma chain, J lane adds, 6 tree levels
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    assert (np.abs(got - exact) <= bound).all()
+
+
+def test_router_closed_forms():
+    g = np.random.default_rng(41)
+    K, E = 1024, 24
+    w = g.standard_normal((E, K)).astype(np.float32)
+    # a one-hot activation picks one weight column exactly
+    x = np.zeros((3, K), np.float32)
+    x[0, 5], x[1, 700], x[2, 1023] = 1.0, 1.0, -1.0
+    assert np.array_equal(O.moe_router(x, w, 3), np.stack([w[:, 5], w[:, 700], -w[:, 1023]]))
+    # small integers: every partial sum is exact in any order
+    xi = g.integers(-8, 8, size=(2, K)).astype(np.float32)
+    wi = g.integers(-8, 8, size=(E, K)).astype(np.float32)
+    assert np.array_equal(O.moe_router(xi, wi, 2), (xi.astype(np.int64) @ wi.astype(np.int64).T).astype(np.float32))
+    # live rows only
+    assert O.moe_router(xi, wi, 1).shape == (1, E)
+
+
+def test_topk_against_stable_sort_and_softmax():
+    g = np.random.default_rng(42)
+    R, E, k = 64, 256, 9
+    logits = g.standard_normal((R, E)).astype(np.float32)
+    logits[3, 10] = logits[3, 200] = logits[3].max() + 1  # a tie at the top: lower id first
+    logits[7, :] = 0.5                                    # all equal: ids 0..k-1
+    ids, w = O.moe_topk(logits, k)
+    want = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    assert np.array_equal(ids, want)
+    assert ids[3, 0] == 10 and ids[3, 1] == 200
+    assert np.array_equal(ids[7], np.arange(k)) and (w[7] == np.float32(1.0) / np.float32(k)).all()
+    sel = np.take_along_axis(logits, ids, axis=1).astype(np.float64)
+    sm = np.exp(sel - sel[:, :1])
+    sm /= sm.sum(axis=1, keepdims=True)
+    assert np.abs(w - sm).max() <= 8 * 2.0 ** -24
+    assert (np.diff(w, axis=1) <= 0).all()  # descending logits give non-increasing weights
+    # k = E: a full stable sort
+    ids_all, _ = O.moe_topk(logits[:2], E)
+    assert np.array_equal(ids_all, np.argsort(-logits[:2], axis=1, kind="stable"))
+    # live rows only
+    assert O.moe_topk(logits, k, live=5)[0].shape == (5, k)
