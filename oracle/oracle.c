@@ -507,22 +507,34 @@ void orc_mmvq_id_per_slot(const uint8_t* qs, const uint16_t* d, int E, int N, in
  * experts, combine as one routed chain).
  *
  * Router: logits[t][e] = sum_k x[t][k] * W[e][k] for live rows t, in a fixed order (the pages
- * give none): leaf c (c < K/4) = fma(x3,w3, fma(x2,w2, fma(x1,w1, x0*w0))) over elements
- * 4c..4c+3; lane l in [0,64) owns leaves c = l + 64 j and adds them in ascending j from +0;
- * the 64 lane sums are combined by a balanced pairwise tree over l.
+ * give none), the order of the RMS sum of squares with products for squares: leaf c (c < K/4)
+ * = fma(x3,w3, fma(x2,w2, fma(x1,w1, x0*w0))) over elements 4c..4c+3; lane l in [0,64) owns
+ * leaves c = l + 64 j, j < J' (J' = next power of two >= ceil(K/256); a missing leaf is +0)
+ * and sums them by a balanced pairwise tree over j; the 64 lane sums by a balanced pairwise
+ * tree over l. (A pairwise tree over j lets a row's K range be split over several waves on
+ * subtree boundaries without changing a bit.)
  * ---------------------------------------------------------------------------------------- */
 float orc_router_dot(const float* x, const float* w, int K) {
   int C = K / 4;
+  int J = (K + 255) / 256;
+  int Jp = 1;
+  while (Jp < J) Jp <<= 1;
   float lane_sum[64];
+  float* v = (float*)malloc(sizeof(float) * (size_t)Jp);
   for (int l = 0; l < 64; ++l) {
-    float acc = 0.0f;
-    for (int c = l; c < C; c += 64) {
-      const float* a = x + 4 * c;
-      const float* b = w + 4 * c;
-      acc = acc + fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], a[0] * b[0])));
+    for (int j = 0; j < Jp; ++j) {
+      int c = l + 64 * j;
+      if (c < C) {
+        const float* a = x + 4 * c;
+        const float* b = w + 4 * c;
+        v[j] = fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], a[0] * b[0])));
+      } else {
+        v[j] = 0.0f;
+      }
     }
-    lane_sum[l] = acc;
+    lane_sum[l] = pairwise_tree(v, Jp);
   }
+  free(v);
   return pairwise_tree(lane_sum, 64);
 }
 

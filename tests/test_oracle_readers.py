@@ -8,6 +8,7 @@ accuracy     -> NMSE against the unquantized float64 activation <= 5e-4, the CPU
 plan         -> brute-force sort of the live pairs; the receipt counts of the padded-bucket page
 routed       -> reduces to the ordinary reader with the pair's expert and image row
 """
+import math
 import os
 
 import numpy as np
@@ -255,7 +256,8 @@ def test_router_against_float64(K):
     got = O.moe_router(x, w, 5).astype(np.float64)
     prod = np.abs(x.astype(np.float64))[:, None, :] * np.abs(w.astype(np.float64))[None, :, :]
     J = -(-K // 256)
-    bound = (J + 3 + 6) * 2.0 ** -24 * prod.sum(-1)  # leaf fma chain, J lane adds, 6 tree levels
+    levels = max(0, math.ceil(math.log2(J)))
+    bound = (3 + levels + 6 + 1) * 2.0 ** -24 * prod.sum(-1)  # leaf fma chain, then two pairwise trees
     exact = x.astype(np.float64) @ w.astype(np.float64).T
     assert (np.abs(got - exact) <= bound).all()
 
