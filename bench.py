@@ -122,8 +122,9 @@ def algorithmic_bytes(wl):
 
 
 class MoeInstance:
-    """Device tensors of one routed MoE FFN: RMS producer + image -> gate/up experts -> per-slot
-    SwiGLU + image -> per-slot down experts -> combine with the routing weights."""
+    """Device tensors of one routed MoE FFN: RMS producer + image -> device router (reading the
+    kept f32 output) and top-k -> gate/up experts -> per-slot SwiGLU + image -> per-slot down
+    experts -> combine with the routing weights."""
 
     def __init__(self, wl):
         from q8_activation_quant_amd import qimg
@@ -145,10 +146,18 @@ class MoeInstance:
         self.wg = qimg.tile_q4_0(dev(wl.readers[0].qs), dev(wl.readers[0].d), K)
         self.wu = qimg.tile_q4_0(dev(wl.readers[1].qs), dev(wl.readers[1].d), K)
         self.wd = qimg.tile_q4_0(dev(wl.down.qs), dev(wl.down.d), F)
+        # device routing: router weights, logits; the top-k rewrites ids and routing weights
+        self.rw = dev(wl.router_w)
+        self.logits = f32(B, wl.E)
 
     def produce(self):
         from q8_activation_quant_amd import qimg
         qimg.emit_rmsnorm(self.x, self.gamma, 1e-6, self.y, self.img, self.live)
+
+    def route(self):
+        from q8_activation_quant_amd import qimg
+        qimg.moe_router(self.y, self.rw, self.logits, self.live)
+        qimg.moe_topk(self.logits, self.ids, self.w, self.live)
 
     def gate_up(self):
         from q8_activation_quant_amd import qimg
@@ -172,26 +181,31 @@ class MoeInstance:
 
     def step(self):
         self.produce()
+        self.route()
         self.gate_up()
         self.glu()
         self.down_proj()
         self.combine()
 
 
-def moe_bytes(wl):
+def moe_bytes(wl, ids):
     """Algorithmic bytes of one MoE FFN (live rows L, pairs P = L top_k, distinct experts U):
-    x, gamma read, y written, token image written and read; gate/up weights of U experts; ids
+    x, gamma read, y written, token image written and read; the router reading y and its f32
+    weights and writing the logits, the top-k reading them and writing ids and routing
+    weights; gate/up weights of U experts; ids
     read by both routed launches; gate/up outputs written and read by the GLU; h written; the
     per-slot image written and read; down weights of U experts; down outputs written and read
     by the combine; routing weights and ids read by the combine; the output written."""
     B, k, K, F = wl.T, wl.top_k, wl.K, wl.n_ff
     L = wl.live if wl.live is not None else B
     P = L * k
-    U = len(np.unique(wl.ids[:L].reshape(-1)))
+    U = len(np.unique(ids[:L].reshape(-1)))  # the experts the device router picked
     img_tok = L * (K // 32) * 36
     img_pair = P * (F // 32) * 36
+    E = wl.E
     parts = {
         "producer": L * K * 4 + K * 4 + L * K * 4 + img_tok,
+        "route": L * K * 4 + E * K * 4 + 2 * L * E * 4 + 2 * P * 4,
         "gate_up": img_tok + U * 2 * F * (K // 32) * 18 + P * 4 + 2 * P * F * 4,
         "glu": 2 * P * F * 4 + P * F * 4 + img_pair,
         "down": img_pair + U * K * (F // 32) * 18 + P * 4 + P * K * 4,
@@ -208,9 +222,11 @@ def run_moe(config, steps, warmup, live=None):
     wbytes = sum(r.nbytes for r in wl.readers) + wl.down.nbytes
     R = max(1, int(np.ceil(ROT_BYTES / wbytes)))
     insts = [MoeInstance(wl) for _ in range(R)]
-    res = {"wl": wl, "R": R, "bytes": moe_bytes(wl)}
+    insts[0].step()
+    torch.cuda.synchronize()
+    res = {"wl": wl, "R": R, "bytes": moe_bytes(wl, insts[0].ids.cpu().numpy())}
     res["us"] = time_graph([i.step for i in insts], steps, warmup)
-    for part in ("produce", "gate_up", "glu", "down_proj", "combine"):
+    for part in ("produce", "route", "gate_up", "glu", "down_proj", "combine"):
         res[part] = float(np.median(time_graph([getattr(i, part) for i in insts], steps, warmup)))
     del insts
     torch.cuda.empty_cache()
@@ -399,7 +415,7 @@ def main():
             "algorithmic_bytes": nb,
             "achieved_GBs": round(nb["total"] / (us * 1e-6) / 1e9, 1),
             "pct_of_hbm_peak": round(100 * nb["total"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
-            "launch_us": {p: round(r[p], 3) for p in ("produce", "gate_up", "glu", "down_proj", "combine")},
+            "launch_us": {p: round(r[p], 3) for p in ("produce", "route", "gate_up", "glu", "down_proj", "combine")},
             "roofline": {"bound": "hbm", "kernel": "mmvq_routed_kernel (per-slot down projection)",
                          "achieved": round(down_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(down_gbs / PEAK_HBM_GBS, 4), "traffic": None,

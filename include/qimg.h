@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 6
+#define QIMG_ABI_VERSION 7
 
 /* status codes */
 #define QIMG_OK 0
@@ -80,6 +80,7 @@ extern "C" {
 #define QIMG_MAX_READERS 8
 #define QIMG_MAX_EXPERTS 1024       /* routed readers: E */
 #define QIMG_MAX_ROUTED_PAIRS 4096  /* routed readers: bucket * top_k */
+#define QIMG_MAX_TOPK 64            /* qimg_moe_topk: top_k */
 
 /* GLU producer formulas ([P1] Coverage: F32 ReGLU, GeGLU, SwiGLU, GeGLU-erf, GeGLU-quick,
  * SwiGLU-OAI and SwiGLU-clamp producers). g = gate, u = up; the last two take alpha and limit
@@ -283,6 +284,32 @@ int mmvq_id_q4_0_q8_1_per_slot(const qimg_q4_0_expert_reader* readers, int32_t n
 int qimg_moe_combine(const float* x, int64_t ld_pair, const float* weights, const int32_t* ids,
                      int32_t E, int32_t bucket, int32_t top_k, const int32_t* live_rows,
                      int32_t N, float* out, int64_t ldo, void* stream);
+
+/*
+ * Device router and top-k with live-row guards ([P3] What this changes: router and top-k take
+ * the live count and skip padding rows, which get no picks; their outputs stay unwritten).
+ *
+ * qimg_moe_router: logits[t*ldl + e] = sum over k < K of x[t*ldx + k] * w[e*K + k] for live
+ *   rows t (t < *live_rows clamped to [0, bucket]; all rows when live_rows is NULL), in a
+ *   fixed order: 4-element fma leaves, lane l of 64 adding leaves l + 64 j in ascending j,
+ *   then a pairwise tree over the 64 lanes (so the logits, and every pick made from them,
+ *   are reproducible bit for bit).
+ *   x: f32, 16-byte aligned, ldx % 4 == 0, ldx >= K (the kept f32 output of a producer is the
+ *   usual input); w: f32 [E][K], 16-byte aligned; logits: f32 [bucket][ldl], ldl >= E, must not
+ *   overlap x, w or live_rows. K: as for the producers.
+ * qimg_moe_topk: for live rows t, ids[t*top_k + r] = the expert with the r-th largest logit
+ *   (equal logits: lower id first), r < top_k, and, when weights != NULL, the softmax over the
+ *   selected logits: e_r = exp(l_r - l_0) (the library's exp), s = e_0 + ... + e_{k-1} in
+ *   ascending r, weights[t*top_k + r] = e_r / s. Live logits must not be NaN.
+ *   1 <= top_k <= min(E, QIMG_MAX_TOPK); E <= QIMG_MAX_EXPERTS (QIMG_EUNSUPPORTED beyond).
+ *   ids: int32 [bucket][top_k]; weights: f32 [bucket][top_k] or NULL; neither may overlap
+ *   logits, live_rows or each other.
+ */
+int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int32_t bucket,
+                    const int32_t* live_rows, int32_t K, float* logits, int64_t ldl, void* stream);
+int qimg_moe_topk(const float* logits, int64_t ldl, int32_t E, int32_t bucket,
+                  const int32_t* live_rows, int32_t top_k, int32_t* ids, float* weights,
+                  void* stream);
 
 /*
  * Debug export of the per-block integer dot products of one ordinary reader, computed by the

@@ -92,6 +92,17 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
   return pair_sum_halves(v);
 }
 
+// balanced pairwise tree over a lane's JW values (JW a power of two)
+template <int JW>
+__device__ __forceinline__ float tree_sum(float (&v)[JW]) {
+#pragma unroll
+  for (int w = JW; w > 1; w >>= 1) {
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  }
+  return v[0];
+}
+
 // exp_q: Cody-Waite reduction by ln 2 split into a 12-bit-short high part and an f32 low part,
 // degree-7 Taylor polynomial of e^r with coefficients 1/k! rounded to f32 (Horner, fma), then
 // scaling by 2^n. NaN passes through, x > 88.8 gives +inf, x < -86 gives +0 (no subnormal
@@ -150,6 +161,204 @@ __device__ __forceinline__ float geglu_erf_act(float g) {
   const float z = g * kSqrtHalf;
   const float ope = (z < 0.0f) ? erfc_q(-z) : 2.0f - erfc_q(z);
   return (0.5f * g) * ope;
+}
+
+// Device router and top-k ("qwen3_5 CUDA: a captured bucket's padding rows no longer go through
+// the routed experts", What this changes: router and top-k read the live count; padding rows
+// get no picks and their outputs stay unwritten).
+//
+// Router: logits[t][e] = x[t] . W[e] over K for live rows, in the order of the RMS sum of
+// squares with products: leaf c (4 elements) = fma(x3,w3, fma(x2,w2, fma(x1,w1, x0*w0)));
+// lane l owns leaves c = l + 64 j, j < Jp (next power of two >= ceil(K/256), missing leaves
+// +0), summed by a pairwise tree over j; the 64 lane sums by a pairwise tree (wave_tree_sum).
+// One workgroup per (block of EB experts, group of 8 rows): wave w holds leaves j in
+// [w JW, (w+1) JW) of every row and expert (JW = Jp / W), sums them by the lower levels of the
+// tree, and the W wave partials are combined through LDS by its top levels; the (expert, row)
+// dots are then finished by the waves in turn. The activations of the rows are loaded once per
+// workgroup and shared by its EB experts; all loads of a wave go out together.
+struct RouterArgs {
+  const float* x;  // [bucket][ldx]
+  int64_t ldx;
+  const float* w;  // [E][K]
+  const int32_t* live_rows;
+  float* logits;   // [bucket][ldl]
+  int64_t ldl;
+  int32_t rows, E, K;
+};
+
+template <int JW, int EB>
+__global__ __launch_bounds__(1024) void moe_router_kernel(RouterArgs a) {
+  const int live = clamp_live(a.live_rows, a.rows, nullptr);
+  const int t0 = blockIdx.y * 8;
+  if (t0 >= live) return;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* part = reinterpret_cast<float*>(smem);  // [W][EB][8][64]
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int e0 = blockIdx.x * EB;
+  const int ne = a.E - e0 < EB ? a.E - e0 : EB;
+  const int nt = live - t0 < 8 ? live - t0 : 8;
+  const int C = a.K >> 2;
+  // leaves past K re-read leaf 0 (in bounds) and count as +0; experts past E re-read expert e0
+  // and rows past the live count re-read row t0 (their results are not stored). With one
+  // expert per workgroup (long rows) the activation leaves are loaded row by row.
+  constexpr int XT = EB > 1 ? 8 : 1;
+  float4 wv[EB][JW], xv[XT][JW];
+  auto load_x = [&](int t, float4 (&dst)[JW]) {
+    const float* xr = a.x + (int64_t)(t0 + (t < nt ? t : 0)) * a.ldx;
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      const int c = lane + 64 * (w * JW + jj);
+      dst[jj] = *reinterpret_cast<const float4*>(xr + 4 * (c < C ? c : 0));
+    }
+  };
+#pragma unroll
+  for (int b = 0; b < EB; ++b) {
+    const float* wr = a.w + (int64_t)(e0 + (b < ne ? b : 0)) * a.K;
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      const int c = lane + 64 * (w * JW + jj);
+      wv[b][jj] = *reinterpret_cast<const float4*>(wr + 4 * (c < C ? c : 0));
+    }
+  }
+  if constexpr (XT == 8) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) load_x(t, xv[t]);
+  }
+#pragma unroll
+  for (int b = 0; b < EB; ++b)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if constexpr (XT == 1) {
+        if (t >= nt) break;
+        load_x(t, xv[0]);
+      }
+      float leaf[JW];
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj) {
+        const int c = lane + 64 * (w * JW + jj);
+        const float4 q = wv[b][jj], v = xv[XT == 8 ? t : 0][jj];
+        leaf[jj] = c < C ? __builtin_fmaf(v.w, q.w, __builtin_fmaf(v.z, q.z,
+                                          __builtin_fmaf(v.y, q.y, v.x * q.x)))
+                         : 0.0f;
+      }
+      part[((w * EB + b) * 8 + t) * 64 + lane] = tree_sum<JW>(leaf);
+    }
+  __syncthreads();
+  for (int q = w; q < EB * 8; q += W) {
+    const int b = q >> 3, t = q & 7;
+    if (b < ne && t < nt) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = i < W ? part[((i * EB + b) * 8 + t) * 64 + lane] : 0.0f;
+      for (int n = W; n > 1; n >>= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < n / 2) v[i] = v[2 * i] + v[2 * i + 1];
+      const float sum = wave_tree_sum(v[0]);
+      if (lane == 0) a.logits[(int64_t)(t0 + t) * a.ldl + e0 + b] = sum;
+    }
+  }
+}
+
+// Top-k: one wave per live row. Each lane keeps the best of its own experts not yet taken as
+// a 64-bit key (order-preserving bits of the logit, -0 made +0, then the complemented id, so
+// equal logits rank the lower id first) and every round takes the wave maximum of the keys
+// by DPP and permlane moves; only the winning lane rescans its experts. Routing weights: the
+// softmax over the selected logits, e_r = exp_q(l_r - l_0), s = e_0 + e_1 + ... in ascending
+// r from +0, w_r = e_r / s. Lane r keeps pick r.
+struct TopkArgs {
+  const float* logits;  // [bucket][ldl]
+  int64_t ldl;
+  const int32_t* live_rows;
+  int32_t* ids;         // [bucket][k]
+  float* w;             // [bucket][k] or null
+  int32_t rows, E, k;
+};
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+template <int CTRL>
+__device__ __forceinline__ void key_max_dpp(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = (uint32_t)dpp_n<CTRL>((int)hi), ol = (uint32_t)dpp_n<CTRL>((int)lo);
+  if (oh > hi || (oh == hi && ol > lo)) {
+    hi = oh;
+    lo = ol;
+  }
+}
+__device__ __forceinline__ void key_max_pair(uint32_t& hi, uint32_t& lo, bool halves) {
+  const auto h = halves ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                        : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const auto l = halves ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                        : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const bool second = h[1] > h[0] || (h[1] == h[0] && l[1] > l[0]);
+  hi = second ? h[1] : h[0];
+  lo = second ? l[1] : l[0];
+}
+
+__global__ __launch_bounds__(64) void moe_topk_kernel(TopkArgs a) {
+  const int t = blockIdx.x;
+  if (t >= clamp_live(a.live_rows, a.rows, nullptr)) return;
+  const int lane = threadIdx.x;
+  constexpr int kPer = QIMG_MAX_EXPERTS / 64;
+  const float* lr = a.logits + (int64_t)t * a.ldl;
+  uint32_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    // unconditional in-bounds load; 0 (below every logit's key) where there is no expert
+    const float v = lr[e < a.E ? e : 0];
+    key[i] = order_key(v) & (e < a.E ? 0xffffffffu : 0u);
+  }
+  // this lane's best: slot bi with key bk (the largest; ties to the lower slot = lower id)
+  int bi = 0;
+  uint32_t bk = 0;
+  auto local_best = [&]() {
+    bi = 0;
+    bk = key[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i)
+      if (key[i] > bk) {
+        bk = key[i];
+        bi = i;
+      }
+  };
+  local_best();
+  int my_id = 0;
+  float my_l = 0.0f;
+  for (int r = 0; r < a.k; ++r) {
+    uint32_t hi = bk, lo = ~(uint32_t)(lane + 64 * bi);
+    key_max_dpp<kDppXor1>(hi, lo);
+    key_max_dpp<kDppXor2>(hi, lo);
+    key_max_dpp<kDppHalfMirror>(hi, lo);
+    key_max_dpp<kDppMirror>(hi, lo);
+    key_max_pair(hi, lo, false);
+    key_max_pair(hi, lo, true);
+    const int id = (int)~lo;
+    if (lane == r) {
+      my_id = id;
+      const uint32_t u = (hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi;
+      my_l = __uint_as_float(u);
+    }
+    if ((id & 63) == lane) {  // the winner's lane takes it and rescans
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (i == (id >> 6)) key[i] = 0u;
+      local_best();
+    }
+  }
+  if (lane < a.k) a.ids[(int64_t)t * a.k + lane] = my_id;
+  if (a.w) {
+    const float m = __shfl(my_l, 0, 64);
+    const float ev = exp_q(my_l - m);
+    float sum = 0.0f;
+    for (int r = 0; r < a.k; ++r)
+      sum = sum + __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ev), r));
+    if (lane < a.k) a.w[(int64_t)t * a.k + lane] = ev / sum;
+  }
 }
 
 // MoE combine ("qwen3_5 CUDA: a captured bucket's padding rows no longer go through the
@@ -309,16 +518,6 @@ struct EmitArgs {
   float scale;         // rms: final factor (1 keeps the value)
   float alpha, limit;  // SwiGLU-OAI / SwiGLU-clamp parameters
 };
-
-template <int JW>
-__device__ __forceinline__ float tree_sum(float (&v)[JW]) {
-#pragma unroll
-  for (int w = JW; w > 1; w >>= 1) {
-#pragma unroll
-    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
-  }
-  return v[0];
-}
 
 __device__ __forceinline__ void quantize_leaf(const float4 y, int row, int blk, int lane,
                                               const EmitArgs& p) {
@@ -1854,6 +2053,71 @@ int mmvq_id_q4_0_q8_1_per_slot(const qimg_q4_0_expert_reader* readers, int32_t n
                                void* workspace, size_t workspace_bytes, void* stream) {
   return routed_common(readers, n_readers, E, img, ids, bucket, top_k, live_rows, K, workspace,
                        workspace_bytes, 1, stream);
+}
+
+int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int32_t bucket,
+                    const int32_t* live_rows, int32_t K, float* logits, int64_t ldl, void* stream) {
+  int st = check_k(K);
+  if (st) return st;
+  if (!x || !w || !logits || E <= 0 || bucket < 0 || ldx < K || ldl < E) return QIMG_EINVAL;
+  if (bucket == 0) return QIMG_OK;
+  if (!al16(x) || ldx % 4 || !al16(w) || !al(logits, 4) || (live_rows && !al(live_rows, 4)))
+    return QIMG_EALIGN;
+  const Span so = span(logits, rows_extent(bucket, ldl, E, 4));
+  if (overlap(so, span(x, rows_extent(bucket, ldx, K, 4))) || overlap(so, span(w, (int64_t)E * K * 4)) ||
+      (live_rows && overlap(so, span(live_rows, 4))))
+    return QIMG_EALIAS;
+  RouterArgs a{x, ldx, w, live_rows, logits, ldl, bucket, E, K};
+  // the RMS producer's shape: Jp leaves per lane over W = min(16, max(1, Jp/2)) waves
+  const int J = (K + 255) / 256;
+  int Jp = 1;
+  while (Jp < J) Jp <<= 1;
+  int W = Jp / 2;
+  if (W < 1) W = 1;
+  if (W > 16) W = 16;
+  const int JW = Jp / W;
+  // experts per workgroup: 4 for buckets of many rows (each workgroup then loads its rows'
+  // activations once for 4 experts) while the wave partials fit in 64 KB of LDS, else 1
+  const int EB = (W <= 8 && bucket > 16) ? 4 : 1;
+  const size_t lds = (size_t)W * EB * 8 * 64 * 4;
+  const dim3 grid((unsigned)((E + EB - 1) / EB), (unsigned)((bucket + 7) / 8)), block((unsigned)(W * 64));
+  hipStream_t s = (hipStream_t)stream;
+  if (EB == 4) {
+    switch (JW) {
+      case 1: hipLaunchKernelGGL((moe_router_kernel<1, 4>), grid, block, lds, s, a); break;
+      case 2: hipLaunchKernelGGL((moe_router_kernel<2, 4>), grid, block, lds, s, a); break;
+      default: return QIMG_EUNSUPPORTED;  // W <= 8 gives JW <= 2
+    }
+  } else {
+    switch (JW) {
+      case 1: hipLaunchKernelGGL((moe_router_kernel<1, 1>), grid, block, lds, s, a); break;
+      case 2: hipLaunchKernelGGL((moe_router_kernel<2, 1>), grid, block, lds, s, a); break;
+      case 4: hipLaunchKernelGGL((moe_router_kernel<4, 1>), grid, block, lds, s, a); break;
+      case 8: hipLaunchKernelGGL((moe_router_kernel<8, 1>), grid, block, lds, s, a); break;
+      default: return QIMG_EUNSUPPORTED;
+    }
+  }
+  return launch_status();
+}
+
+int qimg_moe_topk(const float* logits, int64_t ldl, int32_t E, int32_t bucket,
+                  const int32_t* live_rows, int32_t top_k, int32_t* ids, float* weights,
+                  void* stream) {
+  if (!logits || !ids || E <= 0 || bucket < 0 || top_k <= 0 || top_k > E || ldl < E)
+    return QIMG_EINVAL;
+  if (E > QIMG_MAX_EXPERTS || top_k > QIMG_MAX_TOPK) return QIMG_EUNSUPPORTED;
+  if (bucket == 0) return QIMG_OK;
+  if (!al(logits, 4) || !al(ids, 4) || (weights && !al(weights, 4)) || (live_rows && !al(live_rows, 4)))
+    return QIMG_EALIGN;
+  const Span sl = span(logits, rows_extent(bucket, ldl, E, 4));
+  const Span si = span(ids, (int64_t)bucket * top_k * 4);
+  const Span sw = weights ? span(weights, (int64_t)bucket * top_k * 4) : Span{0, 0};
+  const Span sv = live_rows ? span(live_rows, 4) : Span{0, 0};
+  if (overlap(si, sl) || overlap(si, sv) || overlap(sw, sl) || overlap(sw, sv) || overlap(si, sw))
+    return QIMG_EALIAS;
+  TopkArgs a{logits, ldl, live_rows, ids, weights, bucket, E, top_k};
+  hipLaunchKernelGGL(moe_topk_kernel, dim3((unsigned)bucket), dim3(64), 0, (hipStream_t)stream, a);
+  return launch_status();
 }
 
 int qimg_moe_combine(const float* x, int64_t ld_pair, const float* weights, const int32_t* ids,

@@ -19,7 +19,7 @@ GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF, "reglu": GLU_REGLU,
            "geglu_quick": GLU_GEGLU_QUICK, "swiglu_oai": GLU_SWIGLU_OAI, "swiglu_clamp": GLU_SWIGLU_CLAMP}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
@@ -27,7 +27,7 @@ EXPORTS = (
     "mmvq_id_workspace_bytes", "mmvq_id_q4_0_q8_1", "mmvq_q4_0_q8_1_blockdots",
     "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile", "qimg_eval_math",
     "qimg_emit_glu_per_slot", "mmvq_id_q4_0_q8_1_per_slot", "qimg_moe_combine",
-    "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex",
+    "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex", "qimg_moe_router", "qimg_moe_topk",
 )
 MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7, "reglu": 8,
             "geglu": 9, "geglu_quick": 10, "swiglu_oai_gate": 11}
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
             "qimg_moe_combine": (ctypes.c_int, [P, i64, P, P, i32, i32, i32, P, i32, P, i64, P]),
             "qimg_emit_rmsnorm_ex": (ctypes.c_int, [P, i64, P, P, f32, f32, i32, P, i32, P, i64, P, P]),
             "qimg_emit_glu_ex": (ctypes.c_int, [i32, f32, f32, P, i64, P, i64, i32, P, i32, P, i64, P, P]),
+            "qimg_moe_router": (ctypes.c_int, [P, i64, P, i32, i32, P, i32, P, i64, P]),
+            "qimg_moe_topk": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -259,3 +261,19 @@ def eval_math(fn, first_bits, out, stream=None):
     fn = MATH_FNS[fn] if isinstance(fn, str) else fn
     _check(lib().qimg_eval_math(fn, ctypes.c_uint32(first_bits & 0xFFFFFFFF), out.numel(), _ptr(out),
                                 _stream(stream)), "qimg_eval_math")
+
+
+def moe_router(x, w, logits, live_rows=None, stream=None):
+    """logits [bucket, E] = x [bucket, K] . w [E, K]^T for live rows (fixed summation order)."""
+    bucket, K = x.shape
+    E = w.shape[0]
+    _check(lib().qimg_moe_router(_ptr(x), _ld(x), _ptr(w), E, bucket, _ptr(live_rows), K, _ptr(logits),
+                                 _ld(logits), _stream(stream)), "qimg_moe_router")
+
+
+def moe_topk(logits, ids, weights=None, live_rows=None, stream=None):
+    """ids [bucket, k] (and softmax weights [bucket, k]) of the k largest logits per live row."""
+    bucket, E = logits.shape
+    k = ids.shape[1]
+    _check(lib().qimg_moe_topk(_ptr(logits), _ld(logits), E, bucket, _ptr(live_rows), k, _ptr(ids),
+                               _ptr(weights), _stream(stream)), "qimg_moe_topk")

@@ -21,7 +21,8 @@ MoE FFN extension of the routed workloads (moe=True): the per-slot SwiGLU over t
 outputs, a Q4_0 down projection per (token, slot) with expert weights [E, K, n_ff] (workload
 4: n_ff 768; workload 5: n_ff 512), then the combine with the routing weights. Stage inputs
 for checking each step on its own: pair_gu ~ N(0,1) [T*top_k][2*n_ff] (packed gate|up per
-pair) and pair_x ~ N(0,1) [T][top_k][K] (expert outputs for the combine).
+pair) and pair_x ~ N(0,1) [T][top_k][K] (expert outputs for the combine); router weights
+~ N(0, 0.05^2) [E][K] for the device router.
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ import numpy as np
 
 # tensor ids of the seeded streams
 T_X, T_GAMMA, T_OUTLIER, T_GU, T_LOGITS, T_STALE_IDS, T_EXTRA = 0, 1, 2, 3, 4, 5, 6
-T_PAIR_GU, T_PAIR_X = 7, 8
+T_PAIR_GU, T_PAIR_X, T_ROUTER = 7, 8, 9
 T_READER0 = 10  # reader r uses T_READER0 + r
 T_DOWN = 20     # MoE down projection
 
@@ -93,6 +94,7 @@ class Workload:
     down: Q4Weights | None = None       # MoE: down projection [E, K, n_ff]
     pair_gu: np.ndarray | None = None   # MoE stage input [T*top_k][2*n_ff]
     pair_x: np.ndarray | None = None    # MoE stage input [T][top_k][K]
+    router_w: np.ndarray | None = None  # MoE: router weights [E][K] f32
 
     @property
     def routed(self) -> bool:
@@ -116,6 +118,7 @@ def make(config: int, *, live: int | None = None, glu_op: str = "swiglu", small:
         wl.down = q4_0_weights(rng(c, T_DOWN), (wl.E, wl.K if not small else 80), wl.n_ff)
         wl.pair_gu = rng(c, T_PAIR_GU).standard_normal((wl.T * wl.top_k, 2 * wl.n_ff)).astype(np.float32)
         wl.pair_x = rng(c, T_PAIR_X).standard_normal((wl.T, wl.top_k, wl.K)).astype(np.float32)
+        wl.router_w = (rng(c, T_ROUTER).standard_normal((wl.E, wl.K)) * 0.05).astype(np.float32)
         wl.name += " moe-ffn n_ff%d" % wl.n_ff
     return wl
 

@@ -344,3 +344,37 @@ def test_emit_rmsnorm_ex_validation(L):
     assert rms(y=B + 4096) == qimg.EALIAS
     assert rms(img=B + 4096 - 64) == qimg.EALIAS
     assert rms(x=None) == qimg.EINVAL
+
+
+def test_moe_router_validation(L):
+    def router(x=A, ldx=256, w=B, E=8, bucket=4, live=None, K=256, lg=C, ldl=8):
+        return L.qimg_moe_router(x, ldx, w, E, bucket, live, K, lg, ldl, S)
+
+    assert router(K=100) == qimg.EINVAL
+    assert router(E=0) == qimg.EINVAL
+    assert router(x=None) == qimg.EINVAL
+    assert router(ldx=128) == qimg.EINVAL
+    assert router(ldl=4) == qimg.EINVAL
+    assert router(bucket=0) == qimg.OK
+    assert router(x=A + 4) == qimg.EALIGN
+    assert router(ldx=258) == qimg.EALIGN
+    assert router(lg=C + 2) == qimg.EALIGN
+    assert router(lg=A + 64) == qimg.EALIAS
+    assert router(lg=B + 1024) == qimg.EALIAS
+
+
+def test_moe_topk_validation(L):
+    def topk(lg=A, ldl=256, E=256, bucket=4, live=None, k=8, ids=B, w=C):
+        return L.qimg_moe_topk(lg, ldl, E, bucket, live, k, ids, w, S)
+
+    assert topk(k=0) == qimg.EINVAL
+    assert topk(k=257) == qimg.EINVAL
+    assert topk(ldl=100) == qimg.EINVAL
+    assert topk(ids=None) == qimg.EINVAL
+    assert topk(E=2048, ldl=2048) == qimg.EUNSUPPORTED
+    assert topk(k=65, E=256) == qimg.EUNSUPPORTED
+    assert topk(bucket=0) == qimg.OK
+    assert topk(ids=B + 2) == qimg.EALIGN
+    assert topk(ids=A + 64) == qimg.EALIAS
+    assert topk(w=B + 16) == qimg.EALIAS
+    assert topk(live=B + 32) == qimg.EALIAS

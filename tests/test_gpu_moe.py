@@ -305,3 +305,136 @@ def test_moe_chain_graph_replay_at_changing_live_counts():
         for t, ref in refs.items():
             if t < L:
                 assert np.array_equal(out[t].view(np.uint32), ref.view(np.uint32)), "live %d row %d" % (L, t)
+
+
+# ---- device router and top-k ------------------------------------------------------------------
+@pytest.mark.parametrize("bucket,live,K,E", [(8, None, 2560, 128), (128, 113, 2048, 256), (13, 11, 2592, 37),
+                                             (4, 4, 8192, 1024), (3, 2, 32768, 21), (9, None, 32, 6)])
+def test_router_bit_exact(bucket, live, K, E):
+    g = np.random.default_rng(bucket + K + E)
+    x = g.standard_normal((bucket, K)).astype(np.float32)
+    w = (g.standard_normal((E, K)) * 0.05).astype(np.float32)
+    L = bucket if live is None else live
+    logits = H.sentinel_f32(bucket, E)
+    qimg.moe_router(H.dev(x), H.dev(w), logits, H.live_tensor(live) if live is not None else None)
+    sync()
+    got = H.host(logits)
+    want = O.moe_router(x, w, L)
+    assert np.array_equal(got[:L].view(np.uint32), want.view(np.uint32)), "router logits differ"
+    assert (got[L:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding rows of the logits were written"
+
+
+@pytest.mark.parametrize("bucket,live,E,k", [(8, None, 128, 8), (128, 114, 256, 9), (5, 3, 1024, 64),
+                                             (3, 3, 7, 7), (16, 9, 40, 1)])
+def test_topk_bit_exact(bucket, live, E, k):
+    g = np.random.default_rng(bucket * 1000 + E + k)
+    logits = g.standard_normal((bucket, E)).astype(np.float32)
+    logits[0, E // 2] = logits[0, E // 3] = logits[0].max() + 0.5  # tie at the top: lower id first
+    if bucket > 1:
+        logits[1, :] = -1.25                                      # all equal
+    L = bucket if live is None else live
+    ids = H.torch().full((bucket, k), -7, dtype=H.torch().int32, device="cuda")
+    w = H.sentinel_f32(bucket, k)
+    qimg.moe_topk(H.dev(logits), ids, w, H.live_tensor(live) if live is not None else None)
+    sync()
+    ids, w = H.host(ids), H.host(w)
+    ids_o, w_o = O.moe_topk(logits, k, live=L)
+    assert np.array_equal(ids[:L], ids_o), "top-k ids differ"
+    assert np.array_equal(w[:L].view(np.uint32), w_o.view(np.uint32)), "routing weights differ"
+    assert (ids[L:] == -7).all() and (w[L:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding rows written"
+
+
+class RoutedChain(Chain):
+    """The FFN with device routing: the router reads the producer's kept f32 output, the top-k
+    writes the ids and routing weights that the experts and the combine use."""
+
+    def __init__(self, wl):
+        super().__init__(wl)
+        torch = H.torch()
+        self.rw = H.dev(wl.router_w)
+        self.logits = H.sentinel_f32(wl.T, wl.E)
+        self.ids = torch.full((wl.T, wl.top_k), -7, dtype=torch.int32, device="cuda")
+        self.w = H.sentinel_f32(wl.T, wl.top_k)
+
+    def run(self):
+        wl = self.wl
+        F = wl.n_ff
+        qimg.emit_rmsnorm(self.x, self.gamma, W.EPS, self.y, self.img, self.live)
+        qimg.moe_router(self.y, self.rw, self.logits, self.live)
+        qimg.moe_topk(self.logits, self.ids, self.w, self.live)
+        qimg.mmvq_id([(self.wg, F, self.gate), (self.wu, F, self.up)], wl.E, self.img, self.ids, self.live,
+                     wl.K, self.ws)
+        qimg.emit_glu_per_slot("swiglu", self.gate, self.up, self.h, self.himg, self.live)
+        qimg.mmvq_id_per_slot([(self.wd, wl.down.d.shape[-2], self.down)], wl.E, self.himg, self.ids,
+                              self.live, F, self.ws2)
+        qimg.moe_combine(self.down, self.w, self.ids, wl.E, self.out, self.live)
+
+
+@pytest.mark.parametrize("cfg,live", [(4, None), (5, 9)])
+def test_device_routed_chain(cfg, live):
+    wl = W.make(cfg, moe=True, live=live)
+    L = live_of(wl)
+    ch = RoutedChain(wl)
+    ch.run()
+    sync()
+    # the picks are integer decisions taken from bit-exact logits: they equal the oracle's
+    y_o = O.rmsnorm(wl.x[:L], wl.gamma, W.EPS)
+    ids_o, w_o = O.moe_topk(O.moe_router(y_o, wl.router_w, L), wl.top_k)
+    ids, w = H.host(ch.ids), H.host(ch.w)
+    assert np.array_equal(ids[:L], ids_o) and np.array_equal(w[:L].view(np.uint32), w_o.view(np.uint32))
+    assert (ids[L:] == -7).all()
+    ow = W.Workload(**{**wl.__dict__, "ids": np.concatenate([ids_o, wl.ids[L:]]),
+                       "route_w": np.concatenate([w_o, wl.route_w[L:]])})
+    out = H.host(ch.out)
+    want = oracle_chain(ow, L)
+    nw = np.abs(out[:L].astype(np.float64) - want).max() / np.abs(want).max()
+    assert nw <= 1e-3, "normwise error against the oracle chain %.3g" % nw
+    assert H.nmse(out[:L], f64_chain(ow, L)) <= 5e-4
+    assert (out[L:].view(np.uint8) == H.SENTINEL_BYTE).all()
+
+
+def test_device_routed_chain_graph_replay():
+    # the whole routed chain (router and top-k included) captured once for the 128-row bucket and
+    # replayed at changing live counts; padding rows get no picks and no outputs, live rows equal
+    # one-row runs byte for byte
+    torch = H.torch()
+    wl = W.make(5, moe=True, small=True)
+    ch = RoutedChain(wl)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ch.run()
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ch.run()
+    refs = {}
+    for t in (0, 8, 112, 113, 127):
+        one = W.make(5, moe=True, small=True)
+        one.T, one.live = 1, 1
+        one.x = wl.x[t:t + 1].copy()
+        one.readers, one.down, one.router_w = wl.readers, wl.down, wl.router_w
+        c1 = RoutedChain(one)
+        c1.run()
+        sync()
+        refs[t] = (H.host(c1.out)[0], H.host(c1.ids)[0])
+    for phase, L in enumerate((1, 9, 113, 114, 128, 113, 9, 1)):
+        xp = wl.x.copy()
+        W.poison_rows(xp, L, phase)
+        ch.x.copy_(H.dev(xp))
+        ch.live.fill_(L)
+        ch.ids.fill_(-7)
+        for buf in (ch.out, ch.down, ch.logits, ch.w):
+            buf.view(torch.uint8).fill_(H.SENTINEL_BYTE)
+        sync()
+        g.replay()
+        sync()
+        out, ids = H.host(ch.out), H.host(ch.ids)
+        assert (ids[L:] == -7).all(), "live %d: padding rows were routed" % L
+        assert (H.host(ch.logits)[L:].view(np.uint8) == H.SENTINEL_BYTE).all()
+        assert (out[L:].view(np.uint8) == H.SENTINEL_BYTE).all(), "live %d: padding rows written" % L
+        for t, (ref_out, ref_ids) in refs.items():
+            if t < L:
+                assert np.array_equal(ids[t], ref_ids), "live %d row %d picks" % (L, t)
+                assert np.array_equal(out[t].view(np.uint32), ref_out.view(np.uint32)), "live %d row %d" % (L, t)

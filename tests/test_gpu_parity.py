@@ -514,3 +514,22 @@ def test_padded_bucket_graph_replay_at_changing_live_counts():
         _, img_o = check_producer(w_live, H.host(y_d), H.host(img_d), live=live)
         check_plan(H.host(ws), wl.ids, live, wl.E, k)
         check_routed(w_live, img_o, [H.host(o) for o in outs], live)
+
+
+@pytest.mark.parametrize("live", [512, 455])
+def test_routed_plan_at_the_pair_limit(live):
+    # bucket 512 x top-8 = 4096 pairs (the largest plan one launch takes), far past the 1,024
+    # pairs of a one-block plan; padding rows' stale ids are never planned
+    g = np.random.default_rng(live)
+    B, K, E, k = 512, 2048, 256, 8
+    x = g.standard_normal((B, K)).astype(np.float32)
+    gamma = g.normal(1.0, 0.1, K).astype(np.float32)
+    ids, w = W.topk_ids(g, B, E, k)
+    wl = W.Workload(0, "pair limit", B, K, "rmsnorm", x=x, gamma=gamma,
+                    readers=[W.q4_0_weights(g, (E, 24), K)], E=E, top_k=k, ids=ids, route_w=w, live=live)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl, live=live)
+    _, img_o = check_producer(wl, y, img, live=live)
+    outs, ws = run_routed(wl, H.dev(img), ids, live=live)
+    check_plan(ws, ids, live, E, k)
+    check_routed(wl, img_o, outs, live)
