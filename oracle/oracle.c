@@ -423,6 +423,51 @@ static double reader_row(const uint8_t* qs, const uint16_t* d, int Kb, const int
   return acc;
 }
 
+/* ------------------------------------------------------------------------------------------
+ * Other weight formats of the readers ("Share temporary Q8_1 activation images", Coverage:
+ * quantized MUL_MAT readers on MMVQ use the Q8_1 image; the image's half sums s = d * sum(c)
+ * are what a format with a per-block minimum needs):
+ *   Q8_0: block = 32 int8 codes q and fp16 d, weight = d * q.
+ *         term_b = d_w * d_a * sum_j q_j c_j
+ *   Q4_1: block = 16 bytes of nibbles (ggml order, as Q4_0), fp16 d and fp16 m,
+ *         weight = d * q + m (q in 0..15).
+ *         term_b = d_w * d_a * sum_j q_j c_j + m_w * s_a     (s_a = the image's stored sum)
+ * out[t][n] = sum_b term_b in float64, ascending b. qs layouts: Q8_0 [N][K/32][32] int8,
+ * Q4_1 [N][K/32][16]; d (and m) fp16 [N][K/32].
+ * ---------------------------------------------------------------------------------------- */
+static int32_t block_dot_q8(const int8_t* q, const int8_t* c) {
+  int32_t s = 0;
+  for (int j = 0; j < 32; ++j) s += (int32_t)q[j] * c[j];
+  return s;
+}
+
+void orc_mmvq_fmt(int fmt, const uint8_t* qs, const uint16_t* d, const uint16_t* m, int N, int K,
+                  const uint8_t* img, int img_rows, int rows, double* out) {
+  int Kb = K / 32, RB = orc_row_blocks(K);
+  const int8_t* codes = (const int8_t*)img;
+  const uint32_t* ds = (const uint32_t*)(img + (size_t)img_rows * RB * 32);
+  for (int t = 0; t < rows; ++t)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int b = 0; b < Kb; ++b) {
+        const int8_t* c = codes + ((size_t)t * RB + b) * 32;
+        uint32_t w = ds[(size_t)t * RB + b];
+        double da = orc_f16_to_f64((uint16_t)(w & 0xffffu));
+        double sa = orc_f16_to_f64((uint16_t)(w >> 16));
+        double dw = orc_f16_to_f64(d[(size_t)n * Kb + b]);
+        if (fmt == 1) { /* Q8_0 */
+          int32_t s = block_dot_q8((const int8_t*)qs + ((size_t)n * Kb + b) * 32, c);
+          acc += dw * da * (double)s;
+        } else { /* Q4_1 */
+          int32_t s = block_dot(qs + ((size_t)n * Kb + b) * 16, c);
+          double mw = orc_f16_to_f64(m[(size_t)n * Kb + b]);
+          acc += dw * da * (double)s + mw * sa;
+        }
+      }
+      out[(size_t)t * N + n] = acc;
+    }
+}
+
 /* Ordinary reader: out[t][n] for t < rows (the live image rows), image of img_rows rows. */
 void orc_mmvq(const uint8_t* qs, const uint16_t* d, int N, int K, const uint8_t* img, int img_rows,
               int rows, double* out) {

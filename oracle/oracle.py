@@ -57,6 +57,7 @@ def lib():
             "orc_mmvq_id_per_slot": (None, [P, P, i32, i32, i32, P, i32, P, i32, i32, P]),
             "orc_moe_combine": (None, [P, i64, P, P, i32, i32, i32, i32, P, i64]),
             "orc_moe_router": (None, [P, i64, P, i32, i32, i32, P, i64]),
+            "orc_mmvq_fmt": (None, [i32, P, P, P, i32, i32, P, i32, i32, P]),
             "orc_moe_topk": (None, [P, i64, i32, i32, i32, P, P]),
             "orc_quant_recip_array": (None, [P, P, i64]),
             "orc_quant_scale_array": (None, [P, P, i64]),
@@ -291,6 +292,24 @@ def mmvq(qs: np.ndarray, d16: np.ndarray, K: int, img: np.ndarray, img_rows: int
     out = np.empty((rows, N), dtype=np.float64)
     img = np.ascontiguousarray(img, dtype=np.uint8)
     lib().orc_mmvq(_p(qs), _p(d16), N, K, _p(img), img_rows, rows, _p(out))
+    return out
+
+
+WEIGHT_FMTS = {"q8_0": 1, "q4_1": 2}
+
+
+def mmvq_fmt(fmt: str, qs: np.ndarray, d16: np.ndarray, m16, K: int, img: np.ndarray, img_rows: int,
+             rows: int) -> np.ndarray:
+    """orc_mmvq_fmt: float64 out [rows][N] of one ordinary Q8_0 or Q4_1 reader."""
+    qs = np.ascontiguousarray(qs).view(np.uint8)
+    d16 = np.ascontiguousarray(d16, dtype=np.uint16)
+    m = None if m16 is None else np.ascontiguousarray(m16, dtype=np.uint16)
+    Kb = K // 32
+    N = d16.size // Kb
+    out = np.empty((rows, N), dtype=np.float64)
+    img = np.ascontiguousarray(img, dtype=np.uint8)
+    lib().orc_mmvq_fmt(WEIGHT_FMTS[fmt], _p(qs), _p(d16), None if m is None else _p(m), N, K, _p(img),
+                       img_rows, rows, _p(out))
     return out
 
 

@@ -45,13 +45,16 @@ def rng(config: int, tensor_id: int) -> np.random.Generator:
 
 @dataclass
 class Q4Weights:
-    """Q4_0 weights: qs uint8 [..., N, K/32, 16], d uint16 (fp16 bits) [..., N, K/32]."""
+    """Block-quantized weights. fmt "q4_0": qs uint8 [..., N, K/32, 16], d uint16 (fp16 bits)
+    [..., N, K/32]; "q8_0": qs int8 [..., N, K/32, 32], d; "q4_1": qs as q4_0, d and m."""
     qs: np.ndarray
     d: np.ndarray
+    fmt: str = "q4_0"
+    m: np.ndarray | None = None
 
     @property
     def nbytes(self) -> int:
-        return self.qs.nbytes + self.d.nbytes
+        return self.qs.nbytes + self.d.nbytes + (0 if self.m is None else self.m.nbytes)
 
 
 def q4_0_weights(g: np.random.Generator, shape_rows: tuple, K: int) -> Q4Weights:
@@ -60,6 +63,27 @@ def q4_0_weights(g: np.random.Generator, shape_rows: tuple, K: int) -> Q4Weights
     qs = g.integers(0, 256, size=(*shape_rows, Kb, 16), dtype=np.uint8)
     scales = g.uniform(1e-3, 1e-2, size=(*shape_rows, Kb)).astype(np.float16)
     return Q4Weights(qs=qs, d=scales.view(np.uint16))
+
+
+def q8_0_weights(g: np.random.Generator, shape_rows: tuple, K: int) -> Q4Weights:
+    """Q8_0: codes uniform on -127..127, fp16 scales uniform on [1e-4, 1e-3] (weights of the
+    same spread as the Q4_0 ones)."""
+    Kb = K // 32
+    qs = g.integers(-127, 128, size=(*shape_rows, Kb, 32), dtype=np.int8)
+    scales = g.uniform(1e-4, 1e-3, size=(*shape_rows, Kb)).astype(np.float16)
+    return Q4Weights(qs=qs, d=scales.view(np.uint16), fmt="q8_0")
+
+
+def q4_1_weights(g: np.random.Generator, shape_rows: tuple, K: int) -> Q4Weights:
+    """Q4_1: codes uniform on 0..15, fp16 d uniform on [1e-3, 1e-2], fp16 m = -8 d (1 + u),
+    u uniform on [-0.1, 0.1] (block minima near the Q4_0 offset)."""
+    w = q4_0_weights(g, shape_rows, K)
+    d = w.d.view(np.float16).astype(np.float64)
+    m = (-8.0 * d * (1.0 + g.uniform(-0.1, 0.1, size=d.shape))).astype(np.float16)
+    return Q4Weights(qs=w.qs, d=w.d, fmt="q4_1", m=m.view(np.uint16))
+
+
+WEIGHT_MAKERS = {"q4_0": q4_0_weights, "q8_0": q8_0_weights, "q4_1": q4_1_weights}
 
 
 def topk_ids(g: np.random.Generator, rows: int, E: int, k: int):
@@ -106,11 +130,17 @@ class Workload:
 
 
 def make(config: int, *, live: int | None = None, glu_op: str = "swiglu", small: bool = False,
-         moe: bool = False) -> Workload:
+         moe: bool = False, wfmt: str = "q4_0") -> Workload:
     """Build workload `config` (1..5). `small=True` shrinks the weight row counts (not K or T)
     so the CPU oracle can check every output of a GPU run in well under a second. `moe=True`
     (workloads 4 and 5) adds the down projection and the MoE stage inputs."""
     wl = _make(config, live, glu_op, small, moe)
+    if wfmt != "q4_0":  # ordinary readers in another weight format (same seeds, same shapes)
+        if wl.routed:
+            raise ValueError("other weight formats are built for the ordinary readers")
+        wl.readers = [WEIGHT_MAKERS[wfmt](rng(config, T_READER0 + r), (w.d.shape[-2],), wl.K)
+                      for r, w in enumerate(wl.readers)]
+        wl.name += " " + wfmt
     if moe:
         if not wl.routed:
             raise ValueError("the MoE extension needs a routed workload (4 or 5)")

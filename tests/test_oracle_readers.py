@@ -299,3 +299,46 @@ def test_topk_against_stable_sort_and_softmax():
     assert np.array_equal(ids_all, np.argsort(-logits[:2], axis=1, kind="stable"))
     # live rows only
     assert O.moe_topk(logits, k, live=5)[0].shape == (5, k)
+
+
+# ---- other weight formats (Q8_0, Q4_1) --------------------------------------------------------
+def test_q8_0_reader_is_the_dequantized_dot():
+    g = np.random.default_rng(51)
+    N, K, T = 5, 160, 3
+    w = W.q8_0_weights(g, (N,), K)
+    y, img = _random_image(g, T, K)
+    out = O.mmvq_fmt("q8_0", w.qs, w.d, None, K, img, T, T)
+    codes, d16, s16 = O.image_planes(img, T, K)
+    Kb = K // 32
+    wd = w.qs.astype(np.float64) * _f16(w.d)[..., None]                       # [N][Kb][32]
+    ad = codes[:, :Kb].astype(np.float64) * _f16(d16[:, :Kb])[..., None]    # [T][Kb][32]
+    ref = np.einsum("nbj,tbj->tn", wd, ad)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_q4_1_reader_is_the_dequantized_dot_up_to_the_stored_sum():
+    g = np.random.default_rng(52)
+    N, K, T = 6, 96, 4
+    w = W.q4_1_weights(g, (N,), K)
+    y, img = _random_image(g, T, K)
+    out = O.mmvq_fmt("q4_1", w.qs, w.d, w.m, K, img, T, T)
+    codes, d16, s16 = O.image_planes(img, T, K)
+    Kb = K // 32
+    wd = _unpack_weights(w.qs).astype(np.float64) * _f16(w.d)[..., None] + _f16(w.m)[..., None]
+    ad = codes[:, :Kb].astype(np.float64) * _f16(d16[:, :Kb])[..., None]
+    bf = np.einsum("nbj,tbj->tn", wd, ad)
+    # the stored half sum replaces d_a * sum(c): out - bf = sum_b m_w (s16 - d16 sum c)
+    diff = _f16(s16[:, :Kb]) - _f16(d16[:, :Kb]) * codes[:, :Kb].astype(np.float64).sum(-1)
+    assert np.allclose(out - bf, diff @ _f16(w.m).T, rtol=1e-9, atol=1e-14)
+
+
+def test_q4_1_with_minimum_minus_8d_is_q4_0():
+    # m = -8 d (exact in fp16) turns Q4_1's d q + m into Q4_0's d (q - 8)
+    g = np.random.default_rng(53)
+    N, K, T = 7, 256, 3
+    w = W.q4_0_weights(g, (N,), K)
+    m = (-8.0 * w.d.view(np.float16).astype(np.float32)).astype(np.float16).view(np.uint16)
+    y, img = _random_image(g, T, K)
+    q41 = O.mmvq_fmt("q4_1", w.qs, w.d, m, K, img, T, T)
+    q40 = O.mmvq(w.qs, w.d, K, img, T, T)
+    assert np.allclose(q41, q40, rtol=1e-13, atol=1e-16)
