@@ -58,7 +58,9 @@ class Instance:
         for r in wl.readers:
             N = r.d.shape[-2]
             out = torch.empty(*((T, wl.top_k, N) if wl.routed else (T, N)), dtype=torch.float32, device="cuda")
-            self.specs.append((qimg.tile_q4_0(dev(r.qs), dev(r.d), K), N, out))
+            tiles = qimg.tile_weights(dev(r.qs.view(np.uint8)), dev(r.d), K, fmt=r.fmt,
+                                      w_m=None if r.m is None else dev(r.m))
+            self.specs.append((tiles, N, out))
         if wl.routed:
             self.ids = dev(wl.ids)
             self.ws = torch.empty(qimg.workspace_bytes(T, wl.top_k, wl.E) // 4, dtype=torch.int32, device="cuda")
@@ -85,7 +87,7 @@ class Instance:
         if wl.routed:
             qimg.mmvq_id(self.specs, wl.E, self.img, self.ids, self.live, wl.K, self.ws)
         else:
-            qimg.mmvq(self.specs, self.img, wl.T, wl.K)
+            qimg.mmvq(self.specs, self.img, wl.T, wl.K, fmt=wl.readers[0].fmt)
 
     def step(self, arm="fused"):
         if arm == "fused":
@@ -113,7 +115,8 @@ def algorithmic_bytes(wl):
         out = sum(L * wl.top_k * r.d.shape[-2] * 4 for r in wl.readers)
         ids = L * wl.top_k * 4
     else:
-        w = sum(r.d.shape[-2] * Kb * 18 for r in wl.readers)
+        per_block = {"q4_0": 18, "q8_0": 34, "q4_1": 20}
+        w = sum(r.d.shape[-2] * Kb * per_block[r.fmt] for r in wl.readers)
         out = sum(L * r.d.shape[-2] * 4 for r in wl.readers)
         ids = 0
     return {"producer": prod, "image_write": img, "image_read": img, "weights": w, "outputs": out,
@@ -307,8 +310,10 @@ def cpu_baseline(wl, budget_s=20.0):
             if wl.routed:
                 O.plan(wl.ids, L, wl.E)
                 O.mmvq_id(r.qs, r.d, wl.E, K, img, T, wl.ids, L)
-            else:
+            elif r.fmt == "q4_0":
                 O.mmvq(r.qs, r.d, K, img, T, L)
+            else:
+                O.mmvq_fmt(r.fmt, r.qs, r.d, r.m, K, img, T, L)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() + times[-1] > t_end or len(times) >= 5:
             break
@@ -344,10 +349,11 @@ WORKLOAD_NAMES = {
 }
 
 
-def run(config, steps, warmup, live=None, glu_op="swiglu", want_cpu=True, arms=("fused", "control")):
+def run(config, steps, warmup, live=None, glu_op="swiglu", want_cpu=True, arms=("fused", "control"),
+        wfmt="q4_0"):
     torch = _t()
     from q8_activation_quant_amd import workloads as W
-    wl = W.make(config, live=live, glu_op=glu_op)
+    wl = W.make(config, live=live, glu_op=glu_op, wfmt=wfmt)
     insts = make_instances(wl)
     nb = algorithmic_bytes(wl)
     per_arm = {}
@@ -382,6 +388,8 @@ def main():
                                                         "swiglu_oai", "swiglu_clamp"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print one extra line per workload")
+    ap.add_argument("--wfmt", default="q4_0", choices=["q4_0", "q8_0", "q4_1"],
+                    help="weight format of the ordinary readers")
     ap.add_argument("--moe", action="store_true",
                     help="time the whole routed MoE FFN of workload 4 (or 5 with --config 5) instead")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -440,7 +448,8 @@ def main():
                           "reader_algorithmic_bytes": algorithmic_bytes(wl)["reader_kernel"],
                           "calibration_copy_bytes": src.numel()}), flush=True)
         return
-    r = run(args.config, args.steps, args.warmup, live=args.live, glu_op=args.glu, want_cpu=not args.no_cpu)
+    r = run(args.config, args.steps, args.warmup, live=args.live, glu_op=args.glu, want_cpu=not args.no_cpu,
+            wfmt=args.wfmt)
     wl, nb = r["wl"], r["bytes"]
     us = r["us"]["fused"]
     reader_gbs = nb["reader_kernel"] / (r["reader_us"] * 1e-6) / 1e9
@@ -459,7 +468,8 @@ def main():
         "dtype": "int8xu4->int32 dots, f32 producer and accumulation",
         "data": "synthetic (seeded numpy PCG64; shapes/distributions of the workload)",
         "config": {"workload": WORKLOAD_NAMES[args.config] + ("" if wl.producer in ("rmsnorm", "swiglu")
-                                                              else " (producer %s)" % wl.producer),
+                                                              else " (producer %s)" % wl.producer)
+                               + ("" if args.wfmt == "q4_0" else " (weights %s)" % args.wfmt),
                    "T": wl.T, "K": wl.K,
                    "readers_N": wl.reader_rows, "producer": wl.producer, "arm": "fused",
                    "graph_instances": r["R"], "live_rows": wl.live},
@@ -472,7 +482,7 @@ def main():
         "producer_us": round(r["producer_us"], 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "mmvq_tiled_kernel (Q4_0 x Q8_1 readers)",
+            "kernel": "mmvq_tiled_kernel (%s x Q8_1 readers)" % args.wfmt.upper(),
             "achieved": round(reader_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

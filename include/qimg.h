@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 7
+#define QIMG_ABI_VERSION 8
 
 /* status codes */
 #define QIMG_OK 0
@@ -310,6 +310,32 @@ int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int3
 int qimg_moe_topk(const float* logits, int64_t ldl, int32_t E, int32_t bucket,
                   const int32_t* live_rows, int32_t top_k, int32_t* ids, float* weights,
                   void* stream);
+
+/*
+ * Other weight formats of the ordinary readers ([P1] Coverage: quantized MUL_MAT on the MMVQ
+ * path reads the shared Q8_1 image; the image's half sums carry a format's block minimum).
+ *   Q8_0 standard planes: qs int8 [E][N][K/32][32], d fp16 [E][N][K/32]; weight = d * q.
+ *     Reader: out[t][n] = sum_b d_w d_a sum_j q_j c_j.
+ *     Tiles: chunk c holds 2 KB of codes (the first 16 bytes of each lane's block, then the
+ *     second 16) instead of 1 KB; fp16 scales after all codes as for Q4_0.
+ *   Q4_1 standard planes: qs [E][N][K/32][16] (Q4_0's nibble order), d and m fp16;
+ *     weight = d * q + m (q in 0..15).
+ *     Reader: out[t][n] = sum_b (d_w d_a sum_j q_j c_j + m_w s_a), s_a the image's stored sum.
+ *     Tiles: codes as Q4_0; then the 32-bit words d | m << 16 after all codes.
+ * The readers take the same arguments, errors and aliasing rules as mmvq_q4_0_q8_1, with
+ * qimg_reader.w pointing at tiles of the matching format; every reader of one call has that
+ * format. Accuracy: as mmvq_q4_0_q8_1 (float sums of exact per-block integer dots).
+ */
+int64_t qimg_q8_0_tiled_bytes(int32_t N, int32_t K, int32_t E);
+int64_t qimg_q4_1_tiled_bytes(int32_t N, int32_t K, int32_t E);
+int qimg_q8_0_tile(const void* qs, const void* d, int32_t N, int32_t K, int32_t E, void* tiled,
+                   void* stream);
+int qimg_q4_1_tile(const void* qs, const void* d, const void* m, int32_t N, int32_t K, int32_t E,
+                   void* tiled, void* stream);
+int mmvq_q8_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                   int32_t rows, const int32_t* live_rows, int32_t K, void* stream);
+int mmvq_q4_1_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                   int32_t rows, const int32_t* live_rows, int32_t K, void* stream);
 
 /*
  * Debug export of the per-block integer dot products of one ordinary reader, computed by the

@@ -13,10 +13,11 @@
 //                            32-block Q8_1 quantization, all in one pass over the row.
 //   mmvq_tiled_kernel<N,M,G> ordinary Q4_0 x Q8_1 readers on the matrix cores
 //                            (v_mfma_i32_16x16x64_i8) over tiled weights, the live image rows as
-//                            columns; M = 2: block-dot export.
+//                            columns; M = 2: block-dot export; M = 3, 4: Q8_0, Q4_1 weights.
 //   mmvq_routed_kernel<N,U>  routed readers: the plan of the live pairs built in LDS by every
 //                            workgroup, then (expert, pass, tile) units streamed over full K.
-//   tile_q4_0_kernel         one-time reordering of standard Q4_0 planes into reader tiles.
+//   tile_weights_kernel<F>   one-time reordering of standard Q4_0 / Q8_0 / Q4_1 planes into
+//                            reader tiles.
 //
 // Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off (no fast-math), so every float
 // operation written here is one IEEE binary32 operation with round-to-nearest-even; f32
@@ -836,9 +837,14 @@ constexpr int ring_depth(int ntm) {
 
 // MODE: 0 ordinary readers, 2 block-dot export. NTG: token groups of 4 image columns per pass
 // (1 when a pass has at most 4 columns).
+// MODE: 0 Q4_0 readers, 2 Q4_0 block-dot export, 3 Q8_0 readers, 4 Q4_1 readers.
 template <int NTM, int MODE, int NTG>
 __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   constexpr bool DOTS = MODE == 2;
+  constexpr int FMT = MODE == 3 ? 1 : MODE == 4 ? 2 : 0;    // weight format: Q4_0, Q8_0, Q4_1
+  constexpr uint32_t kCodeBytes = FMT == 1 ? 2048u : 1024u;  // codes per chunk
+  constexpr uint32_t kScaleBytes = FMT == 2 ? 256u : 128u;   // scales (Q4_1: d | m) per chunk
+  constexpr int kLoads = FMT == 1 ? 3 : 2;                   // loads per chunk and tile
   extern __shared__ __align__(16) unsigned char smem[];
   // weight loads in flight per wave: a ring of D slots, each one chunk of NTM tiles
   constexpr int D = ring_depth(NTM);
@@ -896,12 +902,12 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
         rl[t] = lt * 16 + n;  // this lane's weight row in reader ri
         const uint32_t chunk0 = (uint32_t)lt * (uint32_t)KC;
         const uint32_t chunks = (uint32_t)p.r[ri].tiles * (uint32_t)KC;
-        rq[t] = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].qs, (short)0, (int)(chunks * 1024u),
+        rq[t] = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].qs, (short)0, (int)(chunks * kCodeBytes),
                                                   kBufferFlags);
-        rd[t] = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].d, (short)0, (int)(chunks * 128u),
+        rd[t] = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].d, (short)0, (int)(chunks * kScaleBytes),
                                                   kBufferFlags);
-        oq[t] = chunk0 * 1024u;
-        od[t] = chunk0 * 128u;
+        oq[t] = chunk0 * kCodeBytes;
+        od[t] = chunk0 * kScaleBytes;
       }
       float acc[NTM][8];
 #pragma unroll
@@ -909,7 +915,7 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[t][v] = 0.0f;
 
-      uint4 q[D][NTM];
+      uint4 q[D][NTM], q2[FMT == 1 ? D : 1][NTM];  // q2: Q8_0's second 16 bytes per block
       uint32_t dsc[D][NTM];
       // chunks of this wave: with kInterleave, w, w + 8, w + 16, ... (the workgroup's waves
       // read 8 consecutive chunks of a tile at each step); otherwise the range [cs0, cs1)
@@ -919,14 +925,21 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       // value alive and defeat the exact wait counts); a slot past the wave's last chunk
       // repeats that chunk (its lines are in flight or cached), never used. The chunk part of
       // the address is the same in every lane.
-      const uint32_t lq = 16u * lane, ld2 = 2u * lane;
+      const uint32_t lq = 16u * lane, ld2 = 2u * lane, ld4 = 4u * lane;
       auto load = [&](int j, int st) {
         const uint32_t cs = (uint32_t)chunk_of(st < nst ? st : nst - 1);
 #pragma unroll
         for (int t = 0; t < NTM; ++t) {
-          const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq, oq[t] + cs * 1024u, 0);
+          const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq, oq[t] + cs * kCodeBytes, 0);
           q[j][t] = make_uint4(x.x, x.y, x.z, x.w);
-          dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b16(rd[t], ld2, od[t] + cs * 128u, 0);
+          if constexpr (FMT == 1) {
+            const v4u x2 = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq, oq[t] + cs * kCodeBytes + 1024u, 0);
+            q2[j][t] = make_uint4(x2.x, x2.y, x2.z, x2.w);
+          }
+          if constexpr (FMT == 2)
+            dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b32(rd[t], ld4, od[t] + cs * kScaleBytes, 0);
+          else
+            dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b16(rd[t], ld2, od[t] + cs * kScaleBytes, 0);
         }
       };
       // One chunk of NTM tiles: all matrix-core products first (for every tile slot; an idle
@@ -934,18 +947,26 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       // VALU instruction waits on a product issued just before it.
       auto compute = [&](int j, int cs) {
         v4i blo[NTM], bhi[NTM];
-        float dw[NTM];
+        float dw[NTM], mw[NTM];
 #pragma unroll
         for (int t = 0; t < NTM; ++t) {
-          blo[t][0] = (int)(q[j][t].x & 0x0f0f0f0fu);
-          blo[t][1] = (int)(q[j][t].y & 0x0f0f0f0fu);
-          blo[t][2] = (int)(q[j][t].z & 0x0f0f0f0fu);
-          blo[t][3] = (int)(q[j][t].w & 0x0f0f0f0fu);
-          bhi[t][0] = (int)((q[j][t].x >> 4) & 0x0f0f0f0fu);
-          bhi[t][1] = (int)((q[j][t].y >> 4) & 0x0f0f0f0fu);
-          bhi[t][2] = (int)((q[j][t].z >> 4) & 0x0f0f0f0fu);
-          bhi[t][3] = (int)((q[j][t].w >> 4) & 0x0f0f0f0fu);
+          if constexpr (FMT == 1) {  // Q8_0: elements 0..15 and 16..31 are the two 16-byte halves
+            blo[t][0] = (int)q[j][t].x; blo[t][1] = (int)q[j][t].y;
+            blo[t][2] = (int)q[j][t].z; blo[t][3] = (int)q[j][t].w;
+            bhi[t][0] = (int)q2[j][t].x; bhi[t][1] = (int)q2[j][t].y;
+            bhi[t][2] = (int)q2[j][t].z; bhi[t][3] = (int)q2[j][t].w;
+          } else {
+            blo[t][0] = (int)(q[j][t].x & 0x0f0f0f0fu);
+            blo[t][1] = (int)(q[j][t].y & 0x0f0f0f0fu);
+            blo[t][2] = (int)(q[j][t].z & 0x0f0f0f0fu);
+            blo[t][3] = (int)(q[j][t].w & 0x0f0f0f0fu);
+            bhi[t][0] = (int)((q[j][t].x >> 4) & 0x0f0f0f0fu);
+            bhi[t][1] = (int)((q[j][t].y >> 4) & 0x0f0f0f0fu);
+            bhi[t][2] = (int)((q[j][t].z >> 4) & 0x0f0f0f0fu);
+            bhi[t][3] = (int)((q[j][t].w >> 4) & 0x0f0f0f0fu);
+          }
           dw[t] = h2f(dsc[j][t]);
+          mw[t] = FMT == 2 ? h2f(dsc[j][t] >> 16) : 0.0f;
         }
         const int blk = 4 * cs + g;  // this lane's block
         const unsigned char* dam = smem + dam_base + cs * dam_step;
@@ -981,11 +1002,21 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
                       p.sumi[((int64_t)col * p.r[0].N + rl[t]) * p.Kb + blk] = d[v];
                   }
                 }
-              } else {
+              } else if constexpr (FMT == 0) {  // d_w (d_a sumi - 8 s_a)
                 acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.x, (float)d[0], ms4.x), acc[t][4 * tg + 0]);
                 acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.y, (float)d[1], ms4.y), acc[t][4 * tg + 1]);
                 acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.z, (float)d[2], ms4.z), acc[t][4 * tg + 2]);
                 acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.w, (float)d[3], ms4.w), acc[t][4 * tg + 3]);
+              } else if constexpr (FMT == 1) {  // d_w d_a sumi
+                acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], da4.x * (float)d[0], acc[t][4 * tg + 0]);
+                acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], da4.y * (float)d[1], acc[t][4 * tg + 1]);
+                acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], da4.z * (float)d[2], acc[t][4 * tg + 2]);
+                acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], da4.w * (float)d[3], acc[t][4 * tg + 3]);
+              } else {  // d_w d_a sumi + m_w s_a, s_a = -(-8 s_a) / 8 (exact)
+                acc[t][4 * tg + 0] = __builtin_fmaf(mw[t], -0.125f * ms4.x, __builtin_fmaf(dw[t], da4.x * (float)d[0], acc[t][4 * tg + 0]));
+                acc[t][4 * tg + 1] = __builtin_fmaf(mw[t], -0.125f * ms4.y, __builtin_fmaf(dw[t], da4.y * (float)d[1], acc[t][4 * tg + 1]));
+                acc[t][4 * tg + 2] = __builtin_fmaf(mw[t], -0.125f * ms4.z, __builtin_fmaf(dw[t], da4.z * (float)d[2], acc[t][4 * tg + 2]));
+                acc[t][4 * tg + 3] = __builtin_fmaf(mw[t], -0.125f * ms4.w, __builtin_fmaf(dw[t], da4.w * (float)d[3], acc[t][4 * tg + 3]));
               }
             }
           }
@@ -1001,7 +1032,7 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       if (nst > 0) {
 #pragma unroll
         for (int j = 0; j < D - 1; ++j) load(j, j);
-        if (stage) wait_vmcnt<(D - 1) * NTM * 2>();
+        if (stage) wait_vmcnt<(D - 1) * NTM * kLoads>();
       } else if (stage) {
         wait_vmcnt<0>();
       }
@@ -1517,11 +1548,15 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   }
 }
 
-// Standard Q4_0 planes -> tiled order (see the reader notes above). Rows and blocks past N and
-// K/32 are written as zeros, so tiles and chunks are always whole.
-__global__ void tile_q4_0_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
-                                 int N, int Kb, int KC, int tiles, int E,
-                                 uint8_t* __restrict__ tq, uint16_t* __restrict__ td) {
+// Standard planes -> tiled order (see the reader notes above). Rows and blocks past N and
+// K/32 are written as zeros, so tiles and chunks are always whole. FMT 0 Q4_0 and 2 Q4_1:
+// 1 KB of codes per chunk (lane l: the 16 bytes of block 4 s + l/16 of row l%16); Q8_0:
+// 2 KB, the first 16 bytes of every lane's block, then the second 16. Scales after all codes:
+// fp16 d (Q4_0, Q8_0) or the 32-bit word d | m << 16 (Q4_1), lane order.
+template <int FMT>
+__global__ void tile_weights_kernel(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
+                                    const uint16_t* __restrict__ m, int N, int Kb, int KC, int tiles,
+                                    int E, uint8_t* __restrict__ tq, uint8_t* __restrict__ tsc) {
   const int64_t total = (int64_t)E * tiles * KC * 64;
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (int64_t)gridDim.x * blockDim.x) {
@@ -1533,15 +1568,23 @@ __global__ void tile_q4_0_kernel(const uint8_t* __restrict__ qs, const uint16_t*
     const int64_t e = et / tiles;
     const int row = tile * 16 + (lane & 15);
     const int blk = 4 * s + (lane >> 4);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    uint16_t dv = 0;
-    if (row < N && blk < Kb) {
-      const int64_t src = (e * N + row) * Kb + blk;
-      v = reinterpret_cast<const uint4*>(qs)[src];
-      dv = d[src];
+    const bool in = row < N && blk < Kb;
+    const int64_t src = (e * N + row) * Kb + blk;
+    if constexpr (FMT == 1) {
+      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+      if (in) {
+        v0 = reinterpret_cast<const uint4*>(qs)[2 * src];
+        v1 = reinterpret_cast<const uint4*>(qs)[2 * src + 1];
+      }
+      reinterpret_cast<uint4*>(tq)[(2 * c) * 64 + lane] = v0;
+      reinterpret_cast<uint4*>(tq)[(2 * c + 1) * 64 + lane] = v1;
+    } else {
+      reinterpret_cast<uint4*>(tq)[o] = in ? reinterpret_cast<const uint4*>(qs)[src] : make_uint4(0, 0, 0, 0);
     }
-    reinterpret_cast<uint4*>(tq)[o] = v;
-    td[o] = dv;
+    if constexpr (FMT == 2)
+      reinterpret_cast<uint32_t*>(tsc)[o] = in ? ((uint32_t)d[src] | ((uint32_t)m[src] << 16)) : 0u;
+    else
+      reinterpret_cast<uint16_t*>(tsc)[o] = in ? d[src] : (uint16_t)0;
   }
 }
 
@@ -1889,29 +1932,57 @@ int qimg_quantize_q8_1(const float* y, int64_t ldy, int32_t rows, const int32_t*
 }
 
 
-int64_t qimg_q4_0_tiled_bytes(int32_t N, int32_t K, int32_t E) {
+static int64_t tiled_bytes_fmt(int fmt, int32_t N, int32_t K, int32_t E) {
   if (N <= 0 || E <= 0 || check_k(K) != QIMG_OK) return 0;
-  return tiled_chunks(N, K, E) * (1024 + 128);
+  return tiled_chunks(N, K, E) * (fmt == 1 ? 2048 + 128 : fmt == 2 ? 1024 + 256 : 1024 + 128);
 }
 
-int qimg_q4_0_tile(const void* qs, const void* d, int32_t N, int32_t K, int32_t E, void* tiled,
-                   void* stream) {
+static int tile_common(int fmt, const void* qs, const void* d, const void* m, int32_t N, int32_t K,
+                       int32_t E, void* tiled, void* stream) {
   int st = check_k(K);
   if (st) return st;
-  if (!qs || !d || !tiled || N <= 0 || E <= 0) return QIMG_EINVAL;
-  if (!al16(qs) || !al(d, 2) || !al16(tiled)) return QIMG_EALIGN;
+  if (!qs || !d || (fmt == 2 && !m) || !tiled || N <= 0 || E <= 0) return QIMG_EINVAL;
+  if (!al16(qs) || !al(d, 2) || (m && !al(m, 2)) || !al16(tiled)) return QIMG_EALIGN;
   const int Kb = K / 32;
   const int64_t chunks = tiled_chunks(N, K, E);
-  const Span so = span(tiled, chunks * 1152);
-  if (overlap(so, span(qs, (int64_t)E * N * Kb * 16)) || overlap(so, span(d, (int64_t)E * N * Kb * 2)))
+  const int64_t cbytes = fmt == 1 ? 2048 : 1024;
+  const Span so = span(tiled, tiled_bytes_fmt(fmt, N, K, E));
+  const int64_t blocks_in = (int64_t)E * N * Kb;
+  if (overlap(so, span(qs, blocks_in * (fmt == 1 ? 32 : 16))) || overlap(so, span(d, blocks_in * 2)) ||
+      (m && overlap(so, span(m, blocks_in * 2))))
     return QIMG_EALIAS;
   const int64_t total = chunks * 64;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(tile_q4_0_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                     (const uint8_t*)qs, (const uint16_t*)d, N, Kb, (Kb + 3) / 4, (N + 15) / 16, E,
-                     (uint8_t*)tiled, (uint16_t*)((uint8_t*)tiled + chunks * 1024));
+  const int KC = (Kb + 3) / 4, tiles = (N + 15) / 16;
+  uint8_t* tq = (uint8_t*)tiled;
+  uint8_t* tsc = tq + chunks * cbytes;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 g((unsigned)blocks), b(256);
+  if (fmt == 1)
+    hipLaunchKernelGGL(tile_weights_kernel<1>, g, b, 0, s, (const uint8_t*)qs, (const uint16_t*)d, nullptr, N, Kb, KC, tiles, E, tq, tsc);
+  else if (fmt == 2)
+    hipLaunchKernelGGL(tile_weights_kernel<2>, g, b, 0, s, (const uint8_t*)qs, (const uint16_t*)d, (const uint16_t*)m, N, Kb, KC, tiles, E, tq, tsc);
+  else
+    hipLaunchKernelGGL(tile_weights_kernel<0>, g, b, 0, s, (const uint8_t*)qs, (const uint16_t*)d, nullptr, N, Kb, KC, tiles, E, tq, tsc);
   return launch_status();
+}
+
+int64_t qimg_q4_0_tiled_bytes(int32_t N, int32_t K, int32_t E) { return tiled_bytes_fmt(0, N, K, E); }
+int64_t qimg_q8_0_tiled_bytes(int32_t N, int32_t K, int32_t E) { return tiled_bytes_fmt(1, N, K, E); }
+int64_t qimg_q4_1_tiled_bytes(int32_t N, int32_t K, int32_t E) { return tiled_bytes_fmt(2, N, K, E); }
+
+int qimg_q4_0_tile(const void* qs, const void* d, int32_t N, int32_t K, int32_t E, void* tiled,
+                   void* stream) {
+  return tile_common(0, qs, d, nullptr, N, K, E, tiled, stream);
+}
+int qimg_q8_0_tile(const void* qs, const void* d, int32_t N, int32_t K, int32_t E, void* tiled,
+                   void* stream) {
+  return tile_common(1, qs, d, nullptr, N, K, E, tiled, stream);
+}
+int qimg_q4_1_tile(const void* qs, const void* d, const void* m, int32_t N, int32_t K, int32_t E,
+                   void* tiled, void* stream) {
+  return tile_common(2, qs, d, m, N, K, E, tiled, stream);
 }
 
 static int check_image(const void* img) {
@@ -1930,8 +2001,9 @@ static void fill_common(ReadArgs& a, const void* img, int32_t rows, int32_t K) {
   a.rows = rows;
 }
 
-int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
-                   int32_t rows, const int32_t* live_rows, int32_t K, void* stream) {
+static int ordinary_common(int fmt, const qimg_q4_0_reader* readers, int32_t n_readers,
+                           const void* img, int32_t rows, const int32_t* live_rows, int32_t K,
+                           void* stream) {
   int st = check_k(K);
   if (st) return st;
   if (!readers || n_readers < 1 || n_readers > QIMG_MAX_READERS || rows < 0) return QIMG_EINVAL;
@@ -1947,7 +2019,7 @@ int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const voi
     if (!al16(r.w) || !al(r.out, 4)) return QIMG_EALIGN;
     outs[i] = span(r.out, rows_extent(rows, r.ldo, r.N, 4));
     for (int j = 0; j < n_readers; ++j)
-      if (overlap(outs[i], span(readers[j].w, qimg_q4_0_tiled_bytes(readers[j].N, K, 1))))
+      if (overlap(outs[i], span(readers[j].w, tiled_bytes_fmt(fmt, readers[j].N, K, 1))))
         return QIMG_EALIAS;
     if (overlap(outs[i], si) || overlap(outs[i], sl)) return QIMG_EALIAS;
     for (int j = 0; j < i; ++j)
@@ -1958,7 +2030,8 @@ int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const voi
   for (int i = 0; i < n_readers; ++i) {
     const qimg_q4_0_reader& r = readers[i];
     const int64_t ch = tiled_chunks(r.N, K, 1);
-    a.r[i] = ReaderDesc{(const uint8_t*)r.w, (const uint16_t*)((const uint8_t*)r.w + ch * 1024),
+    a.r[i] = ReaderDesc{(const uint8_t*)r.w,
+                        (const uint16_t*)((const uint8_t*)r.w + ch * (fmt == 1 ? 2048 : 1024)),
                         r.out, r.ldo, r.N, (r.N + 15) / 16};
     a.tile_start[i] = tiles;
     tiles += (r.N + 15) / 16;
@@ -1968,7 +2041,22 @@ int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const voi
   a.live_rows = live_rows;
   a.n_readers = n_readers;
   a.top_k = 1;
+  if (fmt == 1) return run_ordinary<3>(a, (hipStream_t)stream);
+  if (fmt == 2) return run_ordinary<4>(a, (hipStream_t)stream);
   return run_ordinary<0>(a, (hipStream_t)stream);
+}
+
+int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                   int32_t rows, const int32_t* live_rows, int32_t K, void* stream) {
+  return ordinary_common(0, readers, n_readers, img, rows, live_rows, K, stream);
+}
+int mmvq_q8_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                   int32_t rows, const int32_t* live_rows, int32_t K, void* stream) {
+  return ordinary_common(1, readers, n_readers, img, rows, live_rows, K, stream);
+}
+int mmvq_q4_1_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                   int32_t rows, const int32_t* live_rows, int32_t K, void* stream) {
+  return ordinary_common(2, readers, n_readers, img, rows, live_rows, K, stream);
 }
 
 size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E) {

@@ -19,7 +19,7 @@ GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF, "reglu": GLU_REGLU,
            "geglu_quick": GLU_GEGLU_QUICK, "swiglu_oai": GLU_SWIGLU_OAI, "swiglu_clamp": GLU_SWIGLU_CLAMP}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
@@ -28,6 +28,8 @@ EXPORTS = (
     "qimg_q4_0_tiled_bytes", "qimg_q4_0_tile", "qimg_eval_math",
     "qimg_emit_glu_per_slot", "mmvq_id_q4_0_q8_1_per_slot", "qimg_moe_combine",
     "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex", "qimg_moe_router", "qimg_moe_topk",
+    "qimg_q8_0_tiled_bytes", "qimg_q4_1_tiled_bytes", "qimg_q8_0_tile", "qimg_q4_1_tile",
+    "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1",
 )
 MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7, "reglu": 8,
             "geglu": 9, "geglu_quick": 10, "swiglu_oai_gate": 11}
@@ -83,6 +85,12 @@ def lib() -> ctypes.CDLL:
             "qimg_emit_rmsnorm_ex": (ctypes.c_int, [P, i64, P, P, f32, f32, i32, P, i32, P, i64, P, P]),
             "qimg_emit_glu_ex": (ctypes.c_int, [i32, f32, f32, P, i64, P, i64, i32, P, i32, P, i64, P, P]),
             "qimg_moe_router": (ctypes.c_int, [P, i64, P, i32, i32, P, i32, P, i64, P]),
+            "qimg_q8_0_tiled_bytes": (i64, [i32, i32, i32]),
+            "qimg_q4_1_tiled_bytes": (i64, [i32, i32, i32]),
+            "qimg_q8_0_tile": (ctypes.c_int, [P, P, i32, i32, i32, P, P]),
+            "qimg_q4_1_tile": (ctypes.c_int, [P, P, P, i32, i32, i32, P, P]),
+            "mmvq_q8_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
+            "mmvq_q4_1_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "qimg_moe_topk": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -196,11 +204,28 @@ def _readers(specs, cls):
     return arr
 
 
-def mmvq(readers, img, rows, K, live_rows=None, stream=None):
-    """Ordinary readers: readers = [(tiled weights, N, out [rows, N] f32)]."""
+def mmvq(readers, img, rows, K, live_rows=None, stream=None, fmt="q4_0"):
+    """Ordinary readers: readers = [(tiled weights of format fmt, N, out [rows, N] f32)]."""
     arr = _readers(readers, Reader)
-    _check(lib().mmvq_q4_0_q8_1(arr, len(readers), _ptr(img), rows, _ptr(live_rows), K,
-                                _stream(stream)), "mmvq_q4_0_q8_1")
+    name = {"q4_0": "mmvq_q4_0_q8_1", "q8_0": "mmvq_q8_0_q8_1", "q4_1": "mmvq_q4_1_q8_1"}[fmt]
+    _check(getattr(lib(), name)(arr, len(readers), _ptr(img), rows, _ptr(live_rows), K, _stream(stream)), name)
+
+
+def tile_weights(w_qs, w_d, K, fmt="q4_0", w_m=None, stream=None):
+    """Reorder standard planes of any reader format into its tiles (new uint8 device tensor)."""
+    import torch
+    if fmt == "q4_0":
+        return tile_q4_0(w_qs, w_d, K, stream)
+    N = w_d.shape[-2]
+    E = 1 if w_d.dim() == 2 else w_d.shape[0]
+    nbytes = int(getattr(lib(), "qimg_%s_tiled_bytes" % fmt)(N, K, E))
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w_qs.device)
+    if fmt == "q8_0":
+        _check(lib().qimg_q8_0_tile(_ptr(w_qs), _ptr(w_d), N, K, E, _ptr(out), _stream(stream)), "qimg_q8_0_tile")
+    else:
+        _check(lib().qimg_q4_1_tile(_ptr(w_qs), _ptr(w_d), _ptr(w_m), N, K, E, _ptr(out), _stream(stream)),
+               "qimg_q4_1_tile")
+    return out
 
 
 def mmvq_id(readers, E, img, ids, live_rows, K, workspace, stream=None):
