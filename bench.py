@@ -346,6 +346,7 @@ WORKLOAD_NAMES = {
     3: "GLU T8: SwiGLU over packed gate|up [8, 2x14336] -> Q8_1 image -> Q4_0 down reader N4096",
     4: "routed T8 K2560 E128 top8: RMSNorm x gamma -> image -> gate+up Q4_0 experts [128,768,2560]",
     5: "padded bucket 128 K2048 E256 top9: RMSNorm x gamma -> image -> Q4_0 experts [256,512,2048]",
+    6: "prefill T3325 K3584: RMSNorm x gamma -> Q8_1 image -> 3 Q4_0 readers N3584/512/512 (matrix-core prefill reader)",
 }
 
 
@@ -382,7 +383,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4600)
     ap.add_argument("--warmup", type=int, default=460)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--live", type=int, default=None)
     ap.add_argument("--glu", default="swiglu", choices=["swiglu", "geglu_erf", "reglu", "geglu", "geglu_quick",
                                                         "swiglu_oai", "swiglu_clamp"])
@@ -482,7 +483,8 @@ def main():
         "producer_us": round(r["producer_us"], 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "mmvq_tiled_kernel (%s x Q8_1 readers)" % args.wfmt.upper(),
+            "kernel": ("mmq_kernel (Q4_0 x Q8_1 prefill readers)" if args.config == 6 else
+                       "mmvq_tiled_kernel (%s x Q8_1 readers)" % args.wfmt.upper()),
             "achieved": round(reader_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -492,6 +494,18 @@ def main():
             "avg_launch_us": round(r["reader_us"], 3),
         },
     }
+    if args.config == 6:
+        # the prefill reader is bound by its per-block scaling on the vector ALUs: 3 operations
+        # (convert, two fused multiply-adds) per (image row, weight row, block), against the
+        # unpacked f32 vector rate of 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+        ops = 3.0 * wl.T * sum(wl.reader_rows) * (wl.K // 32)
+        peak = 256 * 4 * 16 * 2.4e9 / 1e12
+        ach = ops / (r["reader_us"] * 1e-6) / 1e12
+        line["roofline_alu"] = {"bound": "alu", "achieved": round(ach, 2), "peak": round(peak, 2),
+                                "unit": "Tops/s", "frac": round(ach / peak, 4),
+                                "ops_per_launch": ops, "avg_launch_us": round(r["reader_us"], 3),
+                                "int8_mfma_Tops": round(2.0 * wl.T * sum(wl.reader_rows) * wl.K
+                                                        / (r["reader_us"] * 1e-6) / 1e12, 1)}
     if "cpu_us" in r:
         line["cpu_baseline"] = {"value": round(r["cpu_us"], 1), "unit": "us", "cores": 1, "kind": "oracle",
                                 "sample": "%d full component graph(s) of the same workload (median)" % r["cpu_reps"]}

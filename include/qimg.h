@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 8
+#define QIMG_ABI_VERSION 9
 
 /* status codes */
 #define QIMG_OK 0
@@ -310,6 +310,17 @@ int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int3
 int qimg_moe_topk(const float* logits, int64_t ldl, int32_t E, int32_t bucket,
                   const int32_t* live_rows, int32_t top_k, int32_t* ids, float* weights,
                   void* stream);
+
+/*
+ * Prefill readers: Q4_0 x Q8_1 over many image rows (a prompt's tokens) on the matrix cores,
+ * one product per 32-value block ([P2] section 2 Principle: the activation of the q/k/v
+ * projections is quantized once and its image read by every projection). Same arguments,
+ * layouts (Q4_0 reader tiles), errors and output formula as mmvq_q4_0_q8_1; the results agree
+ * with it to the float rounding bound (the sums are ordered differently). mmvq_q4_0_q8_1 itself
+ * takes this path when rows >= 64.
+ */
+int mmq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                  int32_t rows, const int32_t* live_rows, int32_t K, void* stream);
 
 /*
  * Other weight formats of the ordinary readers ([P1] Coverage: quantized MUL_MAT on the MMVQ

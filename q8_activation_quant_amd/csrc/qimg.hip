@@ -1092,6 +1092,144 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 }
 
 // ---------------------------------------------------------------------------------------------
+// Prefill readers (many image rows: a prompt's tokens): Q4_0 x Q8_1 on v_mfma_i32_16x16x32_i8,
+// one 32-value block per product, so every block's int32 dot gets its own scales
+// ("r49 - A-quantize prepass shared-A dedup", section 2 Principle: the activation is
+// quantized once and every projection that reads it shares that one image).
+//
+// A workgroup computes 64 weight rows (4 waves, one 16-row tile each) x 64 image rows (4
+// sub-tiles of 16). Product orientation: A = weights (M = the wave's 16 rows), B = image codes
+// (N = 16 image rows), D[row 4g + v][image row] in lane (image row, g). K order inside a block:
+// lane group g takes nibble bytes 4g..4g+3 of a weight block (elements 4g..4g+3 in the low
+// nibbles, 16+4g..16+4g+3 in the high ones) and the image codes of the same elements, so the
+// reader tiles made for the mat-vec readers serve as they are: a wave regroups its 16 bytes per
+// lane through LDS (lane (row, b) holds block b; lane (row, g) needs bytes 4g..4g+3 of each).
+// Per 4-block chunk: the 64 image rows x 4 blocks are staged in LDS (double buffered, the next
+// chunk's loads in flight during the products), then 16 products and the scaling
+// acc += d_w (d_a sumi - 8 s_a) per block. Image rows past the live count, rows past N and
+// blocks past K/32 contribute nothing and are not stored.
+// ---------------------------------------------------------------------------------------------
+constexpr int kMmqWaves = 4;
+constexpr int kMmqMinRows = 64;  // Q4_0 readers of this many image rows or more use this kernel
+typedef long v1l;
+
+__global__ __launch_bounds__(kMmqWaves * 64) void mmq_kernel(ReadArgs p) {
+  // [buf][block][image row][32 codes + 4 pad]: the 36-byte row pitch spreads the 16 image rows
+  // of a product over distinct LDS banks
+  __shared__ __align__(16) unsigned char s_codes[2][4][64][36];
+  __shared__ __align__(16) float2 s_dam[2][4][64];                // d_a, -8 s_a
+  __shared__ __align__(16) uint32_t s_wq[kMmqWaves][64][4];       // regrouped weight codes
+  __shared__ __align__(16) uint16_t s_wd[kMmqWaves][4][16];       // weight scales [block][row]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int live = clamp_live(p.live_rows, p.rows, nullptr);
+  const int c0 = blockIdx.y * 64;
+  if (c0 >= live) return;  // whole workgroup
+  const int KC = p.KC;
+  // this wave's weight tile (tiles past the end repeat the last one; nothing is stored)
+  const int tile_raw = blockIdx.x * kMmqWaves + w;
+  const bool has = tile_raw < p.tiles_total;
+  const int tile = has ? tile_raw : p.tiles_total - 1;
+  int ri = 0;
+  while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
+  const int lt = tile - p.tile_start[ri];
+  const uint8_t* wq = p.r[ri].qs + ((int64_t)lt * KC * 64 + lane) * 16;
+  const uint16_t* wdp = p.r[ri].d + (int64_t)lt * KC * 64 + lane;
+
+  // staging of one chunk: thread tid -> image row c0 + (tid & 63), block 4 s + (tid >> 6)
+  const int sr = tid & 63, sb = tid >> 6;
+  uint4 ic0, ic1;
+  uint32_t idw;
+  uint4 wv;
+  uint16_t wdv;
+  auto load_chunk = [&](int s) {
+    const int row = c0 + sr, blk = 4 * s + sb;
+    const bool ok = row < live && blk < p.Kb;
+    const uint32_t off = ok ? (uint32_t)(row * p.RB + blk) : 0u;
+    const uint4* src = reinterpret_cast<const uint4*>(p.codes + (size_t)off * 32);
+    ic0 = src[0];
+    ic1 = src[1];
+    idw = p.ds[off];
+    if (!ok) {
+      ic0 = ic1 = make_uint4(0, 0, 0, 0);
+      idw = 0u;
+    }
+    wv = *reinterpret_cast<const uint4*>(wq + (int64_t)s * 1024);
+    wdv = wdp[(int64_t)s * 64];
+  };
+  auto store_chunk = [&](int buf) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&s_codes[buf][sb][sr][0]);  // 4-byte aligned
+    dst[0] = ic0.x; dst[1] = ic0.y; dst[2] = ic0.z; dst[3] = ic0.w;
+    dst[4] = ic1.x; dst[5] = ic1.y; dst[6] = ic1.z; dst[7] = ic1.w;
+    s_dam[buf][sb][sr] = make_float2(h2f(idw), -8.0f * h2f(idw >> 16));
+    // lane (row n, block g) holds bytes 0..15 of block g: dword k goes to lane (n, k), slot g
+    s_wq[w][n + 16 * 0][g] = wv.x;
+    s_wq[w][n + 16 * 1][g] = wv.y;
+    s_wq[w][n + 16 * 2][g] = wv.z;
+    s_wq[w][n + 16 * 3][g] = wv.w;
+    s_wd[w][g][n] = wdv;
+  };
+  float acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[j][v] = 0.0f;
+
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int s = 0; s < KC; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < KC) load_chunk(s + 1);
+    // this lane's weights: bytes 4g..4g+3 of blocks 4s..4s+3 of row n, and the scales of rows
+    // 4g..4g+3 for each block
+    const uint4 wr = *reinterpret_cast<const uint4*>(&s_wq[w][lane][0]);
+    const uint32_t wb[4] = {wr.x, wr.y, wr.z, wr.w};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t lo = wb[b] & 0x0f0f0f0fu, hi = (wb[b] >> 4) & 0x0f0f0f0fu;
+      const v1l a = (v1l)(((uint64_t)hi << 32) | lo);
+      const uint2 dwv = *reinterpret_cast<const uint2*>(&s_wd[w][b][4 * g]);
+      const float dw0 = h2f(dwv.x), dw1 = h2f(dwv.x >> 16), dw2 = h2f(dwv.y), dw3 = h2f(dwv.y >> 16);
+      v4i dd[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned char* cp = &s_codes[buf][b][16 * j + n][0];
+        const uint32_t clo = *reinterpret_cast<const uint32_t*>(cp + 4 * g);
+        const uint32_t chi = *reinterpret_cast<const uint32_t*>(cp + 16 + 4 * g);
+        const v1l bb = (v1l)(((uint64_t)chi << 32) | clo);
+        const v4i zero = {0, 0, 0, 0};
+        dd[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bb, zero, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 dm = s_dam[buf][b][16 * j + n];
+        acc[j][0] = __builtin_fmaf(dw0, __builtin_fmaf(dm.x, (float)dd[j][0], dm.y), acc[j][0]);
+        acc[j][1] = __builtin_fmaf(dw1, __builtin_fmaf(dm.x, (float)dd[j][1], dm.y), acc[j][1]);
+        acc[j][2] = __builtin_fmaf(dw2, __builtin_fmaf(dm.x, (float)dd[j][2], dm.y), acc[j][2]);
+        acc[j][3] = __builtin_fmaf(dw3, __builtin_fmaf(dm.x, (float)dd[j][3], dm.y), acc[j][3]);
+      }
+    }
+    if (s + 1 < KC) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+  if (!has) return;
+  const ReaderDesc& r = p.r[ri];
+  const int row0 = lt * 16 + 4 * g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = c0 + 16 * j + n;
+    if (col < live) {
+      float* o = r.out + (int64_t)col * r.ld + row0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (row0 + v < r.N) o[v] = acc[j][v];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Routed readers (MUL_MAT_ID).
 //
 // Plan ([P3] What this changes: only the live rows' pairs are planned, padding ids are never
@@ -2019,7 +2157,7 @@ static int ordinary_common(int fmt, const qimg_q4_0_reader* readers, int32_t n_r
     if (!al16(r.w) || !al(r.out, 4)) return QIMG_EALIGN;
     outs[i] = span(r.out, rows_extent(rows, r.ldo, r.N, 4));
     for (int j = 0; j < n_readers; ++j)
-      if (overlap(outs[i], span(readers[j].w, tiled_bytes_fmt(fmt, readers[j].N, K, 1))))
+      if (overlap(outs[i], span(readers[j].w, tiled_bytes_fmt(fmt == 3 ? 0 : fmt, readers[j].N, K, 1))))
         return QIMG_EALIAS;
     if (overlap(outs[i], si) || overlap(outs[i], sl)) return QIMG_EALIAS;
     for (int j = 0; j < i; ++j)
@@ -2043,12 +2181,22 @@ static int ordinary_common(int fmt, const qimg_q4_0_reader* readers, int32_t n_r
   a.top_k = 1;
   if (fmt == 1) return run_ordinary<3>(a, (hipStream_t)stream);
   if (fmt == 2) return run_ordinary<4>(a, (hipStream_t)stream);
+  if (fmt == 3 || (fmt == 0 && rows >= kMmqMinRows)) {  // prefill: the many-row reader
+    a.tiles_total = tiles;
+    const dim3 grid((unsigned)((tiles + kMmqWaves - 1) / kMmqWaves), (unsigned)((rows + 63) / 64));
+    hipLaunchKernelGGL(mmq_kernel, grid, dim3(kMmqWaves * 64), 0, (hipStream_t)stream, a);
+    return launch_status();
+  }
   return run_ordinary<0>(a, (hipStream_t)stream);
 }
 
 int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
                    int32_t rows, const int32_t* live_rows, int32_t K, void* stream) {
   return ordinary_common(0, readers, n_readers, img, rows, live_rows, K, stream);
+}
+int mmq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
+                  int32_t rows, const int32_t* live_rows, int32_t K, void* stream) {
+  return ordinary_common(3, readers, n_readers, img, rows, live_rows, K, stream);
 }
 int mmvq_q8_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
                    int32_t rows, const int32_t* live_rows, int32_t K, void* stream) {

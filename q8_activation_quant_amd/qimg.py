@@ -19,7 +19,7 @@ GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF, "reglu": GLU_REGLU,
            "geglu_quick": GLU_GEGLU_QUICK, "swiglu_oai": GLU_SWIGLU_OAI, "swiglu_clamp": GLU_SWIGLU_CLAMP}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
@@ -29,7 +29,7 @@ EXPORTS = (
     "qimg_emit_glu_per_slot", "mmvq_id_q4_0_q8_1_per_slot", "qimg_moe_combine",
     "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex", "qimg_moe_router", "qimg_moe_topk",
     "qimg_q8_0_tiled_bytes", "qimg_q4_1_tiled_bytes", "qimg_q8_0_tile", "qimg_q4_1_tile",
-    "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1",
+    "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1", "mmq_q4_0_q8_1",
 )
 MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7, "reglu": 8,
             "geglu": 9, "geglu_quick": 10, "swiglu_oai_gate": 11}
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "qimg_q4_1_tile": (ctypes.c_int, [P, P, P, i32, i32, i32, P, P]),
             "mmvq_q8_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "mmvq_q4_1_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
+            "mmq_q4_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "qimg_moe_topk": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -205,9 +206,11 @@ def _readers(specs, cls):
 
 
 def mmvq(readers, img, rows, K, live_rows=None, stream=None, fmt="q4_0"):
-    """Ordinary readers: readers = [(tiled weights of format fmt, N, out [rows, N] f32)]."""
+    """Ordinary readers: readers = [(tiled weights of format fmt, N, out [rows, N] f32)];
+    fmt "mmq" forces the many-row (prefill) Q4_0 reader."""
     arr = _readers(readers, Reader)
-    name = {"q4_0": "mmvq_q4_0_q8_1", "q8_0": "mmvq_q8_0_q8_1", "q4_1": "mmvq_q4_1_q8_1"}[fmt]
+    name = {"q4_0": "mmvq_q4_0_q8_1", "q8_0": "mmvq_q8_0_q8_1", "q4_1": "mmvq_q4_1_q8_1",
+            "mmq": "mmq_q4_0_q8_1"}[fmt]
     _check(getattr(lib(), name)(arr, len(readers), _ptr(img), rows, _ptr(live_rows), K, _stream(stream)), name)
 
 

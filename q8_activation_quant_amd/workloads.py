@@ -14,6 +14,8 @@ Workloads (sizes and distributions of the pages' component graphs, chosen per wo
                     Q4_0 expert weights [128, 768, 2560]
   5 padded bucket   bucket 128 rows, live rows in {1, 9, 113, 114, 128}, K=2048, E=256,
                     top-9, Q4_0 expert weights [256, 512, 2048]; padding rows poisoned
+  6 prefill         T=3325 prompt tokens, K=3584, RMSNorm x gamma, three Q4_0 readers
+                    N=3584, 512, 512 (the q/k/v projections of a d=3584 model sharing one image)
 Q4_0 weights: 4-bit codes uniform on 0..15 (uniform random bytes), fp16 block scales uniform
 on [1e-3, 1e-2]. Gamma ~ N(1, 0.1), eps = 1e-6.
 
@@ -131,7 +133,7 @@ class Workload:
 
 def make(config: int, *, live: int | None = None, glu_op: str = "swiglu", small: bool = False,
          moe: bool = False, wfmt: str = "q4_0") -> Workload:
-    """Build workload `config` (1..5). `small=True` shrinks the weight row counts (not K or T)
+    """Build workload `config` (1..6). `small=True` shrinks the weight row counts (not K or T)
     so the CPU oracle can check every output of a GPU run in well under a second. `moe=True`
     (workloads 4 and 5) adds the down projection and the MoE stage inputs."""
     wl = _make(config, live, glu_op, small, moe)
@@ -204,7 +206,14 @@ def _make(config, live, glu_op, small, moe):
         return Workload(5, "padded bucket B128 K2048 E256 top9 live%d" % live, B, K, "rmsnorm",
                         x=x, gamma=gamma, readers=readers, E=E, top_k=k, ids=ids, route_w=w,
                         live=live, n_ff=N)
-    raise ValueError("config must be 1..5")
+    if config == 6:
+        K, T = 3584, 3325
+        x = rng(6, T_X).standard_normal((T, K)).astype(np.float32)
+        gamma = rng(6, T_GAMMA).normal(1.0, 0.1, K).astype(np.float32)
+        Ns = [3584, 512, 512] if not small else [96, 32, 40]
+        readers = [q4_0_weights(rng(6, T_READER0 + r), (N,), K) for r, N in enumerate(Ns)]
+        return Workload(6, "prefill T3325 K3584", T, K, "rmsnorm", x=x, gamma=gamma, readers=readers)
+    raise ValueError("config must be 1..6")
 
 
 POISON = (np.float32(np.nan), np.float32(1e30), np.float32(-1e30))
