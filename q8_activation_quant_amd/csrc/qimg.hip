@@ -756,6 +756,16 @@ __device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
 }
 
 __device__ __forceinline__ int stage_code_insts(const ReadArgs& p) { return (4 * p.KC * p.tp * 2 + 63) / 64; }
+// Staging by the waves for themselves: with 8 image columns per pass a code copy instruction
+// is exactly one chunk (4 blocks x 8 columns x 32 bytes), and wave w streams chunks w, w + 8,
+// ...; when the scale words are copied the same way (below), every wave stages exactly what
+// it reads and needs no barrier before streaming.
+#ifdef QIMG_INTERLEAVE
+constexpr bool kInterleaveChunks = QIMG_INTERLEAVE;
+#else
+constexpr bool kInterleaveChunks = true;
+#endif
+__device__ __forceinline__ bool stage_own(const ReadArgs& p) { return kInterleaveChunks && p.tp == 8; }
 __device__ __forceinline__ int stage_word_insts(const ReadArgs& p) { return (4 * p.KC * p.tp + 63) / 64; }
 
 __device__ __forceinline__ void stage_dma_issue(const ReadArgs& p, unsigned char* smem, int c0, int nc,
@@ -769,6 +779,20 @@ __device__ __forceinline__ void stage_dma_issue(const ReadArgs& p, unsigned char
     const int row = c0 + (c < nc ? c : 0);
     const int bs = b < p.Kb ? b : p.Kb - 1;
     dma_b128(p.codes + ((int64_t)row * p.RB + bs) * 32 + 16 * half, lds_addr(smem + 1024 * k));
+  }
+  if (stage_own(p)) {
+    // the scale words of the wave's own chunks w + 16 j (lanes 0..31) and w + 8 + 16 j
+    // (lanes 32..63), 32 words per chunk, to raw slot 8 j + w (a chunk past the end copies
+    // the first one's words again; they are not used)
+    for (int j = 0; w + 16 * j < p.KC; ++j) {
+      const int ca = w + 16 * j, cb = ca + 8;
+      const int ch = lane < 32 || cb >= p.KC ? ca : cb;
+      const int i = lane & 31, c = i & 7, b = 4 * ch + (i >> 3);
+      const int row = c0 + (c < nc ? c : 0);
+      const int bs = b < p.Kb ? b : p.Kb - 1;
+      dma_b32(p.ds + (int64_t)row * p.RB + bs, lds_addr(smem + p.lds_raw + 256 * (8 * j + w)));
+    }
+    return;
   }
   for (int k = w; k < nwi; k += kOrdWaves) {
     const int i = 64 * k + lane;
@@ -786,6 +810,20 @@ __device__ __forceinline__ void stage_convert(const ReadArgs& p, unsigned char* 
   const int TP = p.tp, TPD = p.tpd, nb = 4 * p.KC;
   const uint32_t* raw = reinterpret_cast<const uint32_t*>(smem + p.lds_raw);
   float2* dam = reinterpret_cast<float2*>(smem + p.lds_da);  // [4 KC][tpd] (d_a, -8 s_a)
+  if (stage_own(p)) {
+    for (int j = 0; w + 16 * j < p.KC; ++j) {
+      const int ca = w + 16 * j, cb = ca + 8;
+      const int ch = lane < 32 ? ca : cb;
+      if (ch < p.KC) {
+        const int i = lane & 31, c = i & 7, b = 4 * ch + (i >> 3);
+        const bool ok = c < nc && b < p.Kb;
+        const uint32_t x = raw[64 * (8 * j + w) + lane];
+        dam[b * TPD + c] = ok ? make_float2(h2f(x), -8.0f * h2f(x >> 16)) : make_float2(0.0f, 0.0f);
+      }
+    }
+    if (lane < 8) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[lane] = 0u;
+    return;
+  }
   const int nwi = stage_word_insts(p);
   for (int k = w; k < nwi; k += kOrdWaves) {
     const int i = 64 * k + lane;
@@ -835,9 +873,8 @@ constexpr int ring_depth(int ntm) {
   return ntm == 1 ? QIMG_RING1 : ntm == 2 ? QIMG_RING2 : ntm == 3 ? QIMG_RING3 : QIMG_RING4;
 }
 
-// MODE: 0 ordinary readers, 2 block-dot export. NTG: token groups of 4 image columns per pass
-// (1 when a pass has at most 4 columns).
-// MODE: 0 Q4_0 readers, 2 Q4_0 block-dot export, 3 Q8_0 readers, 4 Q4_1 readers.
+// MODE: 0 Q4_0 readers, 2 Q4_0 block-dot export, 3 Q8_0 readers, 4 Q4_1 readers. NTG: token
+// groups of 4 image columns per pass (1 when a pass has at most 4 columns).
 template <int NTM, int MODE, int NTG>
 __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) {
   constexpr bool DOTS = MODE == 2;
@@ -848,11 +885,7 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
   extern __shared__ __align__(16) unsigned char smem[];
   // weight loads in flight per wave: a ring of D slots, each one chunk of NTM tiles
   constexpr int D = ring_depth(NTM);
-#ifdef QIMG_INTERLEAVE
-  constexpr bool kInterleave = QIMG_INTERLEAVE;
-#else
-  constexpr bool kInterleave = true;
-#endif
+  constexpr bool kInterleave = kInterleaveChunks;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int n = lane & 15, g = lane >> 4;
@@ -1038,7 +1071,7 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       }
       if (stage) {
         stage_convert(p, smem, nc, w, lane);
-        __syncthreads();
+        if (!stage_own(p)) __syncthreads();
       }
       for (int base = 0; base < nst; base += D) {
 #pragma unroll
@@ -1822,7 +1855,11 @@ inline bool plan_lds(ReadArgs& a, int ntm, int* total) {
   for (int tp : {8, 4, 2, 1}) {
     const int tpd = tp > 4 ? tp : 4;
     const int codes = (nb * tp * 2 + 63) / 64 * 1024;
-    const int raw = (nb * tp + 63) / 64 * 256;
+    int raw = (nb * tp + 63) / 64 * 256;
+    if (tp == 8) {  // per-wave scale-word slots: 8 per 16 chunks (see stage_own)
+      const int own = (a.KC + 15) / 16 * 8 * 256;
+      if (own > raw) raw = own;
+    }
     const int dsz = nb * tpd * 8;
     const int red = kOrdWaves * ntm * 16 * 8 * 4;
     const int t = codes + raw + dsz + 32 + red;
