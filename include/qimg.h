@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 9
+#define QIMG_ABI_VERSION 10
 
 /* status codes */
 #define QIMG_OK 0
@@ -247,6 +247,30 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
                       const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
                       const int32_t* live_rows, int32_t K, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * The routing plan as a launch of its own, and routed readers that take it from the workspace
+ * ([P3] What this changes: the plan covers the live rows' pairs only; launches stay sized for
+ * the bucket). The plan depends on the ids and the live count alone, so it can run beside the
+ * producer (another stream, or a parallel branch of a graph) and serve several routed launches
+ * over the same ids (the gate/up and the down projections of an MoE FFN).
+ *   mmvq_id_plan: writes the plan and the error word into workspace exactly as
+ *     mmvq_id_q4_0_q8_1 does (same layout, same errors); one workgroup.
+ *   mmvq_id_q4_0_q8_1_ex: mmvq_id_q4_0_q8_1 with flags:
+ *     QIMG_ID_PER_SLOT - the image holds one row per pair (mmvq_id_q4_0_q8_1_per_slot);
+ *     QIMG_ID_PLANNED  - read the plan from workspace (written by mmvq_id_plan, or by a routed
+ *                        reader call, over the same ids and live count, and ordered before
+ *                        this call); ids are then not read and workspace is not written.
+ *   Unknown flag bits: QIMG_EINVAL.
+ */
+#define QIMG_ID_PER_SLOT 1
+#define QIMG_ID_PLANNED 2
+int mmvq_id_plan(const int32_t* ids, int32_t bucket, int32_t top_k, const int32_t* live_rows,
+                 int32_t E, void* workspace, size_t workspace_bytes, void* stream);
+int mmvq_id_q4_0_q8_1_ex(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
+                         const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
+                         const int32_t* live_rows, int32_t K, void* workspace,
+                         size_t workspace_bytes, int32_t flags, void* stream);
 
 /*
  * The rest of a routed MoE FFN after the gate and up projections ([P1] Coverage: GLU

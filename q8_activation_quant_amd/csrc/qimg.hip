@@ -1302,7 +1302,10 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-template <int NTM, int KU>
+// PM (plan mode): 0 builds the plan and streams; 1 builds the plan, writes it to the
+// workspace and stops (one workgroup); 2 takes the plan from the workspace (written by a
+// plan-mode-1 launch over the same ids and live count) and streams.
+template <int NTM, int KU, int PM>
 __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int sh_wave[3][kWaves];
@@ -1325,6 +1328,15 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   int32_t* mem = tmp + p.pairs_cap;                                // [pairs_cap]
 
   // ---- plan ----
+  if constexpr (PM == 2) {  // counts from the workspace; offsets, active experts and units below
+    const int32_t* counts = p.ws + 4;
+    for (int e = tid; e < E; e += blockDim.x) fill[e] = counts[e];
+    if (tid < 4) {
+      sh_misc[tid] = 0;
+      reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;
+    }
+    __syncthreads();
+  } else {
   for (int e = tid; e < E; e += blockDim.x) fill[e] = 0;
   if (tid < 4) {
     sh_misc[tid] = 0;
@@ -1339,6 +1351,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   }
   if (nbad) atomicAdd(&sh_misc[0], nbad);
   __syncthreads();
+  }
   {
     const int per = (E + (int)blockDim.x - 1) / (int)blockDim.x;
     const int e0 = tid * per;
@@ -1388,6 +1401,11 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     }
   }
   __syncthreads();
+  if constexpr (PM == 2) {
+    const int32_t* members = p.ws + 4 + 2 * E + 1;
+    for (int q = tid; q < off[E]; q += blockDim.x) mem[q] = members[q];
+    __syncthreads();
+  } else {
   for (int e = tid; e < E; e += blockDim.x) fill[e] = 0;
   __syncthreads();
   for (int pi = tid; pi < P; pi += blockDim.x) {
@@ -1421,6 +1439,8 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       p.ws[3] = 0;
       offsets[E] = nvalid;
     }
+  }
+  if constexpr (PM == 1) return;
   }
 
   // ---- work ----
@@ -1925,7 +1945,7 @@ int run_ordinary(ReadArgs& a, hipStream_t s) {
 // Routed readers: one workgroup per CU over the (expert, pass, tile) units. LDS: `slots`
 // staged segments of [4 KC][tp][32] codes + [4 KC][8] d_a + [4 KC][8] -8 s_a, the zero slot,
 // then the plan arrays off[E+1], fill[E], act[E], ust[E+1], tmp[pairs], mem[pairs].
-int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
+int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s, int pm = 0) {
   const int tiles = a.tile_start[a.n_readers];
   a.tiles_total = tiles;
   a.pairs_cap = pairs_cap;
@@ -1952,11 +1972,26 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
     if (lds >= 0) break;
   }
   if (lds < 0) return QIMG_EUNSUPPORTED;
-  const void* fn = (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu>;
+  if (pm == 1) {  // the plan alone: one workgroup, plan arrays only
+    a.lds_zero = 0;
+    a.lds_plan = 16;
+    const int plds = 16 + plan;
+    const void* fp = (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 1>;
+    if (plds > 64 * 1024 &&
+        hipFuncSetAttribute(fp, hipFuncAttributeMaxDynamicSharedMemorySize, plds) != hipSuccess)
+      return QIMG_EHIP;
+    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 1>), dim3(1), dim3(kWaves * 64), plds, s, a);
+    return launch_status();
+  }
+  const void* fn = pm == 2 ? (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 2>
+                           : (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 0>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
-  hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
+  if (pm == 2)
+    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 2>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
+  else
+    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 0>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
   return launch_status();
 }
 
@@ -2255,7 +2290,7 @@ size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E) {
 static int routed_common(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
                          const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
                          const int32_t* live_rows, int32_t K, void* workspace,
-                         size_t workspace_bytes, int per_slot, void* stream) {
+                         size_t workspace_bytes, int per_slot, void* stream, int pm = 0) {
   int st = check_k(K);
   if (st) return st;
   if (!readers || n_readers < 1 || n_readers > QIMG_MAX_READERS || E <= 0 || bucket < 0 ||
@@ -2309,7 +2344,46 @@ static int routed_common(const qimg_q4_0_expert_reader* readers, int32_t n_reade
   a.top_k = top_k;
   a.img_div = per_slot ? 1 : top_k;
   a.E = E;
-  return run_routed(a, (int)pairs, (hipStream_t)stream);
+  return run_routed(a, (int)pairs, (hipStream_t)stream, pm);
+}
+
+int mmvq_id_q4_0_q8_1_ex(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
+                         const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
+                         const int32_t* live_rows, int32_t K, void* workspace,
+                         size_t workspace_bytes, int32_t flags, void* stream) {
+  if (flags & ~(QIMG_ID_PER_SLOT | QIMG_ID_PLANNED)) return QIMG_EINVAL;
+  return routed_common(readers, n_readers, E, img, ids, bucket, top_k, live_rows, K, workspace,
+                       workspace_bytes, (flags & QIMG_ID_PER_SLOT) ? 1 : 0, stream,
+                       (flags & QIMG_ID_PLANNED) ? 2 : 0);
+}
+
+int mmvq_id_plan(const int32_t* ids, int32_t bucket, int32_t top_k, const int32_t* live_rows,
+                 int32_t E, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ids || E <= 0 || bucket < 0 || top_k <= 0) return QIMG_EINVAL;
+  if (bucket == 0) return QIMG_OK;
+  const int64_t pairs = (int64_t)bucket * top_k;
+  if (pairs > QIMG_MAX_ROUTED_PAIRS || E > QIMG_MAX_EXPERTS) return QIMG_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < mmvq_id_workspace_bytes(bucket, top_k, E))
+    return QIMG_EWORKSPACE;
+  if (!al16(workspace) || !al(ids, 4) || (live_rows && !al(live_rows, 4))) return QIMG_EALIGN;
+  const Span sw = span(workspace, (int64_t)mmvq_id_workspace_bytes(bucket, top_k, E));
+  if (overlap(sw, span(ids, pairs * 4)) || (live_rows && overlap(sw, span(live_rows, 4))))
+    return QIMG_EALIAS;
+  ReadArgs a{};
+  a.n_readers = 1;
+  a.tile_start[0] = 0;
+  a.tile_start[1] = 1;  // the plan does not depend on the readers; one nominal tile
+  a.Kb = 1;
+  a.KC = 1;
+  a.RB = 16;
+  a.rows = bucket;
+  a.live_rows = live_rows;
+  a.ids = ids;
+  a.ws = (int32_t*)workspace;
+  a.top_k = top_k;
+  a.img_div = top_k;
+  a.E = E;
+  return run_routed(a, (int)pairs, (hipStream_t)stream, 1);
 }
 
 int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,

@@ -378,3 +378,25 @@ def test_moe_topk_validation(L):
     assert topk(ids=A + 64) == qimg.EALIAS
     assert topk(w=B + 16) == qimg.EALIAS
     assert topk(live=B + 32) == qimg.EALIAS
+
+
+def test_routed_plan_and_flags_validation(L):
+    E, bucket, k = 8, 16, 2
+    ws_bytes = qimg.workspace_bytes(bucket, k, E)
+    WS, IDS = B, B + (1 << 20)
+    plan = lambda ids=IDS, b=bucket, kk=k, live=None, e=E, ws=WS, wsb=ws_bytes: L.mmvq_id_plan(
+        ids, b, kk, live, e, ws, wsb, S)
+    assert plan(ids=None) == qimg.EINVAL
+    assert plan(e=0) == qimg.EINVAL
+    assert plan(kk=0) == qimg.EINVAL
+    assert plan(b=0) == qimg.OK
+    assert plan(b=4097, kk=1, wsb=qimg.workspace_bytes(4097, 1, E)) == qimg.EUNSUPPORTED
+    assert plan(ws=None) == qimg.EWORKSPACE
+    assert plan(wsb=ws_bytes - 256) == qimg.EWORKSPACE
+    assert plan(ws=WS + 4) == qimg.EALIGN
+    assert plan(ids=IDS + 2) == qimg.EALIGN
+    assert plan(ws=IDS - 64) == qimg.EALIAS
+    r = expert_readers((A, 64, C, 64))
+    ex = lambda flags: L.mmvq_id_q4_0_q8_1_ex(r, 1, E, D, IDS, bucket, k, None, 256, WS, ws_bytes, flags, S)
+    assert ex(4) == qimg.EINVAL
+    assert ex(-1) == qimg.EINVAL
