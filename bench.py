@@ -495,10 +495,11 @@ def main():
         },
     }
     if args.config == 6:
-        # the prefill reader is bound by its per-block scaling on the vector ALUs: 3 operations
-        # (convert, two fused multiply-adds) per (image row, weight row, block), against the
-        # unpacked f32 vector rate of 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-        ops = 3.0 * wl.T * sum(wl.reader_rows) * (wl.K // 32)
+        # the prefill reader is bound by its per-block scaling on the vector ALUs: 2 operations
+        # (convert the block's int32 dot, one fused multiply-add by d_w d_a, which the matrix
+        # cores supply) per (image row, weight row, block), against the unpacked f32 vector
+        # rate of 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+        ops = 2.0 * wl.T * sum(wl.reader_rows) * (wl.K // 32)
         peak = 256 * 4 * 16 * 2.4e9 / 1e12
         ach = ops / (r["reader_us"] * 1e-6) / 1e12
         line["roofline_alu"] = {"bound": "alu", "achieved": round(ach, 2), "peak": round(peak, 2),

@@ -1145,14 +1145,23 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 constexpr int kMmqWaves = 4;
 constexpr int kMmqMinRows = 64;  // Q4_0 readers of this many image rows or more use this kernel
 typedef long v1l;
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kMmqWaves * 64) void mmq_kernel(ReadArgs p) {
+__device__ __forceinline__ v4h as_v4h(uint64_t x) { return __builtin_bit_cast(v4h, x); }
+
+// The scales go through f16 products (exact in f32): per block the outer product
+// d_w[row] d_a[image row] (k slot b of an f16 product whose other slots are zero), and per
+// chunk the sums over its 4 blocks of d_w s_a (k slots 0..3), accumulated over K by the matrix
+// core. Each (image row, weight row, block) then costs a convert and one fma:
+//   acc += (d_w d_a) sumi;     out = acc - 8 sum_b d_w s_a.
+__global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
   // [buf][block][image row][32 codes + 4 pad]: the 36-byte row pitch spreads the 16 image rows
   // of a product over distinct LDS banks
   __shared__ __align__(16) unsigned char s_codes[2][4][64][36];
-  __shared__ __align__(16) float2 s_dam[2][4][64];                // d_a, -8 s_a
-  __shared__ __align__(16) uint32_t s_wq[kMmqWaves][64][4];       // regrouped weight codes
-  __shared__ __align__(16) uint16_t s_wd[kMmqWaves][4][16];       // weight scales [block][row]
+  __shared__ __align__(16) uint16_t s_das[2][64][8];             // d_a[4 blocks], s_a[4 blocks]
+  __shared__ __align__(16) uint32_t s_wq[kMmqWaves][64][4];      // regrouped weight codes
+  __shared__ __align__(16) uint16_t s_wd[kMmqWaves][16][4];      // weight scales [row][block]
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -1195,19 +1204,23 @@ __global__ __launch_bounds__(kMmqWaves * 64) void mmq_kernel(ReadArgs p) {
     uint32_t* dst = reinterpret_cast<uint32_t*>(&s_codes[buf][sb][sr][0]);  // 4-byte aligned
     dst[0] = ic0.x; dst[1] = ic0.y; dst[2] = ic0.z; dst[3] = ic0.w;
     dst[4] = ic1.x; dst[5] = ic1.y; dst[6] = ic1.z; dst[7] = ic1.w;
-    s_dam[buf][sb][sr] = make_float2(h2f(idw), -8.0f * h2f(idw >> 16));
+    s_das[buf][sr][sb] = (uint16_t)(idw & 0xffffu);
+    s_das[buf][sr][4 + sb] = (uint16_t)(idw >> 16);
     // lane (row n, block g) holds bytes 0..15 of block g: dword k goes to lane (n, k), slot g
     s_wq[w][n + 16 * 0][g] = wv.x;
     s_wq[w][n + 16 * 1][g] = wv.y;
     s_wq[w][n + 16 * 2][g] = wv.z;
     s_wq[w][n + 16 * 3][g] = wv.w;
-    s_wd[w][g][n] = wdv;
+    s_wd[w][n][g] = wdv;
   };
   float acc[4][4];
+  v4f sacc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 4; ++j) {
+    sacc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[j][v] = 0.0f;
+  }
 
   load_chunk(0);
   store_chunk(0);
@@ -1215,17 +1228,27 @@ __global__ __launch_bounds__(kMmqWaves * 64) void mmq_kernel(ReadArgs p) {
   for (int s = 0; s < KC; ++s) {
     const int buf = s & 1;
     if (s + 1 < KC) load_chunk(s + 1);
-    // this lane's weights: bytes 4g..4g+3 of blocks 4s..4s+3 of row n, and the scales of rows
-    // 4g..4g+3 for each block
+    // this lane's weights: bytes 4g..4g+3 of blocks 4s..4s+3 of row n; the f16 operands of
+    // the scale products live in the lanes of k group 0 (the other k slots are zero)
     const uint4 wr = *reinterpret_cast<const uint4*>(&s_wq[w][lane][0]);
     const uint32_t wb[4] = {wr.x, wr.y, wr.z, wr.w};
+    const uint64_t dwv = g == 0 ? *reinterpret_cast<const uint64_t*>(&s_wd[w][n][0]) : 0ull;
+    uint64_t dav[4];
 #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t* ds4 = reinterpret_cast<const uint64_t*>(&s_das[buf][16 * j + n][0]);
+      dav[j] = g == 0 ? ds4[0] : 0ull;
+      const uint64_t sav = g == 0 ? ds4[1] : 0ull;
+      sacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_v4h(dwv), as_v4h(sav), sacc[j], 0, 0, 0);
+    }
+    // one block at a time (a full unroll keeps every block's products live: 324 registers)
+#pragma unroll 1
     for (int b = 0; b < 4; ++b) {
       const uint32_t lo = wb[b] & 0x0f0f0f0fu, hi = (wb[b] >> 4) & 0x0f0f0f0fu;
       const v1l a = (v1l)(((uint64_t)hi << 32) | lo);
-      const uint2 dwv = *reinterpret_cast<const uint2*>(&s_wd[w][b][4 * g]);
-      const float dw0 = h2f(dwv.x), dw1 = h2f(dwv.x >> 16), dw2 = h2f(dwv.y), dw3 = h2f(dwv.y >> 16);
+      const uint64_t dwb = dwv & (0xffffull << (16 * b));  // d_w of block b in k slot b
       v4i dd[4];
+      v4f dwda[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const unsigned char* cp = &s_codes[buf][b][16 * j + n][0];
@@ -1233,16 +1256,14 @@ __global__ __launch_bounds__(kMmqWaves * 64) void mmq_kernel(ReadArgs p) {
         const uint32_t chi = *reinterpret_cast<const uint32_t*>(cp + 16 + 4 * g);
         const v1l bb = (v1l)(((uint64_t)chi << 32) | clo);
         const v4i zero = {0, 0, 0, 0};
+        const v4f fzero = {0.0f, 0.0f, 0.0f, 0.0f};
         dd[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bb, zero, 0, 0, 0);
+        dwda[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_v4h(dwb), as_v4h(dav[j]), fzero, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float2 dm = s_dam[buf][b][16 * j + n];
-        acc[j][0] = __builtin_fmaf(dw0, __builtin_fmaf(dm.x, (float)dd[j][0], dm.y), acc[j][0]);
-        acc[j][1] = __builtin_fmaf(dw1, __builtin_fmaf(dm.x, (float)dd[j][1], dm.y), acc[j][1]);
-        acc[j][2] = __builtin_fmaf(dw2, __builtin_fmaf(dm.x, (float)dd[j][2], dm.y), acc[j][2]);
-        acc[j][3] = __builtin_fmaf(dw3, __builtin_fmaf(dm.x, (float)dd[j][3], dm.y), acc[j][3]);
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[j][v] = __builtin_fmaf(dwda[j][v], (float)dd[j][v], acc[j][v]);
     }
     if (s + 1 < KC) store_chunk(buf ^ 1);
     __syncthreads();
@@ -1257,7 +1278,7 @@ __global__ __launch_bounds__(kMmqWaves * 64) void mmq_kernel(ReadArgs p) {
       float* o = r.out + (int64_t)col * r.ld + row0;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (row0 + v < r.N) o[v] = acc[j][v];
+        if (row0 + v < r.N) o[v] = __builtin_fmaf(-8.0f, sacc[j][v], acc[j][v]);
     }
   }
 }
