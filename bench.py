@@ -454,7 +454,8 @@ def main():
     wl, nb = r["wl"], r["bytes"]
     us = r["us"]["fused"]
     reader_gbs = nb["reader_kernel"] / (r["reader_us"] * 1e-6) / 1e9
-    traffic = pmc_traffic("hbm_bytes_per_launch")
+    # the committed counters cover the Q4_0 readers of the K8192/T8 workload only
+    traffic = pmc_traffic("hbm_bytes_per_launch") if (args.config == 2 and args.wfmt == "q4_0" and args.live is None) else None
     line = {
         "metric": "us per component graph + achieved HBM GB/s (% of peak), 1 MI355X",
         "value": round(us, 3),
