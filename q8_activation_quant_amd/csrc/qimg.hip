@@ -697,6 +697,10 @@ constexpr int kOrdWaves = QIMG_OWAVES;  // ordinary readers
 constexpr int kOrdWaves = 8;
 #endif
 
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4h as_v4h(uint64_t x) { return __builtin_bit_cast(v4h, x); }
+
 struct ReaderDesc {
   const uint8_t* qs;  // tiled codes (1 KB per chunk)
   const uint16_t* d;  // tiled scales (64 per chunk)
@@ -718,11 +722,17 @@ struct ReadArgs {
   int32_t n_readers, RB, Kb, KC, rows, top_k, E;
   int32_t img_div;      // routed: image row of pair p is p / img_div (top_k: token rows; 1: per slot)
   int32_t tiles_total;  // tiles per expert summed over readers
+  // ordinary readers: work is split over the workgroups in half tiles (8 weight rows), so that
+  // every workgroup streams the same number of bytes; half_start is the prefix over readers of
+  // ceil(N / 8)
+  int32_t half_start[QIMG_MAX_READERS + 1];
+  int32_t halves_total;
+  int32_t half_q, half_r;  // halves_total = half_q * workgroups + half_r (half_r < workgroups)
   int32_t tp;           // image columns per LDS pass (8, 4, 2 or 1)
   int32_t tp_log2;      // log2(tp)
-  int32_t lds_da, lds_ms, lds_zero, lds_red;  // byte offsets (codes at 0)
-  int32_t lds_raw;      // ordinary: raw image scale words [4 KC][tp]
-  int32_t tpd;          // ordinary: columns per row of d_a / -8 s_a (max(tp, 4))
+  int32_t lds_zero, lds_red;  // byte offsets (codes at 0)
+  int32_t lds_raw;      // ordinary: raw image scale words (d_a | s_a << 16)
+  int32_t raw_wave;     // ordinary, 8 columns per pass: raw word bytes per wave
   // routed readers
   int32_t lds_plan;     // byte offset of the plan arrays
   int32_t slots;        // staged (expert, pass) segments per batch
@@ -732,10 +742,11 @@ struct ReadArgs {
 
 // Staging of image columns [c0, c0 + nc) in LDS for the ordinary readers, all 4 KC blocks, by
 // direct global-to-LDS copies (no registers): codes into [4 KC][tp][32] at LDS 0 as 1 KB wave
-// instructions (16 bytes per lane), raw scale words into [4 KC][tp] at lds_raw as 256-byte
-// instructions. Wave w issues instructions w, w + 8, ... Items past the end of a region copy an
+// instructions (16 bytes per lane), raw scale words (d_a | s_a << 16, used as they are) at
+// lds_raw as 256-byte instructions: [4 KC][tp], or with 8 columns per pass per wave (below).
+// Wave w issues code instructions w, w + 8, ... Items past the end of a region copy an
 // in-bounds image address into the region's padding; blocks past K/32 copy the row's last
-// block (their d_a and -8 s_a are set to zero, which is what makes them contribute nothing).
+// block (the weight tiles hold d_w = 0 there, which is what makes them contribute nothing).
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // One direct global-to-LDS copy per lane, to LDS byte address lds + lane * bytes (lds must be
@@ -781,16 +792,17 @@ __device__ __forceinline__ void stage_dma_issue(const ReadArgs& p, unsigned char
     dma_b128(p.codes + ((int64_t)row * p.RB + bs) * 32 + 16 * half, lds_addr(smem + 1024 * k));
   }
   if (stage_own(p)) {
-    // the scale words of the wave's own chunks w + 16 j (lanes 0..31) and w + 8 + 16 j
-    // (lanes 32..63), 32 words per chunk, to raw slot 8 j + w (a chunk past the end copies
-    // the first one's words again; they are not used)
-    for (int j = 0; w + 16 * j < p.KC; ++j) {
-      const int ca = w + 16 * j, cb = ca + 8;
+    // the scale words of the wave's own chunks of steps 2 j (lanes 0..31) and 2 j + 1 (lanes
+    // 32..63), 32 words per chunk ([block of the chunk][column]), so that the words of the
+    // wave's step st sit at lds_raw + w raw_wave + 128 st (a chunk past the end copies the
+    // first one's words again; they are not used)
+    for (int j = 0; w + 2 * kOrdWaves * j < p.KC; ++j) {
+      const int ca = w + 2 * kOrdWaves * j, cb = ca + kOrdWaves;
       const int ch = lane < 32 || cb >= p.KC ? ca : cb;
       const int i = lane & 31, c = i & 7, b = 4 * ch + (i >> 3);
       const int row = c0 + (c < nc ? c : 0);
       const int bs = b < p.Kb ? b : p.Kb - 1;
-      dma_b32(p.ds + (int64_t)row * p.RB + bs, lds_addr(smem + p.lds_raw + 256 * (8 * j + w)));
+      dma_b32(p.ds + (int64_t)row * p.RB + bs, lds_addr(smem + p.lds_raw + w * p.raw_wave + 256 * j));
     }
     return;
   }
@@ -803,39 +815,9 @@ __device__ __forceinline__ void stage_dma_issue(const ReadArgs& p, unsigned char
   }
 }
 
-// After the wave's own copies have landed: convert the scale words it copied into d_a and
-// -8 s_a rows of tpd columns (zero for padding columns and blocks).
-__device__ __forceinline__ void stage_convert(const ReadArgs& p, unsigned char* smem, int nc, int w,
-                                              int lane) {
-  const int TP = p.tp, TPD = p.tpd, nb = 4 * p.KC;
-  const uint32_t* raw = reinterpret_cast<const uint32_t*>(smem + p.lds_raw);
-  float2* dam = reinterpret_cast<float2*>(smem + p.lds_da);  // [4 KC][tpd] (d_a, -8 s_a)
-  if (stage_own(p)) {
-    for (int j = 0; w + 16 * j < p.KC; ++j) {
-      const int ca = w + 16 * j, cb = ca + 8;
-      const int ch = lane < 32 ? ca : cb;
-      if (ch < p.KC) {
-        const int i = lane & 31, c = i & 7, b = 4 * ch + (i >> 3);
-        const bool ok = c < nc && b < p.Kb;
-        const uint32_t x = raw[64 * (8 * j + w) + lane];
-        dam[b * TPD + c] = ok ? make_float2(h2f(x), -8.0f * h2f(x >> 16)) : make_float2(0.0f, 0.0f);
-      }
-    }
-    if (lane < 8) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[lane] = 0u;
-    return;
-  }
-  const int nwi = stage_word_insts(p);
-  for (int k = w; k < nwi; k += kOrdWaves) {
-    const int i = 64 * k + lane;
-    const int c = i & (TP - 1), b = i >> p.tp_log2;
-    if (b < nb) {
-      const bool ok = c < nc && b < p.Kb;
-      const uint32_t x = raw[i];
-      dam[b * TPD + c] = ok ? make_float2(h2f(x), -8.0f * h2f(x >> 16)) : make_float2(0.0f, 0.0f);
-      if (c == TP - 1)
-        for (int cc = TP; cc < TPD; ++cc) dam[b * TPD + cc] = make_float2(0.0f, 0.0f);
-    }
-  }
+// The 32-byte zero slot that the A operands of lanes outside their k-group (or past the
+// columns) read. Every wave writes it before its own first read (the same zeros in all waves).
+__device__ __forceinline__ void stage_zero(const ReadArgs& p, unsigned char* smem, int lane) {
   if (lane < 8) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[lane] = 0u;
 }
 
@@ -881,7 +863,10 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
   constexpr int FMT = MODE == 3 ? 1 : MODE == 4 ? 2 : 0;    // weight format: Q4_0, Q8_0, Q4_1
   constexpr uint32_t kCodeBytes = FMT == 1 ? 2048u : 1024u;  // codes per chunk
   constexpr uint32_t kScaleBytes = FMT == 2 ? 256u : 128u;   // scales (Q4_1: d | m) per chunk
-  constexpr int kLoads = FMT == 1 ? 3 : 2;                   // loads per chunk and tile
+  // vector memory instructions per chunk and tile that are certain to be issued, which the
+  // staging wait counts (it may undercount, never overcount): the block-dot export does not
+  // use the weight scales, and the compiler drops their loads
+  constexpr int kLoads = (FMT == 1 ? 2 : 1) + (DOTS ? 0 : 1);
   extern __shared__ __align__(16) unsigned char smem[];
   // weight loads in flight per wave: a ring of D slots, each one chunk of NTM tiles
   constexpr int D = ring_depth(NTM);
@@ -893,12 +878,17 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
   const int cs0 = KC * w / kOrdWaves, cs1 = KC * (w + 1) / kOrdWaves;
   const int live = DOTS ? p.rows : clamp_live(p.live_rows, p.rows, nullptr);
   const int wgi = xcd_rank(blockIdx.x, gridDim.x);
-  const int t0 = (int)((int64_t)p.tiles_total * wgi / gridDim.x);
-  const int t1 = (int)((int64_t)p.tiles_total * (wgi + 1) / gridDim.x);
+  // this workgroup's half tiles [h0, h1) = [floor(H i / G), floor(H (i + 1) / G)) in 32-bit
+  // arithmetic (H = q G + r, r i < G^2); a slot is one tile, whole or one of its halves
+  // (the divisions go through the vector ALU: the results are made wave-uniform again)
+  const uint32_t G = gridDim.x;
+  const int h0 = __builtin_amdgcn_readfirstlane(p.half_q * wgi + (int)((uint32_t)p.half_r * (uint32_t)wgi / G));
+  const int h1 = __builtin_amdgcn_readfirstlane(p.half_q * (wgi + 1) +
+                                                (int)((uint32_t)p.half_r * (uint32_t)(wgi + 1) / G));
   float* red = reinterpret_cast<float*>(smem + p.lds_red);
 
   const int ncols = live;
-  if (ncols == 0 || t0 >= t1) return;
+  if (ncols == 0 || h0 >= h1) return;
 
   for (int c0 = 0; c0 < ncols; c0 += TP) {
     const int nc = ncols - c0 < TP ? ncols - c0 : TP;
@@ -907,32 +897,66 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
     // a_base + cs * a_step (low half, high half 16 bytes on), or the 32-byte zero slot
     // (a_step = 0) when the row is outside the lane's k-group or past the columns.
     const int m = n;
-    int a_base[2], a_step[2];
+    // The scale products go through f16 matrix-core products, exact in f32 (an f16 product
+    // has 22 significant bits): per token group the d_a d_w outer product of the chunk's
+    // blocks (A: d_a of image column 4 tg + (m & 3), block 4 cs + g, in k slot 4 g of row m
+    // when the row is in the lane's k-group, as for the codes; B: d_w of the lane's row and
+    // block in k slot 4 g), which lands in the lanes exactly as the block dots do; and per
+    // chunk the sums over its 4 blocks of s_a d_w (A: s_a of column m, block 4 cs + g, in k
+    // slot 4 g), accumulated over K. Their raw words (d_a | s_a << 16) are read in place, at
+    // base + idx * step with idx = the wave's step (8 columns per pass) or the chunk.
+    const bool own = stage_own(p);
+    const int wrd_base = own ? p.lds_raw + w * p.raw_wave + 4 * 8 * g : p.lds_raw + 4 * TP * g;
+    const int wrd_step = own ? 128 : 16 * TP;
+    int a_base[2], a_step[2], da_base[2], da_step[2];
 #pragma unroll
     for (int tg = 0; tg < 2; ++tg) {
       const int col = 4 * tg + (m & 3);
       const bool on = (m >> 2) == g && col < nc;
       a_base[tg] = on ? (g * TP + col) * 32 : p.lds_zero;
       a_step[tg] = on ? 4 * TP * 32 : 0;
+      da_base[tg] = on ? wrd_base + 4 * col : p.lds_zero;
+      da_step[tg] = on ? wrd_step : 0;
     }
-    // d_a, -8 s_a pairs of this lane's block: [block][tpd] float2, block 4 cs + g
-    const int dam_base = p.lds_da + g * p.tpd * 8, dam_step = 4 * p.tpd * 8;
-    for (int tb = t0; tb < t1; tb += NTM) {
-      const int nt = t1 - tb < NTM ? t1 - tb : NTM;
-      // per tile: buffer resources over its reader's code and scale planes, and the byte
-      // offsets of its first chunk (the same in every lane); the lanes add 16 * lane and
-      // 2 * lane
-      __amdgpu_buffer_rsrc_t rq[NTM], rd[NTM];
-      uint32_t oq[NTM], od[NTM];
-      int rl[NTM], rr[NTM];
+    const int sa_base = m < nc ? wrd_base + 4 * m + 2 : p.lds_zero;
+    const int sa_step = m < nc ? wrd_step : 0;
+    for (int hb = h0; hb < h1;) {
+      // the next NTM slots: slot t is tile lt[t] of reader rr[t], rows [lo[t], hi[t]) of it
+      int rr[NTM], lts[NTM], lo[NTM], hi[NTM];
+      int nt = 0, hn = hb;
 #pragma unroll
       for (int t = 0; t < NTM; ++t) {
-        const int tile = tb + (t < nt ? t : nt - 1);  // idle slots re-read the last tile
-        int ri = 0;
-        while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
-        const int lt = tile - p.tile_start[ri];
-        rr[t] = ri;
+        if (hn < h1) {
+          int ri = 0;
+          while (ri + 1 < p.n_readers && hn >= p.half_start[ri + 1]) ++ri;
+          const int lh = hn - p.half_start[ri];
+          const bool both = (lh & 1) == 0 && hn + 1 < h1 && hn + 1 < p.half_start[ri + 1];
+          rr[t] = ri;
+          lts[t] = lh >> 1;
+          lo[t] = 8 * (lh & 1);
+          hi[t] = both ? 16 : lo[t] + 8;
+          hn += both ? 2 : 1;
+          ++nt;
+        } else {  // idle slots (t > 0 here) re-read the last slot
+          const int u = t > 0 ? t - 1 : 0;
+          rr[t] = rr[u];
+          lts[t] = lts[u];
+          lo[t] = lo[u];
+          hi[t] = hi[u];
+        }
+      }
+      // per slot: buffer resources over its reader's code and scale planes, the byte offsets
+      // of its first chunk (the same in every lane), and the lane's offset in a chunk: 16 bytes
+      // per lane (row n, block g) as laid out; in a half slot the lanes of the other half read
+      // the lines of this half again (no traffic of their own; their rows are not stored)
+      __amdgpu_buffer_rsrc_t rq[NTM], rd[NTM];
+      uint32_t oq[NTM], od[NTM], lq[NTM];
+      int rl[NTM];
+#pragma unroll
+      for (int t = 0; t < NTM; ++t) {
+        const int ri = rr[t], lt = lts[t];
         rl[t] = lt * 16 + n;  // this lane's weight row in reader ri
+        lq[t] = 16u * (uint32_t)(16 * g + (hi[t] - lo[t] == 16 ? n : (lo[t] | (n & 7))));
         const uint32_t chunk0 = (uint32_t)lt * (uint32_t)KC;
         const uint32_t chunks = (uint32_t)p.r[ri].tiles * (uint32_t)KC;
         rq[t] = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].qs, (short)0, (int)(chunks * kCodeBytes),
@@ -943,10 +967,13 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
         od[t] = chunk0 * kScaleBytes;
       }
       float acc[NTM][8];
+      v4f sacc[NTM];  // sum over blocks of s_a d_w (Q4_1: of s_a m_w): lane (n, g) column 4 g + v
 #pragma unroll
-      for (int t = 0; t < NTM; ++t)
+      for (int t = 0; t < NTM; ++t) {
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[t][v] = 0.0f;
+        sacc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      }
 
       uint4 q[D][NTM], q2[FMT == 1 ? D : 1][NTM];  // q2: Q8_0's second 16 bytes per block
       uint32_t dsc[D][NTM];
@@ -958,29 +985,28 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       // value alive and defeat the exact wait counts); a slot past the wave's last chunk
       // repeats that chunk (its lines are in flight or cached), never used. The chunk part of
       // the address is the same in every lane.
-      const uint32_t lq = 16u * lane, ld2 = 2u * lane, ld4 = 4u * lane;
       auto load = [&](int j, int st) {
         const uint32_t cs = (uint32_t)chunk_of(st < nst ? st : nst - 1);
 #pragma unroll
         for (int t = 0; t < NTM; ++t) {
-          const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq, oq[t] + cs * kCodeBytes, 0);
+          const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq[t], oq[t] + cs * kCodeBytes, 0);
           q[j][t] = make_uint4(x.x, x.y, x.z, x.w);
           if constexpr (FMT == 1) {
-            const v4u x2 = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq, oq[t] + cs * kCodeBytes + 1024u, 0);
+            const v4u x2 = __builtin_amdgcn_raw_buffer_load_b128(rq[t], lq[t], oq[t] + cs * kCodeBytes + 1024u, 0);
             q2[j][t] = make_uint4(x2.x, x2.y, x2.z, x2.w);
           }
           if constexpr (FMT == 2)
-            dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b32(rd[t], ld4, od[t] + cs * kScaleBytes, 0);
+            dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b32(rd[t], lq[t] >> 2, od[t] + cs * kScaleBytes, 0);
           else
-            dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b16(rd[t], ld2, od[t] + cs * kScaleBytes, 0);
+            dsc[j][t] = __builtin_amdgcn_raw_buffer_load_b16(rd[t], lq[t] >> 3, od[t] + cs * kScaleBytes, 0);
         }
       };
       // One chunk of NTM tiles: all matrix-core products first (for every tile slot; an idle
       // slot repeats the last tile and its sums are never stored), then the scaling, so no
       // VALU instruction waits on a product issued just before it.
-      auto compute = [&](int j, int cs) {
+      auto compute = [&](int j, int cs, int st) {
         v4i blo[NTM], bhi[NTM];
-        float dw[NTM], mw[NTM];
+        v4h bw[NTM], bm[NTM];  // (d_w, 0, 0, 0) and (m_w, 0, 0, 0) at k slot 4 g
 #pragma unroll
         for (int t = 0; t < NTM; ++t) {
           if constexpr (FMT == 1) {  // Q8_0: elements 0..15 and 16..31 are the two 16-byte halves
@@ -998,66 +1024,59 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
             bhi[t][2] = (int)((q[j][t].z >> 4) & 0x0f0f0f0fu);
             bhi[t][3] = (int)((q[j][t].w >> 4) & 0x0f0f0f0fu);
           }
-          dw[t] = h2f(dsc[j][t]);
-          mw[t] = FMT == 2 ? h2f(dsc[j][t] >> 16) : 0.0f;
+          bw[t] = as_v4h((uint64_t)(FMT == 2 ? dsc[j][t] & 0xffffu : dsc[j][t]));
+          bm[t] = as_v4h((uint64_t)(dsc[j][t] >> 16));
         }
         const int blk = 4 * cs + g;  // this lane's block
-        const unsigned char* dam = smem + dam_base + cs * dam_step;
-        {
-          v4i dd[NTG][NTM];
+        const int idx = own ? st : cs;
+        v4i dd[NTG][NTM];
+        v4f dwda[NTG][NTM];
 #pragma unroll
-          for (int tg = 0; tg < NTG; ++tg) {
-            const unsigned char* ap = smem + a_base[tg] + cs * a_step[tg];
-            const v4i alo = *reinterpret_cast<const v4i*>(ap);
-            const v4i ahi = *reinterpret_cast<const v4i*>(ap + 16);
+        for (int tg = 0; tg < NTG; ++tg) {
+          const unsigned char* ap = smem + a_base[tg] + cs * a_step[tg];
+          const v4i alo = *reinterpret_cast<const v4i*>(ap);
+          const v4i ahi = *reinterpret_cast<const v4i*>(ap + 16);
+          const v4h ada = as_v4h((uint64_t)*reinterpret_cast<const uint16_t*>(smem + da_base[tg] + idx * da_step[tg]));
 #pragma unroll
-            for (int t = 0; t < NTM; ++t) {
-              const v4i zero = {0, 0, 0, 0};
-              dd[tg][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[t], zero, 0, 0, 0);
-              dd[tg][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[t], dd[tg][t], 0, 0, 0);
-            }
+          for (int t = 0; t < NTM; ++t) {
+            const v4i zero = {0, 0, 0, 0};
+            dd[tg][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[t], zero, 0, 0, 0);
+            dd[tg][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[t], dd[tg][t], 0, 0, 0);
+            if constexpr (!DOTS)
+              dwda[tg][t] = __builtin_amdgcn_mfma_f32_16x16x16f16(ada, bw[t], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
           }
+        }
+        if constexpr (!DOTS && FMT != 1) {
+          const v4h asa = as_v4h((uint64_t)*reinterpret_cast<const uint16_t*>(smem + sa_base + idx * sa_step));
 #pragma unroll
-          for (int tg = 0; tg < NTG; ++tg) {
-            const float4 dm0 = *reinterpret_cast<const float4*>(dam + 32 * tg);       // cols 0, 1
-            const float4 dm1 = *reinterpret_cast<const float4*>(dam + 32 * tg + 16);  // cols 2, 3
-            const float4 da4 = make_float4(dm0.x, dm0.z, dm1.x, dm1.z);
-            const float4 ms4 = make_float4(dm0.y, dm0.w, dm1.y, dm1.w);
+          for (int t = 0; t < NTM; ++t)
+            sacc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(asa, FMT == 2 ? bm[t] : bw[t], sacc[t], 0, 0, 0);
+        }
 #pragma unroll
-            for (int t = 0; t < NTM; ++t) {
-              const v4i d = dd[tg][t];
-              if constexpr (DOTS) {
-                if (t < nt && rl[t] < p.r[0].N && blk < p.Kb) {
+        for (int tg = 0; tg < NTG; ++tg) {
 #pragma unroll
-                  for (int v = 0; v < 4; ++v) {
-                    const int col = c0 + 4 * tg + v;
-                    if (4 * tg + v < nc)
-                      p.sumi[((int64_t)col * p.r[0].N + rl[t]) * p.Kb + blk] = d[v];
-                  }
+          for (int t = 0; t < NTM; ++t) {
+            const v4i d = dd[tg][t];
+            if constexpr (DOTS) {
+              if (t < nt && n >= lo[t] && n < hi[t] && rl[t] < p.r[0].N && blk < p.Kb) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  const int col = c0 + 4 * tg + v;
+                  if (4 * tg + v < nc)
+                    p.sumi[((int64_t)col * p.r[0].N + rl[t]) * p.Kb + blk] = d[v];
                 }
-              } else if constexpr (FMT == 0) {  // d_w (d_a sumi - 8 s_a)
-                acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.x, (float)d[0], ms4.x), acc[t][4 * tg + 0]);
-                acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.y, (float)d[1], ms4.y), acc[t][4 * tg + 1]);
-                acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.z, (float)d[2], ms4.z), acc[t][4 * tg + 2]);
-                acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], __builtin_fmaf(da4.w, (float)d[3], ms4.w), acc[t][4 * tg + 3]);
-              } else if constexpr (FMT == 1) {  // d_w d_a sumi
-                acc[t][4 * tg + 0] = __builtin_fmaf(dw[t], da4.x * (float)d[0], acc[t][4 * tg + 0]);
-                acc[t][4 * tg + 1] = __builtin_fmaf(dw[t], da4.y * (float)d[1], acc[t][4 * tg + 1]);
-                acc[t][4 * tg + 2] = __builtin_fmaf(dw[t], da4.z * (float)d[2], acc[t][4 * tg + 2]);
-                acc[t][4 * tg + 3] = __builtin_fmaf(dw[t], da4.w * (float)d[3], acc[t][4 * tg + 3]);
-              } else {  // d_w d_a sumi + m_w s_a, s_a = -(-8 s_a) / 8 (exact)
-                acc[t][4 * tg + 0] = __builtin_fmaf(mw[t], -0.125f * ms4.x, __builtin_fmaf(dw[t], da4.x * (float)d[0], acc[t][4 * tg + 0]));
-                acc[t][4 * tg + 1] = __builtin_fmaf(mw[t], -0.125f * ms4.y, __builtin_fmaf(dw[t], da4.y * (float)d[1], acc[t][4 * tg + 1]));
-                acc[t][4 * tg + 2] = __builtin_fmaf(mw[t], -0.125f * ms4.z, __builtin_fmaf(dw[t], da4.z * (float)d[2], acc[t][4 * tg + 2]));
-                acc[t][4 * tg + 3] = __builtin_fmaf(mw[t], -0.125f * ms4.w, __builtin_fmaf(dw[t], da4.w * (float)d[3], acc[t][4 * tg + 3]));
               }
+            } else {  // (d_w d_a) sumi
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                acc[t][4 * tg + v] = __builtin_fmaf(dwda[tg][t][v], (float)d[v], acc[t][4 * tg + v]);
             }
           }
         }
       };
       // Stage the image columns (first tile group of a column pass): the copies go out before
       // the wave's first weight loads, and the wait below covers the copies alone.
-      const bool stage = tb == t0;
+      const bool stage = hb == h0;
       if (stage) {
         if (c0 > 0) __syncthreads();  // every wave is done with the previous pass's columns
         stage_dma_issue(p, smem, c0, nc, w, lane);
@@ -1070,18 +1089,30 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
         wait_vmcnt<0>();
       }
       if (stage) {
-        stage_convert(p, smem, nc, w, lane);
-        if (!stage_own(p)) __syncthreads();
+        stage_zero(p, smem, lane);
+        if (!own) __syncthreads();
       }
       for (int base = 0; base < nst; base += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
           load((j + D - 1) % D, base + j + D - 1);
-          if (base + j < nst) compute(j, chunk_of(base + j));
+          if (base + j < nst) compute(j, chunk_of(base + j), base + j);
           __builtin_amdgcn_sched_barrier(0);  // keep each step's LDS operands local to it
         }
       }
       if constexpr (!DOTS) {
+        // the s_a terms: -8 d_w s_a (Q4_0) or + m_w s_a (Q4_1), column 4 g + v in lanes g = 0, 1
+        if constexpr (FMT != 1) {
+          const float coef = FMT == 2 ? 1.0f : -8.0f;
+          const float f0 = g == 0 ? coef : 0.0f, f1 = g == 1 ? coef : 0.0f;
+#pragma unroll
+          for (int t = 0; t < NTM; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              acc[t][v] = __builtin_fmaf(f0, sacc[t][v], acc[t][v]);
+              if constexpr (NTG == 2) acc[t][4 + v] = __builtin_fmaf(f1, sacc[t][v], acc[t][4 + v]);
+            }
+        }
         // the four k-group lanes of a row: (g0 + g1) + (g2 + g3)
 #pragma unroll
         for (int t = 0; t < NTM; ++t)
@@ -1106,11 +1137,12 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
         __syncthreads();
         for (int o = threadIdx.x; o < nt * 128; o += blockDim.x) {
           const int t = o >> 7, nn = (o >> 3) & 15, col = o & 7;
-          if (col < nc) {
-            const int tile = tb + t;
-            int ri = 0;
-            while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
-            const int row = (tile - p.tile_start[ri]) * 16 + nn;
+          int ri = rr[0], lt = lts[0], rlo = lo[0], rhi = hi[0];
+#pragma unroll
+          for (int u = 1; u < NTM; ++u)
+            if (t == u) ri = rr[u], lt = lts[u], rlo = lo[u], rhi = hi[u];
+          if (col < nc && nn >= rlo && nn < rhi) {
+            const int row = lt * 16 + nn;
             if (row < p.r[ri].N) {
               float s = red[(t * 16 + nn) * 8 + col];
               for (int ww = 1; ww < kOrdWaves; ++ww) s = s + red[((ww * NTM + t) * 16 + nn) * 8 + col];
@@ -1120,6 +1152,7 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
         }
         __syncthreads();
       }
+      hb = hn;
     }
   }
 }
@@ -1145,10 +1178,6 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 constexpr int kMmqWaves = 4;
 constexpr int kMmqMinRows = 64;  // Q4_0 readers of this many image rows or more use this kernel
 typedef long v1l;
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ v4h as_v4h(uint64_t x) { return __builtin_bit_cast(v4h, x); }
 
 // The scales go through f16 products (exact in f32): per block the outer product
 // d_w[row] d_a[image row] (k slot b of an f16 product whose other slots are zero), and per
@@ -1888,30 +1917,28 @@ struct ReadPlan {
 };
 
 // LDS layout of the ordinary reader: staged codes [4 KC][tp][32] (padded to whole 1 KB copy
-// instructions), raw scale words [4 KC][tp] (padded to 256 B instructions), (d_a, -8 s_a)
-// pairs [4 KC][tpd] of f32, a 32-byte zero slot, cross-wave sums [waves][ntm][16][8] f32. tp
-// is the widest of 8, 4, 2, 1 image columns per pass that fits.
+// instructions), raw scale words (d_a | s_a << 16) [4 KC][tp] (padded to 256 B instructions),
+// or with 8 columns per pass 32 words per step in a run per wave, a 32-byte zero slot,
+// cross-wave sums [waves][ntm][16][8] f32. tp is the widest of 8, 4, 2, 1 image columns per
+// pass that fits.
 inline bool plan_lds(ReadArgs& a, int ntm, int* total) {
   const int nb = 4 * a.KC;
   for (int tp : {8, 4, 2, 1}) {
-    const int tpd = tp > 4 ? tp : 4;
     const int codes = (nb * tp * 2 + 63) / 64 * 1024;
     int raw = (nb * tp + 63) / 64 * 256;
-    if (tp == 8) {  // per-wave scale-word slots: 8 per 16 chunks (see stage_own)
-      const int own = (a.KC + 15) / 16 * 8 * 256;
-      if (own > raw) raw = own;
+    a.raw_wave = 0;
+    if (tp == 8 && kInterleaveChunks) {  // per-wave runs of 32 words per step (see stage_own)
+      const int steps = (a.KC + kOrdWaves - 1) / kOrdWaves;
+      a.raw_wave = (steps + 1) / 2 * 256;
+      raw = kOrdWaves * a.raw_wave;
     }
-    const int dsz = nb * tpd * 8;
     const int red = kOrdWaves * ntm * 16 * 8 * 4;
-    const int t = codes + raw + dsz + 32 + red;
+    const int t = codes + raw + 32 + red;
     if (t <= kMaxLds) {
       a.tp = tp;
       a.tp_log2 = tp == 8 ? 3 : tp == 4 ? 2 : tp == 2 ? 1 : 0;
-      a.tpd = tpd;
       a.lds_raw = codes;
-      a.lds_da = codes + raw;
-      a.lds_ms = 0;  // unused: d_a and -8 s_a are interleaved at lds_da
-      a.lds_zero = a.lds_da + dsz;
+      a.lds_zero = codes + raw;
       a.lds_red = a.lds_zero + 32;
       *total = t;
       return true;
@@ -1949,15 +1976,38 @@ inline int ntm_for(int64_t tiles_per_wg) {
   return tiles_per_wg <= 1 ? 1 : tiles_per_wg <= 2 ? 2 : tiles_per_wg <= 3 ? 3 : 4;
 }
 
-// Ordinary readers: one workgroup per CU (fewer when there are fewer tiles); each takes a
-// contiguous run of tiles over the concatenated readers.
+// Ordinary readers: one workgroup per CU (fewer when there are fewer half tiles); each takes an
+// equal contiguous run of half tiles (8 weight rows) over the concatenated readers, so that no
+// workgroup streams more than its share (640 tiles on 256 CUs: 2.5 tiles each, not 3 and 2).
 template <int MODE>
 int run_ordinary(ReadArgs& a, hipStream_t s) {
-  const int tiles = a.tile_start[a.n_readers];
+  int halves = 0;
+  for (int i = 0; i < a.n_readers; ++i) {
+    a.half_start[i] = halves;
+    halves += (a.r[i].N + 7) / 8;
+  }
+  a.half_start[a.n_readers] = halves;
+  a.halves_total = halves;
+  a.tiles_total = a.tile_start[a.n_readers];
   int G = cu_count();
-  if (tiles < G) G = tiles;
-  a.tiles_total = tiles;
-  const int ntm = ntm_for((tiles + G - 1) / G);
+  if (halves < G) G = halves;
+  a.half_q = halves / G;
+  a.half_r = halves % G;
+  // the most slots (whole or half tiles) any workgroup's run of half tiles covers, as the
+  // kernel walks it
+  int most = 1;
+  for (int wg = 0; wg < G; ++wg) {
+    const int h0 = a.half_q * wg + (int)((uint32_t)a.half_r * (uint32_t)wg / (uint32_t)G);
+    const int h1 = a.half_q * (wg + 1) + (int)((uint32_t)a.half_r * (uint32_t)(wg + 1) / (uint32_t)G);
+    int slots = 0, ri = 0;
+    for (int h = h0; h < h1; ++slots) {
+      while (ri + 1 < a.n_readers && h >= a.half_start[ri + 1]) ++ri;
+      const int lh = h - a.half_start[ri];
+      h += ((lh & 1) == 0 && h + 1 < h1 && h + 1 < a.half_start[ri + 1]) ? 2 : 1;
+    }
+    if (slots > most) most = slots;
+  }
+  const int ntm = ntm_for(most);
   int lds = 0;
   if (!plan_lds(a, ntm, &lds)) return QIMG_EUNSUPPORTED;
   return launch_read<MODE>(a, G, ntm, lds, s);

@@ -187,10 +187,13 @@ def test_blockdots_bit_exact(K, T):
     img = O.quantize(y)
     w = W.q4_0_weights(g, (N,), K)
     wt = qimg.tile_q4_0(H.dev(w.qs), H.dev(w.d), K)
-    sumi = H.torch().full((T, N, K // 32), -1, dtype=H.torch().int32, device="cuda")
-    qimg.blockdots(wt, N, H.dev(img), T, K, sumi)
-    sync()
-    assert np.array_equal(H.host(sumi), O.blockdots(w.qs, K, img, T, T))
+    ref = O.blockdots(w.qs, K, img, T, T)
+    # repeated: a staged image read before its copies land differs only now and then
+    for _ in range(4 if K <= 2592 else 1):
+        sumi = H.torch().full((T, N, K // 32), -1, dtype=H.torch().int32, device="cuda")
+        qimg.blockdots(wt, N, H.dev(img), T, K, sumi)
+        sync()
+        assert np.array_equal(H.host(sumi), ref)
 
 
 @pytest.mark.parametrize("N,K,E", [(37, 2592, 1), (768, 2560, 3), (16, 32, 2)])
@@ -270,7 +273,10 @@ def test_ordinary_geglu_full_size():
     check_ordinary(wl, img_o, run_readers(wl, img), nmse=False)
 
 
-@pytest.mark.parametrize("K,T,Ns", [(32, 1, [5]), (2592, 13, [37, 64, 3]), (32768, 2, [9]), (2048, 8, [1, 300])])
+# the last two: more half tiles (8 weight rows) than workgroups, readers with an odd number of
+# half tiles, so that workgroup runs start and end inside tiles and at reader boundaries
+@pytest.mark.parametrize("K,T,Ns", [(32, 1, [5]), (2592, 13, [37, 64, 3]), (32768, 2, [9]), (2048, 8, [1, 300]),
+                                    (2592, 8, [4100, 2056, 4100]), (4096, 3, [2049, 8, 2055])])
 def test_ordinary_edge_shapes(K, T, Ns):
     g = np.random.default_rng(K * 7 + T)
     x = g.standard_normal((T, K)).astype(np.float32)
