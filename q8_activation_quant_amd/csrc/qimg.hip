@@ -902,7 +902,9 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
     // blocks (A: d_a of image column 4 tg + (m & 3), block 4 cs + g, in k slot 4 g of row m
     // when the row is in the lane's k-group, as for the codes; B: d_w of the lane's row and
     // block in k slot 4 g), which lands in the lanes exactly as the block dots do; and per
-    // chunk the sums over its 4 blocks of s_a d_w (A: s_a of column m, block 4 cs + g, in k
+    // chunk the sums over its 4 blocks of s_a d_w (A: s_a of column 2 (m >> 2) + (m & 3) for
+    // m & 3 < 2, block 4 cs + g, in k slot 4 g: the sums land where the epilogue's lane
+    // reduction leaves each column)
     // slot 4 g), accumulated over K. Their raw words (d_a | s_a << 16) are read in place, at
     // base + idx * step with idx = the wave's step (8 columns per pass) or the chunk.
     const bool own = stage_own(p);
@@ -918,8 +920,10 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       da_base[tg] = on ? wrd_base + 4 * col : p.lds_zero;
       da_step[tg] = on ? wrd_step : 0;
     }
-    const int sa_base = m < nc ? wrd_base + 4 * m + 2 : p.lds_zero;
-    const int sa_step = m < nc ? wrd_step : 0;
+    const int s_col = 2 * (m >> 2) + (m & 3);
+    const bool s_on = (m & 3) < 2 && s_col < nc;
+    const int sa_base = s_on ? wrd_base + 4 * s_col + 2 : p.lds_zero;
+    const int sa_step = s_on ? wrd_step : 0;
     for (int hb = h0; hb < h1;) {
       // the next NTM slots: slot t is tile lt[t] of reader rr[t], rows [lo[t], hi[t]) of it
       int rr[NTM], lts[NTM], lo[NTM], hi[NTM];
@@ -1101,39 +1105,34 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
         }
       }
       if constexpr (!DOTS) {
-        // the s_a terms: -8 d_w s_a (Q4_0) or + m_w s_a (Q4_1), column 4 g + v in lanes g = 0, 1
-        if constexpr (FMT != 1) {
-          const float coef = FMT == 2 ? 1.0f : -8.0f;
-          const float f0 = g == 0 ? coef : 0.0f, f1 = g == 1 ? coef : 0.0f;
+        // The four k-group lanes of a row, reduced and scattered: a swap of the lanes 32 apart
+        // carries columns c and c + 4 at once (lanes g < 2 keep column c, g >= 2 column c + 4,
+        // summed over g and g + 2), then a swap of the lanes 16 apart carries two of those
+        // (lane g ends with columns 2 g and 2 g + 1, summed over all four); then the s_a term
+        // of those columns: -8 sum d_w s_a (Q4_0) or + sum m_w s_a (Q4_1).
+        float part[NTM][2];
 #pragma unroll
-          for (int t = 0; t < NTM; ++t)
+        for (int t = 0; t < NTM; ++t) {
+          float h[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              acc[t][v] = __builtin_fmaf(f0, sacc[t][v], acc[t][v]);
-              if constexpr (NTG == 2) acc[t][4 + v] = __builtin_fmaf(f1, sacc[t][v], acc[t][4 + v]);
-            }
-        }
-        // the four k-group lanes of a row: (g0 + g1) + (g2 + g3)
-#pragma unroll
-        for (int t = 0; t < NTM; ++t)
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            // v_permlane16_swap of a value with itself yields rows (r0 r0 r2 r2) and
-            // (r1 r1 r3 r3): their sum is the lane-xor-16 pair sum; likewise permlane32
-            const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[t][v]),
-                                                              __float_as_uint(acc[t][v]), false, false);
-            const float a16 = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-            const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a16),
-                                                              __float_as_uint(a16), false, false);
-            acc[t][v] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+          for (int c = 0; c < 4; ++c) {
+            const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[t][c]),
+                                                              __float_as_uint(acc[t][c + 4]), false, false);
+            h[c] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
           }
-        // lane (n, g) stores columns 2g, 2g+1 of its row for each tile
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(h[c]),
+                                                              __float_as_uint(h[c + 2]), false, false);
+            part[t][c] = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+            if constexpr (FMT != 1) part[t][c] = __builtin_fmaf(FMT == 2 ? 1.0f : -8.0f, sacc[t][c], part[t][c]);
+          }
+        }
+        // lane (n, g) stores columns 2g, 2g+1 of its row for each slot
 #pragma unroll
         for (int t = 0; t < NTM; ++t)
           if (t < nt)
-            *reinterpret_cast<float2*>(red + ((w * NTM + t) * 16 + n) * 8 + 2 * g) =
-                make_float2(g == 0 ? acc[t][0] : g == 1 ? acc[t][2] : g == 2 ? acc[t][4] : acc[t][6],
-                            g == 0 ? acc[t][1] : g == 1 ? acc[t][3] : g == 2 ? acc[t][5] : acc[t][7]);
+            *reinterpret_cast<float2*>(red + ((w * NTM + t) * 16 + n) * 8 + 2 * g) = make_float2(part[t][0], part[t][1]);
         __syncthreads();
         for (int o = threadIdx.x; o < nt * 128; o += blockDim.x) {
           const int t = o >> 7, nn = (o >> 3) & 15, col = o & 7;
