@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
+#include <type_traits>
 #include <string.h>
 
 #include "qimg.h"
@@ -840,7 +841,7 @@ __device__ __forceinline__ int xcd_rank(int i, int G) {
 
 // Weight loads in flight per wave (ring slots of one chunk of NTM tiles each).
 #ifndef QIMG_RING1
-#define QIMG_RING1 6
+#define QIMG_RING1 4
 #endif
 #ifndef QIMG_RING2
 #define QIMG_RING2 2
@@ -980,7 +981,11 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       }
 
       uint4 q[D][NTM], q2[FMT == 1 ? D : 1][NTM];  // q2: Q8_0's second 16 bytes per block
-      uint32_t dsc[D][NTM];
+      // the weight scales as loaded (16 bits; Q4_1 d | m << 16): kept at the loaded width, so
+      // that nothing is computed from a slot between its load and its use (a widening at the
+      // loop latch made the compiler wait there for every load in flight)
+      using ScaleT = typename std::conditional<FMT == 2, uint32_t, uint16_t>::type;
+      ScaleT dsc[D][NTM];
       // chunks of this wave: with kInterleave, w, w + 8, w + 16, ... (the workgroup's waves
       // read 8 consecutive chunks of a tile at each step); otherwise the range [cs0, cs1)
       const int nst = kInterleave ? (KC - w + kOrdWaves - 1) / kOrdWaves : cs1 - cs0;
@@ -1028,8 +1033,8 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
             bhi[t][2] = (int)((q[j][t].z >> 4) & 0x0f0f0f0fu);
             bhi[t][3] = (int)((q[j][t].w >> 4) & 0x0f0f0f0fu);
           }
-          bw[t] = as_v4h((uint64_t)(FMT == 2 ? dsc[j][t] & 0xffffu : dsc[j][t]));
-          bm[t] = as_v4h((uint64_t)(dsc[j][t] >> 16));
+          bw[t] = as_v4h((uint64_t)((uint32_t)dsc[j][t] & 0xffffu));
+          bm[t] = as_v4h((uint64_t)((uint32_t)dsc[j][t] >> 16));
         }
         const int blk = 4 * cs + g;  // this lane's block
         const int idx = own ? st : cs;
