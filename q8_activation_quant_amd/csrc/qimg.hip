@@ -1154,7 +1154,8 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
             }
           }
         }
-        __syncthreads();
+        // the cross-wave sums are reused by the next slot group or column pass, if any
+        if (hn < h1 || c0 + TP < ncols) __syncthreads();
       }
       hb = hn;
     }
