@@ -88,7 +88,10 @@ def test_format_reader_full_size(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_1"])
-@pytest.mark.parametrize("K,T,live,Ns", [(2592, 13, 11, (37, 16)), (32, 2, None, (5,)), (8192, 8, 3, (64, 24))])
+# the last: more half tiles (8 weight rows) than workgroups and readers with an odd number of
+# them, so that workgroup runs start and end inside tiles and at reader boundaries
+@pytest.mark.parametrize("K,T,live,Ns", [(2592, 13, 11, (37, 16)), (32, 2, None, (5,)), (8192, 8, 3, (64, 24)),
+                                         (2592, 8, None, (4100, 2056, 1032))])
 def test_format_reader_edge_shapes(fmt, K, T, live, Ns):
     g = np.random.default_rng(K + T + len(Ns))
     x = g.standard_normal((T, K)).astype(np.float32)
