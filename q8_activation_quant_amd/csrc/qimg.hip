@@ -562,8 +562,15 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
   const int C = p.K >> 2;
   // leaves of this workgroup: the whole row (RMS, whose sum needs it), or slice blockIdx.y of
   // W * 64 * JW leaves (the element-wise producers and the quantizer)
-  const int c_off = blockIdx.y * (W * 64 * JW);
+  const int c_off = OP == OP_RMS ? 0 : blockIdx.y * (W * 64 * JW);
   const float* arow = p.a + (int64_t)row * p.lda;
+  // RMS rows split over gridDim.y workgroups: each sums the whole row (in the same order, so
+  // every one gets the same scale) and normalizes, stores and quantizes only its share of the
+  // leaf groups (64 leaves, one wave's jj-th), so that the per-element work of a few rows is
+  // spread over many CUs
+  const int gps = OP == OP_RMS ? (W * JW) / (int)gridDim.y : 0;  // leaf groups per share
+  const int g_lo = gps * (int)blockIdx.y;
+  auto mine = [&](int jj) { return OP != OP_RMS || (unsigned)(w * JW + jj - g_lo) < (unsigned)gps; };
 
   // all input loads of the row go out at once (in bounds: leaves past K re-read leaf 0 and
   // are zeroed): x (or gate, or y) and gamma (or up)
@@ -575,8 +582,8 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
     const int cc = c < C ? c : 0;
     v[jj] = *reinterpret_cast<const float4*>(arow + 4 * cc);
     if (c >= C) v[jj] = make_float4(0, 0, 0, 0);
-    if (OP != OP_QUANT && brow) u[jj] = *reinterpret_cast<const float4*>(brow + 4 * cc);
-    if (OP == OP_RMS && p.beta) bt[jj] = *reinterpret_cast<const float4*>(p.beta + 4 * cc);
+    if (OP != OP_QUANT && brow && mine(jj)) u[jj] = *reinterpret_cast<const float4*>(brow + 4 * cc);
+    if (OP == OP_RMS && p.beta && mine(jj)) bt[jj] = *reinterpret_cast<const float4*>(p.beta + 4 * cc);
   }
 
   if constexpr (OP == OP_RMS) {
@@ -601,6 +608,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
     const float r = 1.0f / __builtin_sqrtf(mean + p.eps);
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
+      if (!mine(jj)) continue;
       const int c = c_off + lane + 64 * (w * JW + jj);
       float4 y;
       y.x = v[jj].x * r; y.y = v[jj].y * r; y.z = v[jj].z * r; y.w = v[jj].w * r;
@@ -638,7 +646,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
       const int c = c_off + lane + 64 * (w * JW + jj);
-      if (c < C) *reinterpret_cast<float4*>(yrow + 4 * c) = v[jj];
+      if (c < C && mine(jj)) *reinterpret_cast<float4*>(yrow + 4 * c) = v[jj];
     }
   }
 
@@ -646,7 +654,7 @@ __global__ __launch_bounds__(1024) void emit_kernel(EmitArgs p) {
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
       const int blk = (c_off >> 3) + 8 * (w * JW + jj) + (lane >> 3);
-      if (blk < p.Kb) quantize_leaf(v[jj], row, blk, lane, p);  // whole 8-lane groups agree
+      if (blk < p.Kb && mine(jj)) quantize_leaf(v[jj], row, blk, lane, p);  // whole 8-lane groups agree
     }
     // row padding blocks [Kb, RB) are zero bytes (written by the row's last slice)
     const int npad = blockIdx.y + 1 == gridDim.y ? p.RB - p.Kb : 0;
@@ -1869,6 +1877,11 @@ inline int launch_status() {
 // W = min(16, max(1, Jp/2)) waves, JW = Jp / W slots per lane.
 // The element-wise producers and the quantizer need no row-wide value: their rows are cut into
 // slices of at most 16 waves x 64 lanes x 1 leaf (4096 elements), one workgroup each.
+#ifndef QIMG_RMS_SPLIT
+#define QIMG_RMS_SPLIT 128
+#endif
+constexpr int kRmsSplitWgs = QIMG_RMS_SPLIT;  // RMS rows are split while rows x shares stay within this
+
 int launch_emit(int op, EmitArgs& a, hipStream_t s) {
   const int J = (a.K + 255) / 256;
   int W, JW, S = 1;
@@ -1879,6 +1892,10 @@ int launch_emit(int op, EmitArgs& a, hipStream_t s) {
     if (W < 1) W = 1;
     if (W > 16) W = 16;
     JW = Jp / W;
+    // few rows: split each row's per-element work over S workgroups (powers of two, at least
+    // two leaf groups each, about one workgroup per CU in all)
+    const int groups = W * JW;
+    while (S * 2 <= groups / 2 && (int64_t)a.rows * S * 2 <= kRmsSplitWgs) S *= 2;
   } else {
     W = J < 16 ? J : 16;
     JW = 1;
