@@ -1880,7 +1880,11 @@ inline int launch_status() {
 #ifndef QIMG_RMS_SPLIT
 #define QIMG_RMS_SPLIT 128
 #endif
-constexpr int kRmsSplitWgs = QIMG_RMS_SPLIT;  // RMS rows are split while rows x shares stay within this
+constexpr int kRmsSplitWgs = QIMG_RMS_SPLIT;
+#ifndef QIMG_ELT_WAVES
+#define QIMG_ELT_WAVES 4
+#endif
+constexpr int kEltWaves = QIMG_ELT_WAVES;  // waves per workgroup of the element-wise producers  // RMS rows are split while rows x shares stay within this
 
 int launch_emit(int op, EmitArgs& a, hipStream_t s) {
   const int J = (a.K + 255) / 256;
@@ -1897,7 +1901,7 @@ int launch_emit(int op, EmitArgs& a, hipStream_t s) {
     const int groups = W * JW;
     while (S * 2 <= groups / 2 && (int64_t)a.rows * S * 2 <= kRmsSplitWgs) S *= 2;
   } else {
-    W = J < 16 ? J : 16;
+    W = J < kEltWaves ? J : kEltWaves;
     JW = 1;
     S = (J + W - 1) / W;
   }
