@@ -203,9 +203,10 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(RouterArgs a) {
   const int nt = live - t0 < 8 ? live - t0 : 8;
   const int C = a.K >> 2;
   // leaves past K re-read leaf 0 (in bounds) and count as +0; experts past E re-read expert e0
-  // and rows past the live count re-read row t0 (their results are not stored). With one
-  // expert per workgroup (long rows) the activation leaves are loaded row by row.
-  constexpr int XT = EB > 1 ? 8 : 1;
+  // and rows past the live count re-read row t0 (their results are not stored). All 8 rows'
+  // activation leaves are loaded at once (one round trip) unless the rows are long (more than
+  // 2 leaves per lane), then row by row.
+  constexpr int XT = (EB > 1 || JW <= 2) ? 8 : 1;
   float4 wv[EB][JW], xv[XT][JW];
   auto load_x = [&](int t, float4 (&dst)[JW]) {
     const float* xr = a.x + (int64_t)(t0 + (t < nt ? t : 0)) * a.ldx;
@@ -301,11 +302,13 @@ __device__ __forceinline__ void key_max_pair(uint32_t& hi, uint32_t& lo, bool ha
   lo = second ? l[1] : l[0];
 }
 
+// PER keys per lane: E <= 64 PER (the launch picks the smallest power of two that holds E)
+template <int PER>
 __global__ __launch_bounds__(64) void moe_topk_kernel(TopkArgs a) {
   const int t = blockIdx.x;
   if (t >= clamp_live(a.live_rows, a.rows, nullptr)) return;
   const int lane = threadIdx.x;
-  constexpr int kPer = QIMG_MAX_EXPERTS / 64;
+  constexpr int kPer = PER;
   const float* lr = a.logits + (int64_t)t * a.ldl;
   uint32_t key[kPer];
 #pragma unroll
@@ -2560,7 +2563,14 @@ int qimg_moe_topk(const float* logits, int64_t ldl, int32_t E, int32_t bucket,
   if (overlap(si, sl) || overlap(si, sv) || overlap(sw, sl) || overlap(sw, sv) || overlap(si, sw))
     return QIMG_EALIAS;
   TopkArgs a{logits, ldl, live_rows, ids, weights, bucket, E, top_k};
-  hipLaunchKernelGGL(moe_topk_kernel, dim3((unsigned)bucket), dim3(64), 0, (hipStream_t)stream, a);
+  const dim3 grid((unsigned)bucket), block(64);
+  hipStream_t st = (hipStream_t)stream;
+  static_assert(QIMG_MAX_EXPERTS <= 64 * 16, "top-k keys per lane");
+  if (E <= 64) hipLaunchKernelGGL(moe_topk_kernel<1>, grid, block, 0, st, a);
+  else if (E <= 128) hipLaunchKernelGGL(moe_topk_kernel<2>, grid, block, 0, st, a);
+  else if (E <= 256) hipLaunchKernelGGL(moe_topk_kernel<4>, grid, block, 0, st, a);
+  else if (E <= 512) hipLaunchKernelGGL(moe_topk_kernel<8>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(moe_topk_kernel<16>, grid, block, 0, st, a);
   return launch_status();
 }
 
