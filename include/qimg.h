@@ -206,7 +206,9 @@ typedef struct {
  *   sumi = sum_{j<16} (qs[n][b][j] & 15) * c[t][b][j] + (qs[n][b][j] >> 4) * c[t][b][j+16]
  * (qs, d_w: the reader's weights in standard order; the reader takes them tiled) for image
  * rows t < live (live as above; rows = image rows). Rows t >= live of every out are not
- * written. Outputs must not overlap each other, the image or the weights.
+ * written. Outputs must not overlap each other, the image or the weights. A reader's tiled
+ * code plane (N*K/2 bytes, rounded up to whole tiles and chunks; Q8_0: N*K) must stay under
+ * 4 GiB (QIMG_EUNSUPPORTED otherwise).
  */
 int mmvq_q4_0_q8_1(const qimg_q4_0_reader* readers, int32_t n_readers, const void* img,
                    int32_t rows, const int32_t* live_rows, int32_t K, void* stream);

@@ -2326,6 +2326,8 @@ static int ordinary_common(int fmt, const qimg_q4_0_reader* readers, int32_t n_r
   for (int i = 0; i < n_readers; ++i) {
     const qimg_q4_0_reader& r = readers[i];
     if (!r.w || !r.out || r.N <= 0 || r.ldo < r.N) return QIMG_EINVAL;
+    // the mat-vec readers address a reader's code plane with 32-bit buffer offsets
+    if (tiled_chunks(r.N, K, 1) * (fmt == 1 ? 2048 : 1024) > (int64_t)0xffffffff) return QIMG_EUNSUPPORTED;
     if (!al16(r.w) || !al(r.out, 4)) return QIMG_EALIGN;
     outs[i] = span(r.out, rows_extent(rows, r.ldo, r.N, 4));
     for (int j = 0; j < n_readers; ++j)

@@ -181,6 +181,11 @@ def test_mmvq_validation(L):
     assert L.mmvq_q4_0_q8_1(readers((A, 0, C, 64)), 1, D, 4, None, 256, S) == qimg.EINVAL
     assert L.mmvq_q4_0_q8_1(readers((None, 64, C, 64)), 1, D, 4, None, 256, S) == qimg.EINVAL
     assert L.mmvq_q4_0_q8_1(readers((A + 8, 64, C, 64)), 1, D, 4, None, 256, S) == qimg.EALIGN
+    # a code plane of 4 GiB or more (32-bit buffer offsets)
+    big = 262144  # rows: 16384 tiles x 256 chunks x 1 KB = 4 GiB at K = 32768
+    assert L.mmvq_q4_0_q8_1(readers((A, big, C, big)), 1, D, 4, None, 32768, S) == qimg.EUNSUPPORTED
+    assert L.mmvq_q8_0_q8_1(readers((A, big // 2, C, big)), 1, D, 4, None, 32768, S) == qimg.EUNSUPPORTED
+    assert L.mmvq_q4_1_q8_1(readers((A, big, C, big)), 1, D, 4, None, 32768, S) == qimg.EUNSUPPORTED
     assert L.mmvq_q4_0_q8_1(readers((A, 64, C + 2, 64)), 1, D, 4, None, 256, S) == qimg.EALIGN
     # output over the weights, the image, the live count or another output
     assert L.mmvq_q4_0_q8_1(readers((A, 64, A + 64, 64)), 1, D, 4, None, 256, S) == qimg.EALIAS
