@@ -315,7 +315,7 @@ def cpu_baseline(wl, budget_s=20.0):
             else:
                 O.mmvq_fmt(r.fmt, r.qs, r.d, r.m, K, img, T, L)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() + times[-1] > t_end or len(times) >= 5:
+        if time.perf_counter() + times[-1] > t_end or len(times) >= 24:
             break
     return float(np.median(times)) * 1e6, len(times)
 
