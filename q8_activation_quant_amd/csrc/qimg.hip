@@ -1877,13 +1877,18 @@ inline int launch_status() {
 }
 
 // Producer launch shape: Jp = next power of two >= ceil(K/256) leaf slots per lane;
-// W = min(16, max(1, Jp/2)) waves, JW = Jp / W slots per lane.
+// W = min(kRmsWaves, max(1, Jp/2)) waves, or Jp/8 where that is more, JW = Jp / W slots per
+// lane (at most 8).
 // The element-wise producers and the quantizer need no row-wide value: their rows are cut into
-// slices of at most 16 waves x 64 lanes x 1 leaf (4096 elements), one workgroup each.
+// slices of at most kEltWaves waves x 64 lanes x 1 leaf (256 elements a wave), one workgroup each.
 #ifndef QIMG_RMS_SPLIT
 #define QIMG_RMS_SPLIT 128
 #endif
 constexpr int kRmsSplitWgs = QIMG_RMS_SPLIT;
+#ifndef QIMG_RMS_WAVES
+#define QIMG_RMS_WAVES 8
+#endif
+constexpr int kRmsWaves = QIMG_RMS_WAVES;  // RMS producer waves per workgroup, up to K = 16384
 #ifndef QIMG_ELT_WAVES
 #define QIMG_ELT_WAVES 4
 #endif
@@ -1895,9 +1900,12 @@ int launch_emit(int op, EmitArgs& a, hipStream_t s) {
   if (op == OP_RMS) {
     int Jp = 1;
     while (Jp < J) Jp <<= 1;
+    // 8 waves of 2 to 8 leaves per lane (the sum's order does not depend on the split); 16
+    // waves only where a lane would otherwise hold more than 8 leaves (K above 16384)
     W = Jp / 2;
     if (W < 1) W = 1;
-    if (W > 16) W = 16;
+    if (W > kRmsWaves) W = kRmsWaves;
+    if (Jp / W > 8) W = Jp / 8;
     JW = Jp / W;
     // few rows: split each row's per-element work over S workgroups (powers of two, at least
     // two leaf groups each, about one workgroup per CU in all)
