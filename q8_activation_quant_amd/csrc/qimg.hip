@@ -9,15 +9,21 @@
 //        experts" (TensorFold PR #1047): What this changes, Receipt.
 //
 // Kernels
-//   emit_kernel<OP,JW>       one workgroup per live row: (RMS reduction) -> f32 output -> per
-//                            32-block Q8_1 quantization, all in one pass over the row.
+//   emit_kernel<OP,JW>       producers, per live row (RMS: a few rows each split over several
+//                            workgroups that all take the same row sum; element-wise ops: row
+//                            slices): (RMS reduction) -> f32 output -> per 32-block Q8_1
+//                            quantization, all in one pass.
 //   mmvq_tiled_kernel<N,M,G> ordinary Q4_0 x Q8_1 readers on the matrix cores
 //                            (v_mfma_i32_16x16x64_i8) over tiled weights, the live image rows as
 //                            columns; M = 2: block-dot export; M = 3, 4: Q8_0, Q4_1 weights.
-//   mmvq_routed_kernel<N,U>  routed readers: the plan of the live pairs built in LDS by every
-//                            workgroup, then (expert, pass, tile) units streamed over full K.
+//   mmq_kernel               prefill reader for many image rows (v_mfma_i32_16x16x32_i8).
+//   mmvq_routed_kernel<N,U,P> routed readers: the plan of the live pairs built in LDS by every
+//                            workgroup (or read from a plan launch), then (expert, pass, tile)
+//                            units streamed over full K.
+//   moe_router_kernel, moe_topk_kernel, moe_combine_kernel: the rest of a routed MoE FFN.
 //   tile_weights_kernel<F>   one-time reordering of standard Q4_0 / Q8_0 / Q4_1 planes into
 //                            reader tiles.
+//   eval_math_kernel<FN>     the producers' scalar math over ranges of f32 inputs (a check hook).
 //
 // Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off (no fast-math), so every float
 // operation written here is one IEEE binary32 operation with round-to-nearest-even; f32
@@ -439,7 +445,9 @@ __device__ __forceinline__ float geglu_quick_act(float g) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Producer: one workgroup per live row.
+// Producer: workgroups of live rows (RMS: a whole row, or for few rows the same row in several
+// workgroups that each take the whole row's sum and finish a share of it; element-wise ops: row
+// slices of up to kEltWaves waves).
 // Element mapping: leaf c covers elements 4c..4c+3; lane l of wave w holds leaves
 // c = l + 64 j for j in [w*JW, (w+1)*JW). A 32-element block is 8 consecutive leaves, i.e. 8
 // consecutive lanes at the same j, so the block amax and code sum are 3-step lane reductions.
