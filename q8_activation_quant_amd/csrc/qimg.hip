@@ -1969,6 +1969,7 @@ struct ReadPlan {
 inline bool plan_lds(ReadArgs& a, int ntm, int* total) {
   const int nb = 4 * a.KC;
   for (int tp : {8, 4, 2, 1}) {
+    if (tp > 1 && tp / 2 >= a.rows) continue;  // a narrower pass holds every image row
     const int codes = (nb * tp * 2 + 63) / 64 * 1024;
     int raw = (nb * tp + 63) / 64 * 256;
     a.raw_wave = 0;
