@@ -1916,9 +1916,9 @@ int launch_emit(int op, EmitArgs& a, hipStream_t s) {
     if (Jp / W > 8) W = Jp / 8;
     JW = Jp / W;
     // few rows: split each row's per-element work over S workgroups (powers of two, at least
-    // two leaf groups each, about one workgroup per CU in all)
+    // one leaf group each, at most kRmsSplitWgs workgroups in all)
     const int groups = W * JW;
-    while (S * 2 <= groups / 2 && (int64_t)a.rows * S * 2 <= kRmsSplitWgs) S *= 2;
+    while (S * 2 <= groups && (int64_t)a.rows * S * 2 <= kRmsSplitWgs) S *= 2;
   } else {
     W = J < kEltWaves ? J : kEltWaves;
     JW = 1;
