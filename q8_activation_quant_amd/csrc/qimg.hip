@@ -1890,7 +1890,7 @@ inline int launch_status() {
 // The element-wise producers and the quantizer need no row-wide value: their rows are cut into
 // slices of at most kEltWaves waves x 64 lanes x 1 leaf (256 elements a wave), one workgroup each.
 #ifndef QIMG_RMS_SPLIT
-#define QIMG_RMS_SPLIT 128
+#define QIMG_RMS_SPLIT 256
 #endif
 constexpr int kRmsSplitWgs = QIMG_RMS_SPLIT;
 #ifndef QIMG_RMS_WAVES
