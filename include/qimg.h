@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 10
+#define QIMG_ABI_VERSION 11
 
 /* status codes */
 #define QIMG_OK 0
@@ -121,9 +121,19 @@ int64_t qimg_image_bytes(int32_t rows, int32_t K);
  *   gamma : f32 [K], 16-byte aligned, or NULL
  *   y     : f32 [rows][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= K; must not overlap x,
  *           gamma or img
- *   img   : qimg_image_bytes(rows, K) bytes, 16-byte aligned, or NULL
+ *   img   : qimg_image_bytes(rows, K) bytes, 16-byte aligned, or NULL; must not overlap y or
+ *           live_rows (QIMG_EALIAS). An img that overlaps the producer's inputs is declined
+ *           (below).
  *   live_rows : device int32, or NULL
  * Rows >= live are not read and not written.
+ *
+ * Declined emission ([P1] Coverage: unsafe input/output aliases keep the original
+ * preparation). Emitting while the producer runs is unsafe when img overlaps one of its inputs
+ * (x, gamma, beta; gate, up for the GLU producers), since workgroups still reading an input
+ * would see image bytes. Such a call is not rejected: it enqueues the original two steps on
+ * `stream`, the producer writing y alone and then the separate quantizer (qimg_quantize_q8_1)
+ * reading y into img, and returns QIMG_OK. The bytes of y and img are those of an emitting
+ * call on non-overlapping buffers. This holds for every producer entry point below.
  */
 int qimg_emit_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps, int32_t rows,
                       const int32_t* live_rows, int32_t K, float* y, int64_t ldy, void* img,
@@ -251,30 +261,6 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
                       size_t workspace_bytes, void* stream);
 
 /*
- * The routing plan as a launch of its own, and routed readers that take it from the workspace
- * ([P3] What this changes: the plan covers the live rows' pairs only; launches stay sized for
- * the bucket). The plan depends on the ids and the live count alone, so it can run beside the
- * producer (another stream, or a parallel branch of a graph) and serve several routed launches
- * over the same ids (the gate/up and the down projections of an MoE FFN).
- *   mmvq_id_plan: writes the plan and the error word into workspace exactly as
- *     mmvq_id_q4_0_q8_1 does (same layout, same errors); one workgroup.
- *   mmvq_id_q4_0_q8_1_ex: mmvq_id_q4_0_q8_1 with flags:
- *     QIMG_ID_PER_SLOT - the image holds one row per pair (mmvq_id_q4_0_q8_1_per_slot);
- *     QIMG_ID_PLANNED  - read the plan from workspace (written by mmvq_id_plan, or by a routed
- *                        reader call, over the same ids and live count, and ordered before
- *                        this call); ids are then not read and workspace is not written.
- *   Unknown flag bits: QIMG_EINVAL.
- */
-#define QIMG_ID_PER_SLOT 1
-#define QIMG_ID_PLANNED 2
-int mmvq_id_plan(const int32_t* ids, int32_t bucket, int32_t top_k, const int32_t* live_rows,
-                 int32_t E, void* workspace, size_t workspace_bytes, void* stream);
-int mmvq_id_q4_0_q8_1_ex(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
-                         const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
-                         const int32_t* live_rows, int32_t K, void* workspace,
-                         size_t workspace_bytes, int32_t flags, void* stream);
-
-/*
  * The rest of a routed MoE FFN after the gate and up projections ([P1] Coverage: GLU
  * producers emit images, routed MUL_MAT_ID readers on MMVQ, per-slot routed projections;
  * [P3] What this changes: padding rows get no expert work and no combine, their outputs stay
@@ -317,9 +303,12 @@ int qimg_moe_combine(const float* x, int64_t ld_pair, const float* weights, cons
  *
  * qimg_moe_router: logits[t*ldl + e] = sum over k < K of x[t*ldx + k] * w[e*K + k] for live
  *   rows t (t < *live_rows clamped to [0, bucket]; all rows when live_rows is NULL), in a
- *   fixed order: 4-element fma leaves, lane l of 64 adding leaves l + 64 j in ascending j,
- *   then a pairwise tree over the 64 lanes (so the logits, and every pick made from them,
- *   are reproducible bit for bit).
+ *   fixed order: leaf c = fma(x3,w3, fma(x2,w2, fma(x1,w1, x0*w0))) over elements 4c..4c+3;
+ *   lane l of 64 owns leaves c = l + 64 j, j < Jp (Jp = the next power of two >= ceil(K/256),
+ *   missing leaves +0) and sums them by a balanced pairwise tree over j; the 64 lane sums are
+ *   then added by a balanced pairwise tree over the lanes. This is the RMS producer's sum of
+ *   squares with products in place of squares, so the logits, and every pick made from them,
+ *   are reproducible bit for bit whatever the launch shape.
  *   x: f32, 16-byte aligned, ldx % 4 == 0, ldx >= K (the kept f32 output of a producer is the
  *   usual input); w: f32 [E][K], 16-byte aligned; logits: f32 [bucket][ldl], ldl >= E, must not
  *   overlap x, w or live_rows. K: as for the producers.
@@ -336,6 +325,19 @@ int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int3
 int qimg_moe_topk(const float* logits, int64_t ldl, int32_t E, int32_t bucket,
                   const int32_t* live_rows, int32_t top_k, int32_t* ids, float* weights,
                   void* stream);
+
+/*
+ * Extra floating reader of a producer's kept f32 output ([P1] Coverage: every original F32
+ * store remains, including live outputs and extra floating readers). For live rows t (as for
+ * qimg_moe_router) and n < N:
+ *   out[t*ldo + n] = sum over k < K of y[t*ldy + k] * v[n*K + k]
+ * in qimg_moe_router's fixed order (so the result is reproducible bit for bit); the same
+ * kernel, named for a consumer that reads y in f32 beside the Q8_1 readers of its image.
+ *   y: f32, 16-byte aligned, ldy % 4 == 0, ldy >= K; v: f32 [N][K], 16-byte aligned;
+ *   out: f32 [rows][ldo], ldo >= N, must not overlap y, v or live_rows. K: as for the producers.
+ */
+int qimg_f32_reader(const float* y, int64_t ldy, const float* v, int32_t N, int32_t rows,
+                    const int32_t* live_rows, int32_t K, float* out, int64_t ldo, void* stream);
 
 /*
  * Prefill readers: Q4_0 x Q8_1 over many image rows (a prompt's tokens) on the matrix cores,

@@ -18,7 +18,7 @@
 //                            columns; M = 2: block-dot export; M = 3, 4: Q8_0, Q4_1 weights.
 //   mmq_kernel               prefill reader for many image rows (v_mfma_i32_16x16x32_i8).
 //   mmvq_routed_kernel<N,U,P> routed readers: the plan of the live pairs built in LDS by every
-//                            workgroup (or read from a plan launch), then (expert, pass, tile)
+//                            workgroup, then (expert, pass, tile)
 //                            units streamed over full K.
 //   moe_router_kernel, moe_topk_kernel, moe_combine_kernel: the rest of a routed MoE FFN.
 //   tile_weights_kernel<F>   one-time reordering of standard Q4_0 / Q8_0 / Q4_1 planes into
@@ -1376,10 +1376,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// PM (plan mode): 0 builds the plan and streams; 1 builds the plan, writes it to the
-// workspace and stops (one workgroup); 2 takes the plan from the workspace (written by a
-// plan-mode-1 launch over the same ids and live count) and streams.
-template <int NTM, int KU, int PM>
+template <int NTM, int KU>
 __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int sh_wave[3][kWaves];
@@ -1402,15 +1399,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   int32_t* mem = tmp + p.pairs_cap;                                // [pairs_cap]
 
   // ---- plan ----
-  if constexpr (PM == 2) {  // counts from the workspace; offsets, active experts and units below
-    const int32_t* counts = p.ws + 4;
-    for (int e = tid; e < E; e += blockDim.x) fill[e] = counts[e];
-    if (tid < 4) {
-      sh_misc[tid] = 0;
-      reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;
-    }
-    __syncthreads();
-  } else {
   for (int e = tid; e < E; e += blockDim.x) fill[e] = 0;
   if (tid < 4) {
     sh_misc[tid] = 0;
@@ -1425,7 +1413,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   }
   if (nbad) atomicAdd(&sh_misc[0], nbad);
   __syncthreads();
-  }
   {
     const int per = (E + (int)blockDim.x - 1) / (int)blockDim.x;
     const int e0 = tid * per;
@@ -1475,11 +1462,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     }
   }
   __syncthreads();
-  if constexpr (PM == 2) {
-    const int32_t* members = p.ws + 4 + 2 * E + 1;
-    for (int q = tid; q < off[E]; q += blockDim.x) mem[q] = members[q];
-    __syncthreads();
-  } else {
   for (int e = tid; e < E; e += blockDim.x) fill[e] = 0;
   __syncthreads();
   for (int pi = tid; pi < P; pi += blockDim.x) {
@@ -1513,8 +1495,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       p.ws[3] = 0;
       offsets[E] = nvalid;
     }
-  }
-  if constexpr (PM == 1) return;
   }
 
   // ---- work ----
@@ -2062,7 +2042,7 @@ int run_ordinary(ReadArgs& a, hipStream_t s) {
 // Routed readers: one workgroup per CU over the (expert, pass, tile) units. LDS: `slots`
 // staged segments of [4 KC][tp][32] codes + [4 KC][8] d_a + [4 KC][8] -8 s_a, the zero slot,
 // then the plan arrays off[E+1], fill[E], act[E], ust[E+1], tmp[pairs], mem[pairs].
-int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s, int pm = 0) {
+int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   const int tiles = a.tile_start[a.n_readers];
   a.tiles_total = tiles;
   a.pairs_cap = pairs_cap;
@@ -2089,26 +2069,11 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s, int pm = 0) {
     if (lds >= 0) break;
   }
   if (lds < 0) return QIMG_EUNSUPPORTED;
-  if (pm == 1) {  // the plan alone: one workgroup, plan arrays only
-    a.lds_zero = 0;
-    a.lds_plan = 16;
-    const int plds = 16 + plan;
-    const void* fp = (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 1>;
-    if (plds > 64 * 1024 &&
-        hipFuncSetAttribute(fp, hipFuncAttributeMaxDynamicSharedMemorySize, plds) != hipSuccess)
-      return QIMG_EHIP;
-    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 1>), dim3(1), dim3(kWaves * 64), plds, s, a);
-    return launch_status();
-  }
-  const void* fn = pm == 2 ? (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 2>
-                           : (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 0>;
+  const void* fn = (const void*)mmvq_routed_kernel<kRoutedNtm, kRoutedKu>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
-  if (pm == 2)
-    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 2>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
-  else
-    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu, 0>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
+  hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedNtm, kRoutedKu>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
   return launch_status();
 }
 
@@ -2168,21 +2133,30 @@ static int emit_common(int op, const float* a, int64_t lda, const float* b, int6
   const Span si = img ? span(img, ib) : Span{0, 0};
   const Span sl = live_rows ? span(live_rows, 4) : Span{0, 0};
   const Span sbeta = ex.beta ? span(ex.beta, (int64_t)K * 4) : Span{0, 0};
-  for (Span out : {sy, si}) {
-    if (overlap(out, sa) || overlap(out, sb) || overlap(out, sl) || overlap(out, sbeta))
-      return QIMG_EALIAS;
-  }
-  if (overlap(sy, si)) return QIMG_EALIAS;
+  if (overlap(sy, sa) || overlap(sy, sb) || overlap(sy, sl) || overlap(sy, sbeta) ||
+      overlap(si, sl) || overlap(sy, si))
+    return QIMG_EALIAS;
+  // an image over the producer's own inputs: emission declined, the original two steps run
+  const bool decline = overlap(si, sa) || overlap(si, sb) || overlap(si, sbeta);
+  if (decline && op == OP_QUANT) return QIMG_EALIAS;  // the quantizer's input is y itself
 
   EmitArgs e{};
   e.a = a; e.lda = lda; e.b = b; e.ldb = ldb; e.y = y; e.ldy = ldy;
   const int RB = row_blocks(K);
-  e.codes = (uint8_t*)img;
-  e.ds = img ? (uint32_t*)((uint8_t*)img + (size_t)rows * RB * 32) : nullptr;
+  uint8_t* codes = (uint8_t*)img;
+  uint32_t* ds = img ? (uint32_t*)((uint8_t*)img + (size_t)rows * RB * 32) : nullptr;
+  e.codes = decline ? nullptr : codes;
+  e.ds = decline ? nullptr : ds;
   e.live_rows = live_rows; e.rows = rows; e.K = K; e.Kb = K / 32; e.RB = RB; e.eps = eps;
   e.live_mul = live_mul;
   e.beta = ex.beta; e.scale = ex.scale; e.alpha = ex.alpha; e.limit = ex.limit;
-  return launch_emit(op, e, (hipStream_t)stream);
+  st = launch_emit(op, e, (hipStream_t)stream);
+  if (st || !decline) return st;
+  EmitArgs q{};
+  q.a = y; q.lda = ldy; q.codes = codes; q.ds = ds;
+  q.live_rows = live_rows; q.rows = rows; q.K = K; q.Kb = K / 32; q.RB = RB;
+  q.live_mul = live_mul; q.scale = 1.0f;
+  return launch_emit(OP_QUANT, q, (hipStream_t)stream);
 }
 
 int qimg_emit_rmsnorm(const float* x, int64_t ldx, const float* gamma, float eps, int32_t rows,
@@ -2409,7 +2383,7 @@ size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E) {
 static int routed_common(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
                          const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
                          const int32_t* live_rows, int32_t K, void* workspace,
-                         size_t workspace_bytes, int per_slot, void* stream, int pm = 0) {
+                         size_t workspace_bytes, int per_slot, void* stream) {
   int st = check_k(K);
   if (st) return st;
   if (!readers || n_readers < 1 || n_readers > QIMG_MAX_READERS || E <= 0 || bucket < 0 ||
@@ -2463,46 +2437,7 @@ static int routed_common(const qimg_q4_0_expert_reader* readers, int32_t n_reade
   a.top_k = top_k;
   a.img_div = per_slot ? 1 : top_k;
   a.E = E;
-  return run_routed(a, (int)pairs, (hipStream_t)stream, pm);
-}
-
-int mmvq_id_q4_0_q8_1_ex(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
-                         const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
-                         const int32_t* live_rows, int32_t K, void* workspace,
-                         size_t workspace_bytes, int32_t flags, void* stream) {
-  if (flags & ~(QIMG_ID_PER_SLOT | QIMG_ID_PLANNED)) return QIMG_EINVAL;
-  return routed_common(readers, n_readers, E, img, ids, bucket, top_k, live_rows, K, workspace,
-                       workspace_bytes, (flags & QIMG_ID_PER_SLOT) ? 1 : 0, stream,
-                       (flags & QIMG_ID_PLANNED) ? 2 : 0);
-}
-
-int mmvq_id_plan(const int32_t* ids, int32_t bucket, int32_t top_k, const int32_t* live_rows,
-                 int32_t E, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!ids || E <= 0 || bucket < 0 || top_k <= 0) return QIMG_EINVAL;
-  if (bucket == 0) return QIMG_OK;
-  const int64_t pairs = (int64_t)bucket * top_k;
-  if (pairs > QIMG_MAX_ROUTED_PAIRS || E > QIMG_MAX_EXPERTS) return QIMG_EUNSUPPORTED;
-  if (!workspace || workspace_bytes < mmvq_id_workspace_bytes(bucket, top_k, E))
-    return QIMG_EWORKSPACE;
-  if (!al16(workspace) || !al(ids, 4) || (live_rows && !al(live_rows, 4))) return QIMG_EALIGN;
-  const Span sw = span(workspace, (int64_t)mmvq_id_workspace_bytes(bucket, top_k, E));
-  if (overlap(sw, span(ids, pairs * 4)) || (live_rows && overlap(sw, span(live_rows, 4))))
-    return QIMG_EALIAS;
-  ReadArgs a{};
-  a.n_readers = 1;
-  a.tile_start[0] = 0;
-  a.tile_start[1] = 1;  // the plan does not depend on the readers; one nominal tile
-  a.Kb = 1;
-  a.KC = 1;
-  a.RB = 16;
-  a.rows = bucket;
-  a.live_rows = live_rows;
-  a.ids = ids;
-  a.ws = (int32_t*)workspace;
-  a.top_k = top_k;
-  a.img_div = top_k;
-  a.E = E;
-  return run_routed(a, (int)pairs, (hipStream_t)stream, 1);
+  return run_routed(a, (int)pairs, (hipStream_t)stream);
 }
 
 int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
@@ -2521,8 +2456,10 @@ int mmvq_id_q4_0_q8_1_per_slot(const qimg_q4_0_expert_reader* readers, int32_t n
                        workspace_bytes, 1, stream);
 }
 
-int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int32_t bucket,
-                    const int32_t* live_rows, int32_t K, float* logits, int64_t ldl, void* stream) {
+// logits[t][e] = x[t] . w[e] for live rows t in the router's fixed order (the router and the
+// extra f32 reader run this one kernel)
+static int f32_rows_dot(const float* x, int64_t ldx, const float* w, int32_t E, int32_t bucket,
+                        const int32_t* live_rows, int32_t K, float* logits, int64_t ldl, void* stream) {
   int st = check_k(K);
   if (st) return st;
   if (!x || !w || !logits || E <= 0 || bucket < 0 || ldx < K || ldl < E) return QIMG_EINVAL;
@@ -2564,6 +2501,16 @@ int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int3
     }
   }
   return launch_status();
+}
+
+int qimg_moe_router(const float* x, int64_t ldx, const float* w, int32_t E, int32_t bucket,
+                    const int32_t* live_rows, int32_t K, float* logits, int64_t ldl, void* stream) {
+  return f32_rows_dot(x, ldx, w, E, bucket, live_rows, K, logits, ldl, stream);
+}
+
+int qimg_f32_reader(const float* y, int64_t ldy, const float* v, int32_t N, int32_t rows,
+                    const int32_t* live_rows, int32_t K, float* out, int64_t ldo, void* stream) {
+  return f32_rows_dot(y, ldy, v, N, rows, live_rows, K, out, ldo, stream);
 }
 
 int qimg_moe_topk(const float* logits, int64_t ldl, int32_t E, int32_t bucket,

@@ -19,7 +19,7 @@ GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF, "reglu": GLU_REGLU,
            "geglu_quick": GLU_GEGLU_QUICK, "swiglu_oai": GLU_SWIGLU_OAI, "swiglu_clamp": GLU_SWIGLU_CLAMP}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
@@ -29,9 +29,8 @@ EXPORTS = (
     "qimg_emit_glu_per_slot", "mmvq_id_q4_0_q8_1_per_slot", "qimg_moe_combine",
     "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex", "qimg_moe_router", "qimg_moe_topk",
     "qimg_q8_0_tiled_bytes", "qimg_q4_1_tiled_bytes", "qimg_q8_0_tile", "qimg_q4_1_tile",
-    "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1", "mmq_q4_0_q8_1", "mmvq_id_plan", "mmvq_id_q4_0_q8_1_ex",
+    "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1", "mmq_q4_0_q8_1", "qimg_f32_reader",
 )
-ID_PER_SLOT, ID_PLANNED = 1, 2
 MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7, "reglu": 8,
             "geglu": 9, "geglu_quick": 10, "swiglu_oai_gate": 11}
 
@@ -93,9 +92,7 @@ def lib() -> ctypes.CDLL:
             "mmvq_q8_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "mmvq_q4_1_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "mmq_q4_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
-            "mmvq_id_plan": (ctypes.c_int, [P, i32, i32, P, i32, P, ctypes.c_size_t, P]),
-            "mmvq_id_q4_0_q8_1_ex": (ctypes.c_int, [ctypes.POINTER(ExpertReader), i32, i32, P, P, i32, i32, P,
-                                                    i32, P, ctypes.c_size_t, i32, P]),
+            "qimg_f32_reader": (ctypes.c_int, [P, i64, P, i32, i32, P, i32, P, i64, P]),
             "qimg_moe_topk": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -252,23 +249,6 @@ def _pair_ld(t):
     return t.stride(1)
 
 
-def mmvq_id_plan(ids, E, workspace, live_rows=None, stream=None):
-    """The routing plan of ids [bucket, top_k] (live rows only) into workspace."""
-    bucket, top_k = ids.shape
-    _check(lib().mmvq_id_plan(_ptr(ids), bucket, top_k, _ptr(live_rows), E, _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(stream)), "mmvq_id_plan")
-
-
-def mmvq_id_ex(readers, E, img, ids, live_rows, K, workspace, flags, stream=None):
-    """Routed readers with QIMG_ID_* flags (per-slot image, plan taken from the workspace)."""
-    bucket, top_k = ids.shape
-    arr = _readers(readers, ExpertReader)
-    _check(lib().mmvq_id_q4_0_q8_1_ex(arr, len(readers), E, _ptr(img), _ptr(ids), bucket, top_k,
-                                      _ptr(live_rows), K, _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), flags, _stream(stream)),
-           "mmvq_id_q4_0_q8_1_ex")
-
-
 def mmvq_id_per_slot(readers, E, img, ids, live_rows, K, workspace, stream=None):
     """Routed readers over a per-slot image (image row = pair): as mmvq_id, img has
     bucket*top_k rows."""
@@ -318,6 +298,15 @@ def moe_router(x, w, logits, live_rows=None, stream=None):
     E = w.shape[0]
     _check(lib().qimg_moe_router(_ptr(x), _ld(x), _ptr(w), E, bucket, _ptr(live_rows), K, _ptr(logits),
                                  _ld(logits), _stream(stream)), "qimg_moe_router")
+
+
+def f32_reader(y, v, out, live_rows=None, stream=None):
+    """out [rows, N] = y [rows, K] . v [N, K]^T for live rows: an extra f32 reader of a
+    producer's kept output (the router's fixed summation order)."""
+    rows, K = y.shape
+    N = v.shape[0]
+    _check(lib().qimg_f32_reader(_ptr(y), _ld(y), _ptr(v), N, rows, _ptr(live_rows), K, _ptr(out), _ld(out),
+                                 _stream(stream)), "qimg_f32_reader")
 
 
 def moe_topk(logits, ids, weights=None, live_rows=None, stream=None):

@@ -119,12 +119,7 @@ def test_down_per_slot(cfg, live, small):
     got = out.reshape(B * k, -1)
     P = L * k
     valid = (ids.reshape(-1)[:P] >= 0) & (ids.reshape(-1)[:P] < wl.E)
-    codes, da, sa = O.image_planes(img_o, B * k, F)
-    Kb = F // 32
-    ta = np.abs(H.f16(da[:, :Kb])) * 15 * np.abs(codes[:, :Kb].astype(np.float64)).sum(-1) + 8 * np.abs(H.f16(sa[:, :Kb]))
-    A = np.zeros_like(o64)
-    for p in np.flatnonzero(valid):
-        A[p] = np.abs(H.f16(wl.down.d[ids.reshape(-1)[p]])) @ ta[p]
+    A = H.routed_abs_sum(wl.down.qs, wl.down.d, wl.E, F, img_o, B * k, ids, L, per_slot=True)
     H.check_reader(got[:P][valid], o64[valid], A[valid], F, "per-slot down projection")
     assert (got[:P][~valid].view(np.uint8) == H.SENTINEL_BYTE).all(), "a skipped pair was written"
     assert (got[P:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding pairs were written"
@@ -438,95 +433,3 @@ def test_device_routed_chain_graph_replay():
             if t < L:
                 assert np.array_equal(ids[t], ref_ids), "live %d row %d picks" % (L, t)
                 assert np.array_equal(out[t].view(np.uint32), ref_out.view(np.uint32)), "live %d row %d" % (L, t)
-
-
-# ---- the plan as a launch of its own ----------------------------------------------------------
-@pytest.mark.parametrize("cfg,live", [(4, None), (5, 113), (5, 114), (5, 1)])
-def test_plan_launch_and_planned_readers(cfg, live):
-    # the plan launch writes the oracle's plan; readers that take it from the workspace give the
-    # same bytes as readers that build it themselves (token image and per-slot image)
-    from test_gpu_parity import check_plan
-    torch = H.torch()
-    wl = W.make(cfg, moe=True, live=live, small=True)
-    B, k, F = wl.T, wl.top_k, wl.n_ff
-    L = live_of(wl)
-    ids = H.dev(wl.ids)
-    lt = H.live_tensor(live) if live is not None else None
-    ws = torch.full((qimg.workspace_bytes(B, k, wl.E) // 4,), -7, dtype=torch.int32, device="cuda")
-    qimg.mmvq_id_plan(ids, wl.E, ws, lt)
-    sync()
-    check_plan(H.host(ws), wl.ids, L, wl.E, k)
-    _, img = gpu_glu_per_slot(wl, "swiglu", H.dev(wl.pair_gu).view(B, k, 2 * F), live)
-    x = H.dev(wl.x)
-    y = H.sentinel_f32(B, wl.K)
-    timg = H.sentinel_u8(qimg.image_bytes(B, wl.K))
-    qimg.emit_rmsnorm(x, H.dev(wl.gamma), W.EPS, y, timg, lt)
-    for flags, image, readers, K in ((0, timg, wl.readers, wl.K), (qimg.ID_PER_SLOT, img, [wl.down], F)):
-        outs = []
-        for fl in (flags, flags | qimg.ID_PLANNED):
-            specs, res = [], []
-            for r in readers:
-                N = r.d.shape[-2]
-                out = H.sentinel_f32(B, k, N)
-                specs.append((tiled(r, K), N, out))
-                res.append(out)
-            ws2 = torch.empty_like(ws)
-            if fl & qimg.ID_PLANNED:
-                ws2.copy_(ws)
-            qimg.mmvq_id_ex(specs, wl.E, image, ids, lt, K, ws2 if fl & qimg.ID_PLANNED else ws2, fl)
-            sync()
-            outs.append([H.host(o) for o in res])
-        for a, b in zip(*outs):
-            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "planned reader differs"
-
-
-def test_plan_beside_the_producer_in_a_graph():
-    # the plan on a second stream in parallel with the producer, joined before the planned
-    # readers; one graph replayed at changing live counts equals the one-launch readers
-    torch = H.torch()
-    wl = W.make(5, moe=True, small=True)
-    B, k = wl.T, wl.top_k
-    x = H.dev(wl.x)
-    gamma = H.dev(wl.gamma)
-    ids = H.dev(wl.ids)
-    live = H.live_tensor(B)
-    y = H.sentinel_f32(B, wl.K)
-    img = H.sentinel_u8(qimg.image_bytes(B, wl.K))
-    ws = torch.empty(qimg.workspace_bytes(B, k, wl.E) // 4, dtype=torch.int32, device="cuda")
-    ws_ref = torch.empty_like(ws)
-    N = wl.readers[0].d.shape[-2]
-    out = H.sentinel_f32(B, k, N)
-    ref = H.sentinel_f32(B, k, N)
-    w0 = tiled(wl.readers[0], wl.K)
-    side = torch.cuda.Stream()
-
-    def step():
-        cur = torch.cuda.current_stream()
-        side.wait_stream(cur)
-        with torch.cuda.stream(side):
-            qimg.mmvq_id_plan(ids, wl.E, ws, live)
-        qimg.emit_rmsnorm(x, gamma, W.EPS, y, img, live)
-        cur.wait_stream(side)
-        qimg.mmvq_id_ex([(w0, N, out)], wl.E, img, ids, live, wl.K, ws, qimg.ID_PLANNED)
-
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()
-    torch.cuda.current_stream().wait_stream(s)
-    sync()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for L in (1, 9, 113, 114, 128, 113, 9, 1):
-        live.fill_(L)
-        out.view(torch.uint8).fill_(H.SENTINEL_BYTE)
-        ref.view(torch.uint8).fill_(H.SENTINEL_BYTE)
-        sync()
-        g.replay()
-        sync()
-        qimg.mmvq_id([(w0, N, ref)], wl.E, img, ids, live, wl.K, ws_ref)
-        sync()
-        assert np.array_equal(H.host(out).view(np.uint32), H.host(ref).view(np.uint32)), "live %d" % L
-        used = 4 + 2 * wl.E + 1 + L * k  # the plan of the live pairs (later words are stale)
-        assert np.array_equal(H.host(ws)[:used], H.host(ws_ref)[:used]), "plan differs at live %d" % L

@@ -233,13 +233,9 @@ def run_readers(wl, img_host, rows=None, live=None):
 
 def check_ordinary(wl, img_o, outs, live=None, nmse=True):
     live = wl.T if live is None else live
-    codes, da, sa = O.image_planes(img_o, wl.T, wl.K)
-    Kb = wl.K // 32
     for i, (r, out) in enumerate(zip(wl.readers, outs)):
         o64 = O.mmvq(r.qs, r.d, wl.K, img_o, wl.T, live)
-        dw = np.abs(H.f16(r.d))
-        A = np.einsum("nb,tb->tn", dw, np.abs(H.f16(da[:live, :Kb])) * 15 * np.abs(codes[:live, :Kb].astype(np.float64)).sum(-1)
-                      + 8 * np.abs(H.f16(sa[:live, :Kb])))
+        A = H.reader_abs_sum(r.qs, r.d, wl.K, img_o, wl.T, live)
         H.check_reader(out[:live], o64, A, wl.K, "reader %d" % i)
         assert (out[live:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding rows of out written"
         if nmse:
@@ -257,20 +253,104 @@ def test_ordinary_small(config):
     check_ordinary(wl, img_o, run_readers(wl, img))
 
 
-@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("config", [1, 2])
 def test_ordinary_full_size(config):
     wl = W.make(config)
     print("ordinary full config", config, flush=True)
     y, img = run_producer(wl)
     _, img_o = check_producer(wl, y, img)
-    check_ordinary(wl, img_o, run_readers(wl, img), nmse=(config != 3))
+    check_ordinary(wl, img_o, run_readers(wl, img))
 
 
-def test_ordinary_geglu_full_size():
-    wl = W.make(3, glu_op="geglu_erf")
-    y, img = run_producer(wl)
-    _, img_o = check_producer(wl, y, img)
-    check_ordinary(wl, img_o, run_readers(wl, img), nmse=False)
+@pytest.mark.parametrize("op", ["swiglu", "geglu_erf"])
+def test_glu_workload_full_size_with_extra_f32_reader(op):
+    # the GLU workload at full size: producer, the Q4_0 down reader (NMSE against the float64
+    # activation included), then the kept f32 output is still the oracle's bit for bit and an
+    # extra f32 reader of it (a dot with a seeded vector) matches the oracle's fixed-order sum
+    # bit for bit and the float64 dot within its rounding bound
+    torch = H.torch()
+    wl = W.make(3, glu_op=op)
+    print("GLU workload full size", op, flush=True)
+    T, K = wl.T, wl.K
+    gu = H.dev(wl.gu)
+    y = H.sentinel_f32(T, K)
+    img = H.sentinel_u8(qimg.image_bytes(T, K))
+    qimg.emit_glu(op, gu[:, :K], gu[:, K:], y, img)
+    outs, specs = [], []
+    for r in wl.readers:
+        N = r.d.shape[-2]
+        out = H.sentinel_f32(T, N)
+        specs.append((qimg.tile_q4_0(H.dev(r.qs), H.dev(r.d), K), N, out))
+        outs.append(out)
+    qimg.mmvq(specs, img, T, K)
+    v = H.dev(wl.extra_v.reshape(1, K))
+    fo = H.sentinel_f32(T, 1)
+    qimg.f32_reader(y, v, fo)
+    sync()
+    y_h, img_h = H.host(y), H.host(img)
+    _, img_o = check_producer(wl, y_h, img_h)   # y read after both readers ran
+    check_ordinary(wl, img_o, [H.host(o) for o in outs])
+    y_o = H.oracle_producer(wl)[0]
+    f_o = O.moe_router(y_o, wl.extra_v.reshape(1, K), T)
+    got = H.host(fo)
+    assert np.array_equal(got.view(np.uint32), f_o.view(np.uint32)), "extra f32 reader differs"
+    exact = y_o.astype(np.float64) @ wl.extra_v.astype(np.float64)
+    J = -(-K // 256)
+    n = 3 + int(np.ceil(np.log2(J))) + 7
+    mag = np.abs(y_o.astype(np.float64)) @ np.abs(wl.extra_v.astype(np.float64))
+    bound = n * H.U / (1 - n * H.U) * mag + 2.0 ** -50 * mag
+    assert (np.abs(got[:, 0] - exact) <= bound).all()
+
+
+@pytest.mark.parametrize("live", [None, 5])
+def test_declined_emission_when_the_image_overlaps_the_inputs(live):
+    # an image placed over the producer's own input is not emitted in the same pass: the call
+    # runs the producer (y only) and then the separate quantizer, with the same bytes as an
+    # emitting call; image rows past the live count keep the input bytes they overlap
+    torch = H.torch()
+    T, K = 8, 2592
+    g = np.random.default_rng(2024)
+    x = g.standard_normal((T, K)).astype(np.float32)
+    gamma = g.normal(1.0, 0.1, K).astype(np.float32)
+    L = T if live is None else live
+    lt = H.live_tensor(live) if live is not None else None
+    nb = qimg.image_bytes(T, K)
+    RB = qimg.row_blocks(K)
+    # RMS: the image at the start of x's buffer
+    buf = H.dev(x).view(torch.uint8).reshape(-1)
+    before = H.host(buf).copy()
+    y = H.sentinel_f32(T, K)
+    qimg.emit_rmsnorm(buf.view(torch.float32).view(T, K), H.dev(gamma), W.EPS, y, buf[:nb], lt)
+    sync()
+    y_o = O.rmsnorm(x[:L], gamma, W.EPS)
+    img_o = O.quantize(y_o, img_rows=T)
+    img_h = H.host(buf)[:nb]
+    assert np.array_equal(H.host(y)[:L].view(np.uint32), y_o.view(np.uint32))
+    c, d = split_image(img_h, T, K)
+    co, do = split_image(img_o, T, K)
+    cb, db = split_image(before[:nb], T, K)
+    assert np.array_equal(c[:L], co[:L]) and np.array_equal(d[:L], do[:L]), "declined RMS image differs"
+    assert np.array_equal(c[L:], cb[L:]) and np.array_equal(d[L:], db[L:]), "padding image rows written"
+    # GLU: the image over the packed gate|up rows
+    gu = g.standard_normal((T, 2 * K)).astype(np.float32)
+    gbuf = H.dev(gu)
+    y2 = H.sentinel_f32(T, K)
+    qimg.emit_glu("swiglu", gbuf[:, :K], gbuf[:, K:], y2, gbuf.view(torch.uint8).reshape(-1)[:nb], lt)
+    sync()
+    yg_o = O.glu_ex(gu[:L, :K], gu[:L, K:], "swiglu")
+    assert np.array_equal(H.host(y2)[:L].view(np.uint32), yg_o.view(np.uint32))
+    gi = H.host(gbuf.view(torch.uint8).reshape(-1))[:nb]
+    c2, d2 = split_image(gi, T, K)
+    co2, do2 = split_image(O.quantize(yg_o, img_rows=T), T, K)
+    assert np.array_equal(c2[:L], co2[:L]) and np.array_equal(d2[:L], do2[:L]), "declined GLU image differs"
+    # the same bytes as the emitting path on separate buffers
+    y3 = H.sentinel_f32(T, K)
+    img3 = H.sentinel_u8(nb)
+    qimg.emit_rmsnorm(H.dev(x), H.dev(gamma), W.EPS, y3, img3, lt)
+    sync()
+    c3, d3 = split_image(H.host(img3), T, K)
+    assert np.array_equal(c3[:L], c[:L]) and np.array_equal(d3[:L], d[:L])
+    assert RB * 36 * T == nb
 
 
 # the last two: more half tiles (8 weight rows) than workgroups, readers with an odd number of
@@ -345,22 +425,19 @@ def check_plan(ws, ids, live, E, top_k):
     assert g_counts.sum() == P and (P == 0 or g_members.max() == P - 1)
 
 
-def check_routed(wl, img_o, outs, live, ids=None):
+def check_routed(wl, img_o, outs, live, ids=None, nmse=False):
     ids = wl.ids if ids is None else ids
-    codes, da, sa = O.image_planes(img_o, wl.T, wl.K)
-    Kb = wl.K // 32
     P = live * wl.top_k
-    flat_ids = ids.reshape(-1)[:P]
     for i, (r, out) in enumerate(zip(wl.readers, outs)):
         o64 = O.mmvq_id(r.qs, r.d, wl.E, wl.K, img_o, wl.T, ids, live)   # [P][N]
         got = out.reshape(-1, out.shape[-1])
-        A = np.empty_like(o64)
-        ta = np.abs(H.f16(da[:, :Kb])) * 15 * np.abs(codes[:, :Kb].astype(np.float64)).sum(-1) + 8 * np.abs(H.f16(sa[:, :Kb]))
-        for p in range(P):
-            e, t = flat_ids[p], p // wl.top_k
-            A[p] = np.abs(H.f16(r.d[e])) @ ta[t]
+        A = H.routed_abs_sum(r.qs, r.d, wl.E, wl.K, img_o, wl.T, ids, live)
         H.check_reader(got[:P], o64, A, wl.K, "routed reader %d" % i)
         assert (got[P:].view(np.uint8) == H.SENTINEL_BYTE).all(), "padding pairs were written"
+        if nmse and P:
+            ref = H.unquantized_routed_ref(wl, r.qs, r.d, live, ids)
+            e = H.nmse(got[:P], ref)
+            assert e <= 5e-4, "routed reader %d NMSE %.3g" % (i, e)
 
 
 def test_routed_config4_full():
@@ -370,7 +447,7 @@ def test_routed_config4_full():
     _, img_o = check_producer(wl, y, img)
     outs, ws = run_routed(wl, H.dev(img), wl.ids)
     check_plan(ws, wl.ids, wl.T, wl.E, wl.top_k)
-    check_routed(wl, img_o, outs, wl.T)
+    check_routed(wl, img_o, outs, wl.T, nmse=True)
 
 
 def test_routed_agrees_with_ordinary_reader_of_the_expert():
@@ -457,7 +534,7 @@ def test_padded_bucket(live):
     img_d = H.dev(img)
     outs, ws = run_routed(wl, img_d, wl.ids, live=live)
     check_plan(ws, wl.ids, live, wl.E, wl.top_k)
-    check_routed(wl, img_o, outs, live)
+    check_routed(wl, img_o, outs, live, nmse=True)
     # a different poison in the padding rows changes nothing
     x2 = wl.x.copy()
     W.poison_rows(x2, live, phase=1)
