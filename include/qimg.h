@@ -261,6 +261,24 @@ int mmvq_id_q4_0_q8_1(const qimg_q4_0_expert_reader* readers, int32_t n_readers,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * Routed readers for callers that cannot allocate device memory (code recorded under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): mmvq_id_q4_0_q8_1 with the
+ * same arguments minus the workspace. The routing plan is kept in a static device array of the
+ * library, one per GPU, of QIMG_NOALLOC_SCRATCH_BYTES (enough for QIMG_MAX_ROUTED_PAIRS pairs and
+ * QIMG_MAX_EXPERTS experts); the call allocates nothing. The array of the current device is used
+ * (the stream must belong to it); its address is looked up once per device on the first call.
+ * Every call on one GPU shares that array and rewrites it entirely, so calls that overlap in
+ * time on one GPU (two streams, parallel graph branches) race and must not be made; calls
+ * ordered on one stream are safe. Results equal those of mmvq_id_q4_0_q8_1 bit for bit.
+ * Errors: as mmvq_id_q4_0_q8_1; QIMG_EUNSUPPORTED when the plan would not fit the array;
+ * QIMG_EHIP when the array's address cannot be obtained.
+ */
+#define QIMG_NOALLOC_SCRATCH_BYTES 25600
+int mmvq_id_q4_0_q8_1_noalloc(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
+                              const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
+                              const int32_t* live_rows, int32_t K, void* stream);
+
+/*
  * The rest of a routed MoE FFN after the gate and up projections ([P1] Coverage: GLU
  * producers emit images, routed MUL_MAT_ID readers on MMVQ, per-slot routed projections;
  * [P3] What this changes: padding rows get no expert work and no combine, their outputs stay

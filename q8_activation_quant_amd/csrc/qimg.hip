@@ -33,6 +33,7 @@
 #include <stdint.h>
 #include <type_traits>
 #include <string.h>
+#include <mutex>
 
 #include "qimg.h"
 
@@ -2077,6 +2078,34 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   return launch_status();
 }
 
+// Plan memory of the allocation-free routed reader: one array per GPU (each device holds its
+// own copy until the process ends) with room for the routed workspace of the largest call the
+// routed readers take (QIMG_MAX_ROUTED_PAIRS pairs, QIMG_MAX_EXPERTS experts). In host code the
+// name is a host-side stand-in, not a device address: the kernels get the address that
+// hipGetSymbolAddress returns for the current device, kept per device below.
+constexpr int kScratchWords = 6400;
+static_assert(4 + 2 * QIMG_MAX_EXPERTS + 1 + QIMG_MAX_ROUTED_PAIRS <= kScratchWords, "scratch plan size");
+static __device__ __align__(256) int32_t scratch[kScratchWords];
+static_assert(sizeof(scratch) == QIMG_NOALLOC_SCRATCH_BYTES, "documented scratch size");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`, looked up once per device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QIMG_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return QIMG_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QIMG_OK;
+}
+
 }  // namespace
 
 // =============================================================================================
@@ -2454,6 +2483,23 @@ int mmvq_id_q4_0_q8_1_per_slot(const qimg_q4_0_expert_reader* readers, int32_t n
                                void* workspace, size_t workspace_bytes, void* stream) {
   return routed_common(readers, n_readers, E, img, ids, bucket, top_k, live_rows, K, workspace,
                        workspace_bytes, 1, stream);
+}
+
+int mmvq_id_q4_0_q8_1_noalloc(const qimg_q4_0_expert_reader* readers, int32_t n_readers, int32_t E,
+                              const void* img, const int32_t* ids, int32_t bucket, int32_t top_k,
+                              const int32_t* live_rows, int32_t K, void* stream) {
+  if (!readers || n_readers < 1 || n_readers > QIMG_MAX_READERS || E <= 0 || bucket < 0 ||
+      top_k <= 0 || !ids)
+    return QIMG_EINVAL;
+  if (bucket == 0) return QIMG_OK;
+  if ((int64_t)bucket * top_k > QIMG_MAX_ROUTED_PAIRS || E > QIMG_MAX_EXPERTS ||
+      mmvq_id_workspace_bytes(bucket, top_k, E) > sizeof(scratch))
+    return QIMG_EUNSUPPORTED;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st) return st;
+  return routed_common(readers, n_readers, E, img, ids, bucket, top_k, live_rows, K, ws,
+                       sizeof(scratch), 0, stream);
 }
 
 // logits[t][e] = x[t] . w[e] for live rows t in the router's fixed order (the router and the

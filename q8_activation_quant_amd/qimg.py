@@ -29,7 +29,7 @@ EXPORTS = (
     "qimg_emit_glu_per_slot", "mmvq_id_q4_0_q8_1_per_slot", "qimg_moe_combine",
     "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex", "qimg_moe_router", "qimg_moe_topk",
     "qimg_q8_0_tiled_bytes", "qimg_q4_1_tiled_bytes", "qimg_q8_0_tile", "qimg_q4_1_tile",
-    "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1", "mmq_q4_0_q8_1", "qimg_f32_reader",
+    "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1", "mmq_q4_0_q8_1", "qimg_f32_reader", "mmvq_id_q4_0_q8_1_noalloc",
 )
 MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7, "reglu": 8,
             "geglu": 9, "geglu_quick": 10, "swiglu_oai_gate": 11}
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "mmvq_q4_1_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "mmq_q4_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "qimg_f32_reader": (ctypes.c_int, [P, i64, P, i32, i32, P, i32, P, i64, P]),
+            "mmvq_id_q4_0_q8_1_noalloc": (ctypes.c_int, [ctypes.POINTER(ExpertReader), i32, i32, P, P, i32, i32,
+                                                         P, i32, P]),
             "qimg_moe_topk": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -247,6 +249,15 @@ def _pair_ld(t):
     assert t.dim() == 3 and t.stride(2) == 1 and t.stride(0) == t.shape[1] * t.stride(1), \
         "pair tensors are [bucket, top_k, width] with evenly spaced pair rows"
     return t.stride(1)
+
+
+def mmvq_id_noalloc(readers, E, img, ids, live_rows, K, stream=None):
+    """Routed readers without a workspace (the library's per-GPU plan array; nothing is
+    allocated): as mmvq_id."""
+    bucket, top_k = ids.shape
+    arr = _readers(readers, ExpertReader)
+    _check(lib().mmvq_id_q4_0_q8_1_noalloc(arr, len(readers), E, _ptr(img), _ptr(ids), bucket, top_k,
+                                           _ptr(live_rows), K, _stream(stream)), "mmvq_id_q4_0_q8_1_noalloc")
 
 
 def mmvq_id_per_slot(readers, E, img, ids, live_rows, K, workspace, stream=None):

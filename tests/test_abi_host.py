@@ -400,3 +400,16 @@ def test_f32_reader_validation(L):
     assert rd(y=A + 4) == qimg.EALIGN
     assert rd(out=A + 64) == qimg.EALIAS
     assert rd(out=B) == qimg.EALIAS
+
+
+def test_noalloc_routed_validation(L):
+    r = expert_readers((A, 64, C, 64))
+    na = lambda bucket=16, k=2, E=8, ids=B, rd=r, n=1: L.mmvq_id_q4_0_q8_1_noalloc(
+        rd, n, E, D, ids, bucket, k, None, 256, S)
+    assert na(ids=None) == qimg.EINVAL
+    assert na(E=0) == qimg.EINVAL
+    assert na(n=0) == qimg.EINVAL
+    assert na(bucket=0) == qimg.OK
+    # beyond the per-GPU plan array (and the routed pair limit): rejected before anything else
+    assert na(bucket=4097, k=1) == qimg.EUNSUPPORTED
+    assert na(E=2048) == qimg.EUNSUPPORTED
