@@ -715,11 +715,7 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kNt = 2;
 
 constexpr int kWaves = 8;  // routed readers
-#ifdef QIMG_OWAVES
-constexpr int kOrdWaves = QIMG_OWAVES;  // ordinary readers
-#else
-constexpr int kOrdWaves = 8;
-#endif
+constexpr int kOrdWaves = 8;  // ordinary readers
 
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -795,12 +791,7 @@ __device__ __forceinline__ int stage_code_insts(const ReadArgs& p) { return (4 *
 // is exactly one chunk (4 blocks x 8 columns x 32 bytes), and wave w streams chunks w, w + 8,
 // ...; when the scale words are copied the same way (below), every wave stages exactly what
 // it reads and needs no barrier before streaming.
-#ifdef QIMG_INTERLEAVE
-constexpr bool kInterleaveChunks = QIMG_INTERLEAVE;
-#else
-constexpr bool kInterleaveChunks = true;
-#endif
-__device__ __forceinline__ bool stage_own(const ReadArgs& p) { return kInterleaveChunks && p.tp == 8; }
+__device__ __forceinline__ bool stage_own(const ReadArgs& p) { return p.tp == 8; }
 __device__ __forceinline__ int stage_word_insts(const ReadArgs& p) { return (4 * p.KC * p.tp + 63) / 64; }
 
 __device__ __forceinline__ void stage_dma_issue(const ReadArgs& p, unsigned char* smem, int c0, int nc,
@@ -862,22 +853,9 @@ __device__ __forceinline__ int xcd_rank(int i, int G) {
   return x * q + (x < r ? x : r) + i / kXcds;
 }
 
-// Weight loads in flight per wave (ring slots of one chunk of NTM tiles each).
-#ifndef QIMG_RING1
-#define QIMG_RING1 4
-#endif
-#ifndef QIMG_RING2
-#define QIMG_RING2 2
-#endif
-#ifndef QIMG_RING3
-#define QIMG_RING3 2
-#endif
-#ifndef QIMG_RING4
-#define QIMG_RING4 2
-#endif
-constexpr int ring_depth(int ntm) {
-  return ntm == 1 ? QIMG_RING1 : ntm == 2 ? QIMG_RING2 : ntm == 3 ? QIMG_RING3 : QIMG_RING4;
-}
+// Weight loads in flight per wave: a ring of D slots of one chunk of NTM tiles each (D - 1 in
+// flight while one is computed); deeper rings measured slower for NTM >= 2.
+constexpr int ring_depth(int ntm) { return ntm == 1 ? 4 : 2; }
 
 // MODE: 0 Q4_0 readers, 2 Q4_0 block-dot export, 3 Q8_0 readers, 4 Q4_1 readers. NTG: token
 // groups of 4 image columns per pass (1 when a pass has at most 4 columns).
@@ -894,12 +872,10 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
   extern __shared__ __align__(16) unsigned char smem[];
   // weight loads in flight per wave: a ring of D slots, each one chunk of NTM tiles
   constexpr int D = ring_depth(NTM);
-  constexpr bool kInterleave = kInterleaveChunks;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int n = lane & 15, g = lane >> 4;
   const int KC = p.KC, TP = p.tp;
-  const int cs0 = KC * w / kOrdWaves, cs1 = KC * (w + 1) / kOrdWaves;
   const int live = DOTS ? p.rows : clamp_live(p.live_rows, p.rows, nullptr);
   const int wgi = xcd_rank(blockIdx.x, gridDim.x);
   // this workgroup's half tiles [h0, h1) = [floor(H i / G), floor(H (i + 1) / G)) in 32-bit
@@ -1009,10 +985,10 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
       // loop latch made the compiler wait there for every load in flight)
       using ScaleT = typename std::conditional<FMT == 2, uint32_t, uint16_t>::type;
       ScaleT dsc[D][NTM];
-      // chunks of this wave: with kInterleave, w, w + 8, w + 16, ... (the workgroup's waves
-      // read 8 consecutive chunks of a tile at each step); otherwise the range [cs0, cs1)
-      const int nst = kInterleave ? (KC - w + kOrdWaves - 1) / kOrdWaves : cs1 - cs0;
-      auto chunk_of = [&](int st) { return kInterleave ? w + kOrdWaves * st : cs0 + st; };
+      // chunks of this wave: w, w + 8, w + 16, ... (the workgroup's waves read 8 consecutive
+      // chunks of a tile at each step)
+      const int nst = (KC - w + kOrdWaves - 1) / kOrdWaves;
+      auto chunk_of = [&](int st) { return w + kOrdWaves * st; };
       // Every slot is loaded unconditionally (a conditional load would keep the slot's stale
       // value alive and defeat the exact wait counts); a slot past the wave's last chunk
       // repeats that chunk (its lines are in flight or cached), never used. The chunk part of
@@ -1915,18 +1891,9 @@ inline int launch_status() {
 // lane (at most 8).
 // The element-wise producers and the quantizer need no row-wide value: their rows are cut into
 // slices of at most kEltWaves waves x 64 lanes x 1 leaf (256 elements a wave), one workgroup each.
-#ifndef QIMG_RMS_SPLIT
-#define QIMG_RMS_SPLIT 256
-#endif
-constexpr int kRmsSplitWgs = QIMG_RMS_SPLIT;
-#ifndef QIMG_RMS_WAVES
-#define QIMG_RMS_WAVES 8
-#endif
-constexpr int kRmsWaves = QIMG_RMS_WAVES;  // RMS producer waves per workgroup, up to K = 16384
-#ifndef QIMG_ELT_WAVES
-#define QIMG_ELT_WAVES 4
-#endif
-constexpr int kEltWaves = QIMG_ELT_WAVES;  // waves per workgroup of the element-wise producers  // RMS rows are split while rows x shares stay within this
+constexpr int kRmsSplitWgs = 256;  // RMS rows are split while rows x shares stay within this
+constexpr int kRmsWaves = 8;       // RMS producer waves per workgroup, up to K = 16384
+constexpr int kEltWaves = 4;       // waves per workgroup of the element-wise producers
 
 int launch_emit(int op, EmitArgs& a, hipStream_t s) {
   const int J = (a.K + 255) / 256;
@@ -1999,7 +1966,7 @@ inline bool plan_lds(ReadArgs& a, int ntm, int* total) {
     const int codes = (nb * tp * 2 + 63) / 64 * 1024;
     int raw = (nb * tp + 63) / 64 * 256;
     a.raw_wave = 0;
-    if (tp == 8 && kInterleaveChunks) {  // per-wave runs of 32 words per step (see stage_own)
+    if (tp == 8) {  // per-wave runs of 32 words per step (see stage_own)
       const int steps = (a.KC + kOrdWaves - 1) / kOrdWaves;
       a.raw_wave = (steps + 1) / 2 * 256;
       raw = kOrdWaves * a.raw_wave;
