@@ -1343,12 +1343,17 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
 constexpr int kRoutedMaxSlots = 4;
 constexpr int kRoutedKu = 4;  // chunks per load of a routed wave; two loads in flight
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes in lane order, by DPP moves: shifts by 1, 2, 4 and 8
+// lanes within each row of 16, then the last lane of row 0 into row 1 and of row 2 into row 3
+// (row_bcast:15), then the last lane of row 1 into rows 2 and 3 (row_bcast:31). A lane whose
+// source lies outside the move's rows adds 0.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
   return v;
 }
 
@@ -1378,7 +1383,7 @@ __device__ __forceinline__ void ballot_members(const int32_t* sid, int P, int e,
 template <int KU>
 __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int sh_wave[2][kWaves];
+  __shared__ int sh_wave[1][kWaves];
   __shared__ int sh_misc[4];                  // bad ids, units U, unused, unused
   __shared__ int sh_seg[kRoutedMaxSlots][4];  // start unit, expert, columns, pass
   __shared__ int sh_mem[kRoutedMaxSlots][8];  // pair ids of a segment's columns
@@ -1438,17 +1443,15 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         lu += (c + TP - 1) >> p.tp_log2;
       }
     }
-    const int ic = wave_incl_scan(lc, lane), iu = wave_incl_scan(lu, lane);
-    if (lane == 63) {
-      sh_wave[0][w] = ic;
-      sh_wave[1][w] = iu;
-    }
+    // both prefix sums in one word: pairs in the low 16 bits, segments in the high 16 (each
+    // total is at most the pair count, <= 4096, so no carry crosses)
+    const int lv = lc | (lu << 16);
+    const int iv = wave_incl_scan(lv);
+    if (lane == 63) sh_wave[0][w] = iv;
     __syncthreads();
-    int xc = ic - lc, xu = iu - lu;
-    for (int i = 0; i < w; ++i) {
-      xc += sh_wave[0][i];
-      xu += sh_wave[1][i];
-    }
+    int xv = iv - lv;
+    for (int i = 0; i < w; ++i) xv += sh_wave[0][i];
+    int xc = xv & 0xffff, xu = (int)((uint32_t)xv >> 16);
     for (int j = 0; j < per; ++j) {
       const int e = e0 + j;
       if (e < E) {
@@ -1533,7 +1536,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     // load cursor: the unit's code and scale bases (a wave without units keeps the first chunk
     // of reader 0, a valid address it loads and never uses)
     const uint8_t* lq = p.r[0].qs + lane * 16;
-    const uint16_t* ldp = p.r[0].d + lane;
+    const uint32_t* ldp = reinterpret_cast<const uint32_t*>(p.r[0].d) + (lane >> 1);
     int crow = 0, cri = 0;         // compute cursor: output row of this lane, reader
     auto bind_load = [&](const Cursor& c) {
       const int e = uni(sh_seg[c.k][1]);
@@ -1542,7 +1545,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       while (ri + 1 < p.n_readers && tt >= p.tile_start[ri + 1]) ++ri;
       const int64_t chunk0 = ((int64_t)e * p.r[ri].tiles + (tt - p.tile_start[ri])) * KC;
       lq = p.r[ri].qs + (chunk0 * 64 + lane) * 16;
-      ldp = p.r[ri].d + chunk0 * 64 + lane;
+      ldp = reinterpret_cast<const uint32_t*>(p.r[ri].d + chunk0 * 64) + (lane >> 1);
     };
     auto bind_compute = [&](const Cursor& c) {
       const int tt = c.u - uni(sh_seg[c.k][0]);
@@ -1570,39 +1573,43 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         }
       }
     };
-    // one load: KU chunks of codes and their 16-bit scales, kept at the loaded width (a widening
-    // where loop paths merge would make the compiler wait for every load in flight)
+    // one load: KU chunks of codes and their scales, the scales as the 32-bit word that holds
+    // the lane's fp16 d_w and its neighbour's (lane pairs read the same word), so that every
+    // loop-carried value is a whole register: 16-bit values would be packed in pairs where the
+    // loop paths merge, and that packing waits for nearly every load in flight
     uint4 qa[KU], qb[KU];
-    uint16_t da_[KU], db_[KU];
-    auto load = [&](uint4 (&q)[KU], uint16_t (&d)[KU]) {
+    uint32_t da_[KU], db_[KU];
+    auto load = [&](uint4 (&q)[KU], uint32_t (&d)[KU]) {
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int cs = lc.kb + u < KC ? lc.kb + u : KC - 1;
         const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(lq + (int64_t)cs * 1024));
         q[u] = make_uint4(x.x, x.y, x.z, x.w);
-        d[u] = __builtin_nontemporal_load(ldp + (int64_t)cs * 64);
+        d[u] = __builtin_nontemporal_load(ldp + (int64_t)cs * 32);
       }
     };
-    // Stage the batch: codes items (slot, block, column, half) and scale items (slot, block,
-    // column slot of 8); unconditional in-bounds loads, padding items stored as zeros. The
-    // loads of the first part go out before the wave's first weight loads (so that waiting for
-    // them does not wait for the weights), their stores after those.
+    // Stage the batch. Codes: direct global-to-LDS copies of 1 KB per wave instruction into
+    // [4 KC][TP][32] per segment slot (lane l: half l & 1 of column (l >> 1) & (TP - 1) of
+    // block i >> (1 + log2 TP), i = 64 q + l for copy instruction q), no registers; a column
+    // past the segment's members copies column 0 and a block past K/32 the row's last block
+    // (finite values the reader never uses, or multiplies by d_w = 0). Scales: item (slot,
+    // block, column slot of 8) loaded into registers and stored as f32 d_a and -8 s_a.
+    // Order: scale loads, copies, then the wave's first two weight loads, then one explicit
+    // wait that leaves exactly those weight loads in flight (the counter retires in order).
     {
-      const int nitc = ns * ncode, nitd = ns * nds;
-      const int iters = (nitc + 4095) / 4096 > (nitd + 2047) / 2048 ? (nitc + 4095) / 4096
-                                                                     : (nitd + 2047) / 2048;
-      uint4 v[8];
+      const int nitd = ns * nds;
+      const int iters = (nitd + 2047) / 2048;
       uint32_t dw[4];
-      bool okc[8], okd[4];
-      // An item's column (and half) depends on the thread alone (the segment sizes and 512 are
-      // multiples of 2 TP and of 8), so each thread reads the image rows of its column once:
-      // 16 bits per segment (rows < 4096; 0xffff: no such column), two segments per word.
-      const int cc = (tid >> 1) & (TP - 1), cd = tid & 7;
-      uint32_t rc01 = 0xffffffffu, rc23 = 0xffffffffu, rd01 = 0xffffffffu, rd23 = 0xffffffffu;
+      bool okd[4];
+      // image rows of this thread's code column and scale column in each slot, 16 bits each
+      // (rows < 4096), two slots per word; a code column past the members takes column 0's
+      // row, a scale column past them 0xffff (stored as zeros)
+      const int cc = (lane >> 1) & (TP - 1), cd = tid & 7;
+      uint32_t rc01 = 0, rc23 = 0, rd01 = 0xffffffffu, rd23 = 0xffffffffu;
 #pragma unroll
       for (int k = 0; k < kRoutedMaxSlots; ++k) {
         const int nck = k < ns ? sh_seg[k][2] : 0;
-        const uint32_t vc = cc < nck ? (uint32_t)sh_row[k][cc] : 0xffffu;
+        const uint32_t vc = k < ns ? (uint32_t)sh_row[k][cc < nck ? cc : 0] : 0u;
         const uint32_t vd = cd < nck ? (uint32_t)sh_row[k][cd] : 0xffffu;
         const int sh = 16 * (k & 1);
         const uint32_t keep = ~(0xffffu << sh);
@@ -1619,16 +1626,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       };
       auto stage_load = [&](int it) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = tid + 512 * j + 4096 * it;
-          const int k = (i >= ncode ? 1 : 0) + (i >= 2 * ncode ? 1 : 0) + (i >= 3 * ncode ? 1 : 0);
-          const int b = (i - k * ncode) >> (1 + p.tp_log2);
-          const uint32_t irow = row_of(rc01, rc23, k);
-          okc[j] = i < nitc && irow != 0xffffu && b < p.Kb;
-          const uint32_t src = okc[j] ? (irow * (uint32_t)p.RB + (uint32_t)b) * 32u + 16u * (tid & 1) : 0u;
-          v[j] = *reinterpret_cast<const uint4*>(p.codes + src);
-        }
-#pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = tid + 512 * j + 2048 * it;
           const int k = (i >= nds ? 1 : 0) + (i >= 2 * nds ? 1 : 0) + (i >= 3 * nds ? 1 : 0);
@@ -1639,14 +1636,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         }
       };
       auto stage_store = [&](int it) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = tid + 512 * j + 4096 * it;
-          const int k = (i >= ncode ? 1 : 0) + (i >= 2 * ncode ? 1 : 0) + (i >= 3 * ncode ? 1 : 0);
-          const int r = i - k * ncode;
-          if (i < nitc)
-            *reinterpret_cast<uint4*>(smem + k * p.slot_bytes + r * 16) = okc[j] ? v[j] : make_uint4(0, 0, 0, 0);
-        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = tid + 512 * j + 2048 * it;
@@ -1661,17 +1650,38 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         }
       };
       stage_load(0);
-      // every wave's staging loads are issued before any wave's weight loads, so the staging
-      // is not queued behind the weights; then the first two weight loads (a wave without units
-      // loads its default address, unused)
-      __syncthreads();
+      {  // code copies: this wave's instructions w, w + 8, ... of the batch, slot by slot
+        const int ipk = (ncode + 63) >> 6;  // copy instructions per slot
+        const int half = lane & 1, bl = lane >> (1 + p.tp_log2);
+        const int bstep = 64 >> (1 + p.tp_log2);  // blocks per instruction
+        int k = 0, q = w;
+        while (k < ns && q >= ipk) {
+          q -= ipk;
+          ++k;
+        }
+        while (k < ns) {
+          const int b = q * bstep + bl;
+          const uint32_t irow = row_of(rc01, rc23, k);
+          const uint32_t bs = (uint32_t)(b < p.Kb ? b : p.Kb - 1);
+          if (64 * q + lane < ncode)
+            dma_b128(p.codes + ((irow * (uint32_t)p.RB + bs) * 32u + 16u * half),
+                     lds_addr(smem + k * p.slot_bytes + 1024 * q));
+          q += kWaves;
+          while (k < ns && q >= ipk) {
+            q -= ipk;
+            ++k;
+          }
+        }
+      }
       load(qa, da_);
       advance_load();
       load(qb, db_);
       advance_load();
+      wait_vmcnt<4 * KU>();
       stage_store(0);
       for (int it = 1; it < iters; ++it) {
         stage_load(it);
+        wait_vmcnt<0>();  // these scale loads are the latest issued
         stage_store(it);
       }
     }
@@ -1696,7 +1706,8 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         }
       };
       bind_a(cc);
-      auto compute = [&](const uint4 (&q)[KU], const uint16_t (&d)[KU]) {
+      const int dsh = 16 * (lane & 1);  // this lane's half of a scale word
+      auto compute = [&](const uint4 (&q)[KU], const uint32_t (&d)[KU]) {
         const unsigned char* slot = smem + cc.k * p.slot_bytes;
         const float* daL = reinterpret_cast<const float*>(slot + code_bytes);
         const float* msL = daL + nds;
@@ -1714,7 +1725,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           bhi[1] = (int)((q[u].y >> 4) & 0x0f0f0f0fu);
           bhi[2] = (int)((q[u].z >> 4) & 0x0f0f0f0fu);
           bhi[3] = (int)((q[u].w >> 4) & 0x0f0f0f0fu);
-          const float dw = h2f(d[u]);
+          const float dw = h2f(d[u] >> dsh);
           const int blk = 4 * cs + g;
 #pragma unroll
           for (int tg = 0; tg < 2; ++tg) {
@@ -1785,6 +1796,10 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         advance_load();
       }
     }
+    // the trailing repeated loads land before the next batch reuses their registers (without
+    // this the compiler waits for every load at the start of each batch's streaming, the
+    // first included)
+    wait_vmcnt<0>();
     __syncthreads();
     ub = ue;
   }

@@ -1,8 +1,8 @@
 """Host-side check of the ordinary readers' staging wait (no GPU needed: hipcc compiles the
 library to gfx950 assembly).
 
-The ordinary readers copy the image columns into LDS with direct global-to-LDS loads issued as
-inline assembly, issue their first weight loads, and then wait with an explicit
+The ordinary and the routed readers copy the image columns into LDS with direct global-to-LDS
+loads issued as inline assembly, issue their first weight loads, and then wait with an explicit
 `s_waitcnt vmcnt(N)`: N must equal the number of vector-memory loads issued after the last
 copy, since the counter retires in order (a smaller N only waits longer; a larger N would let
 the wave read LDS before the copies land). N is derived in the source from the loads each step
@@ -49,6 +49,9 @@ VMEM_LOAD = re.compile(r"^(buffer_load_|global_load_(?!lds))")
 def test_staging_wait_counts_the_loads_issued_after_the_copies(asm):
     ks = kernels(asm, "mmvq_tiled_kernel")
     assert len(ks) >= 16, "reader instantiations not found"
+    routed = kernels(asm, "mmvq_routed_kernel")
+    assert routed, "routed reader not found"
+    ks.update(routed)
     for name, lines in ks.items():
         copies = [i for i, ln in enumerate(lines) if ln.startswith("global_load_lds")]
         assert copies, name
