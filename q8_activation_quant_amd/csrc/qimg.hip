@@ -730,6 +730,22 @@ struct ReaderDesc {
   int32_t tiles;      // ceil(N / 16): tiles per expert
 };
 
+// Division of values in [0, 2^31) by a divisor fixed for a launch, as a multiply-high, an add
+// and a shift (Granlund and Montgomery, "Division by invariant integers using multiplication",
+// 1994): for 1 <= d < 2^31 with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// floor(n / d) = (mulhi(n, m) + n) >> s; the sum stays below 2^32 since mulhi(n, m) <= n.
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv fast_div(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  return FastDiv{(uint32_t)((((uint64_t)1 << 32) * ((1ull << s) - d)) / d + 1), s};
+}
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  return (int)((__umulhi((uint32_t)n, f.m) + (uint32_t)n) >> f.s);
+}
+
 struct ReadArgs {
   ReaderDesc r[QIMG_MAX_READERS];
   int32_t tile_start[QIMG_MAX_READERS + 1];  // tile prefix over readers (within one expert)
@@ -756,8 +772,10 @@ struct ReadArgs {
   // routed readers
   int32_t lds_plan;     // byte offset of the plan arrays
   int32_t slots;        // staged (expert, pass) segments per batch
-  int32_t slot_bytes;   // LDS bytes per staged segment
+  int32_t slot_bytes;   // LDS code bytes per staged segment
+  int32_t lds_da, lds_ms;  // byte offsets of the staged f32 d_a and -8 s_a, [slots][4 KC][8]
   int32_t pairs_cap;    // bucket * top_k
+  FastDiv fd_grid, fd_tiles;  // division by the workgroup count and by tiles_total
 };
 
 // Staging of image columns [c0, c0 + nc) in LDS for the ordinary readers, all 4 KC blocks, by
@@ -1383,8 +1401,8 @@ __device__ __forceinline__ void ballot_members(const int32_t* sid, int P, int e,
 template <int KU>
 __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int sh_wave[1][kWaves];
-  __shared__ int sh_misc[4];                  // bad ids, units U, unused, unused
+  __shared__ __align__(16) int sh_wave[2][kWaves];  // per-wave totals of the plan scans
+  __shared__ int sh_misc[4];                  // bad-id flag, segments, unused, unused
   __shared__ int sh_seg[kRoutedMaxSlots][4];  // start unit, expert, columns, pass
   __shared__ int sh_mem[kRoutedMaxSlots][8];  // pair ids of a segment's columns
   __shared__ int sh_row[kRoutedMaxSlots][8];  // and their image rows
@@ -1394,7 +1412,8 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   const int E = p.E, T = p.tiles_total, TP = p.tp, KC = p.KC;
   int clamped = 0;
   const int live = clamp_live(p.live_rows, p.rows, &clamped);
-  const int P = live * p.top_k;  // <= rows * top_k = pairs_cap
+  const int P = live * p.top_k;     // <= rows * top_k = pairs_cap
+  const int Pp = (P + 255) & ~255;  // sid entries the member ballots read (runs of 256)
 
   const int sid_n = (p.pairs_cap + 255) & ~255;
   int32_t* sid = reinterpret_cast<int32_t*>(smem + p.lds_plan);  // [sid_n]: expert of a live pair or -1
@@ -1402,70 +1421,73 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   int32_t* off = cnt + E;                                          // [E + 1] pair offsets
   int32_t* pps = off + E + 1;                                      // [E + 1] first segment
 
-  // ---- plan: per-expert counts, then offsets and unit starts ----
-  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+  // ---- plan: per-expert counts, then offsets and segment starts ----
+  for (int e = tid; e < E; e += kWaves * 64) cnt[e] = 0;
   if (tid < 4) {
     sh_misc[tid] = 0;
     reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;
   }
-  // the ids of this thread's pairs (P <= pairs_cap <= 8 * 512)
+  // the ids of pairs tid + 512 j (P <= pairs_cap <= 8 * 512): buffer loads, which read 0 past
+  // the P live pairs' ids; all eight go out, so that their waits are exact
+  const __amdgpu_buffer_rsrc_t rid =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.ids, (short)0, P * 4, kBufferFlags);
   int idv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {  // unconditional loads (in bounds), so their waits are exact
-    const int pi = tid + 512 * j;
-    idv[j] = p.ids[pi < P ? pi : 0];
-  }
-  __syncthreads();
-  int nbad = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int pi = tid + 512 * j;
-    if (pi < sid_n) {
-      const int id = idv[j];
-      const bool ok = pi < P && id >= 0 && id < E;
-      sid[pi] = ok ? id : -1;
-      if (ok) atomicAdd(&cnt[id], 1);
-      else if (pi < P) ++nbad;
-    }
-  }
-  if (nbad) atomicAdd(&sh_misc[0], nbad);
+  for (int j = 0; j < 8; ++j)
+    idv[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, 4u * (uint32_t)(tid + 512 * j), 0u, 0);
   __syncthreads();
   {
-    const int per = (E + (int)blockDim.x - 1) / (int)blockDim.x;
-    const int e0 = tid * per;
-    // segments (passes of up to TP pairs) per expert, TP a power of two
-    int lc = 0, lu = 0;
-    for (int j = 0; j < per; ++j) {
-      const int e = e0 + j;
-      if (e < E) {
-        const int c = cnt[e];
-        lc += c;
-        lu += (c + TP - 1) >> p.tp_log2;
+    const int nj = (Pp + 511) >> 9;
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < nj) {
+        const int pi = tid + 512 * j, id = idv[j];
+        const bool ok = pi < P && (uint32_t)id < (uint32_t)E;
+        bad |= pi < P && !ok;
+        if (pi < Pp) sid[pi] = ok ? id : -1;
+        if (ok) atomicAdd(&cnt[id], 1);
       }
     }
-    // both prefix sums in one word: pairs in the low 16 bits, segments in the high 16 (each
-    // total is at most the pair count, <= 4096, so no carry crosses)
-    const int lv = lc | (lu << 16);
-    const int iv = wave_incl_scan(lv);
-    if (lane == 63) sh_wave[0][w] = iv;
+    if (bad) sh_misc[0] = 1;
+  }
+  __syncthreads();
+  {  // thread t: experts t and t + 512 (E <= 1024)
+    const int ea = tid, eb = tid + kWaves * 64;
+    const int ca = ea < E ? cnt[ea] : 0, cb = eb < E ? cnt[eb] : 0;
+    // pairs in the low 16 bits, segments (passes of up to TP pairs) in the high 16: each total
+    // is at most the pair count (<= 4096), so no carry crosses
+    const int va = ca | (((ca + TP - 1) >> p.tp_log2) << 16);
+    const int vb = cb | (((cb + TP - 1) >> p.tp_log2) << 16);
+    const int ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
+    if (lane == 63) {
+      sh_wave[0][w] = ia;
+      sh_wave[1][w] = ib;
+    }
     __syncthreads();
-    int xv = iv - lv;
-    for (int i = 0; i < w; ++i) xv += sh_wave[0][i];
-    int xc = xv & 0xffff, xu = (int)((uint32_t)xv >> 16);
-    for (int j = 0; j < per; ++j) {
-      const int e = e0 + j;
-      if (e < E) {
-        const int c = cnt[e];
-        off[e] = xc;
-        pps[e] = xu;
-        xc += c;
-        xu += (c + TP - 1) >> p.tp_log2;
-      }
+    int xa = 0, xb = 0, ta = 0, tb = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const int a = sh_wave[0][i], b = sh_wave[1][i];
+      xa += i < w ? a : 0;
+      xb += i < w ? b : 0;
+      ta += a;
+      tb += b;
     }
-    if (tid == (int)blockDim.x - 1) {  // its running sums end at the totals
-      off[E] = xc;
-      pps[E] = xu;
-      sh_misc[1] = xu;
+    const int pa = xa + ia - va, pb = ta + xb + ib - vb;  // before experts ea and eb
+    if (ea < E) {
+      off[ea] = pa & 0xffff;
+      pps[ea] = (int)((uint32_t)pa >> 16);
+    }
+    if (eb < E) {
+      off[eb] = pb & 0xffff;
+      pps[eb] = (int)((uint32_t)pb >> 16);
+    }
+    if (tid == 0) {
+      const uint32_t tot = (uint32_t)(ta + tb);
+      off[E] = (int)(tot & 0xffffu);
+      pps[E] = (int)(tot >> 16);
+      sh_misc[1] = (int)(tot >> 16);
     }
   }
   __syncthreads();
@@ -1479,34 +1501,34 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   const int G = gridDim.x;
   const int wr = xcd_rank(blockIdx.x, G);
   // [u0, u1) = [floor(U wr / G), floor(U (wr + 1) / G)) in 32-bit arithmetic (U = q G + r,
-  // r wr < G^2)
-  const int uq = U / G, urm = U - uq * G;
-  const int u0 = uq * wr + urm * wr / G, u1 = uq * (wr + 1) + urm * (wr + 1) / G;
-  const int nb = 4 * KC;                 // staged blocks per segment (K padded to chunks)
-  const int code_bytes = nb * TP * 32;   // staged codes [nb][TP][32]
-  const int ncode = nb * TP * 2, nds = nb * 8;
+  // r (wr + 1) <= G^2)
+  const int uq = fdiv(U, p.fd_grid), urm = U - uq * G;
+  const int u0 = uq * wr + fdiv(urm * wr, p.fd_grid), u1 = uq * (wr + 1) + fdiv(urm * (wr + 1), p.fd_grid);
+  const int nb = 4 * KC;               // staged blocks per segment (K padded to chunks)
+  const int ncode = nb * TP * 2;       // 16-byte code items per slot: [nb][TP][2]
+  const int nds = nb * 8;              // scale items per slot: [nb][column slot of 8]
+  float* const daA = reinterpret_cast<float*>(smem + p.lds_da);  // [slots][nds]
+  float* const msA = reinterpret_cast<float*>(smem + p.lds_ms);  // [slots][nds]
   for (int ub = u0; ub < u1;) {
     // this batch: segments [s_lo, s_lo + ns), units [ub, ue)
-    const int s_lo = ub / T, s_last = (u1 - 1) / T;
+    const int s_lo = fdiv(ub, p.fd_tiles), s_last = fdiv(u1 - 1, p.fd_tiles);
     const int ns = s_last - s_lo + 1 < p.slots ? s_last - s_lo + 1 : p.slots;
     const int ue = (s_lo + ns) * T < u1 ? (s_lo + ns) * T : u1;
-    {  // the batch's segments, found in parallel over the experts
-      const int per = (E + (int)blockDim.x - 1) / (int)blockDim.x;
-      for (int j = 0; j < per; ++j) {
-        const int e = tid * per + j;
-        if (e < E) {
-          const int a0 = pps[e], a1 = pps[e + 1];
-          const int sa = a0 > s_lo ? a0 : s_lo, sb = a1 < s_lo + ns ? a1 : s_lo + ns;
-          for (int sg = sa; sg < sb; ++sg) {
-            const int k = sg - s_lo, pass = sg - a0;
-            const int left = cnt[e] - pass * TP;
-            sh_seg[k][0] = sg * T;
-            sh_seg[k][1] = e;
-            sh_seg[k][2] = left < TP ? left : TP;
-            sh_seg[k][3] = pass;
-          }
+    {  // the batch's segments, found by the threads of their experts
+      auto find = [&](int e) {
+        const int a0 = pps[e], a1 = pps[e + 1];
+        const int sa = a0 > s_lo ? a0 : s_lo, sb = a1 < s_lo + ns ? a1 : s_lo + ns;
+        for (int sg = sa; sg < sb; ++sg) {
+          const int k = sg - s_lo, pass = sg - a0;
+          const int left = cnt[e] - pass * TP;
+          sh_seg[k][0] = sg * T;
+          sh_seg[k][1] = e;
+          sh_seg[k][2] = left < TP ? left : TP;
+          sh_seg[k][3] = pass;
         }
-      }
+      };
+      if (tid < E) find(tid);
+      if (tid + kWaves * 64 < E) find(tid + kWaves * 64);
       if (tid < kRoutedMaxSlots && tid >= ns) sh_seg[tid][0] = 0x7fffffff;
     }
     __syncthreads();
@@ -1522,9 +1544,10 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     }
     __syncthreads();
 
-    // ---- this wave's units [wa, wb) of the batch: the first loads go out before the staging ----
+    // ---- this wave's units [wa, wb) of the batch: the first loads go out with the staging ----
     const int m = ue - ub;
-    const int wa = ub + (int)((int64_t)m * w / kWaves), wb = ub + (int)((int64_t)m * (w + 1) / kWaves);
+    const int wa = ub + (int)(((int64_t)m * w) >> 3), wb = ub + (int)(((int64_t)m * (w + 1)) >> 3);
+    static_assert(kWaves == 8, "unit split by shifts");
     struct Cursor {
       int u, k, kb;
     };
@@ -1533,26 +1556,33 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       c.k = seg_of(u);
       c.kb = 0;
     };
-    // load cursor: the unit's code and scale bases (a wave without units keeps the first chunk
-    // of reader 0, a valid address it loads and never uses)
-    const uint8_t* lq = p.r[0].qs + lane * 16;
-    const uint32_t* ldp = reinterpret_cast<const uint32_t*>(p.r[0].d) + (lane >> 1);
-    int crow = 0, cri = 0;         // compute cursor: output row of this lane, reader
+    auto reader_of = [&](int tt) {  // reader of tile tt of an expert
+      int ri = 0;
+      while (ri + 1 < p.n_readers && tt >= p.tile_start[ri + 1]) ++ri;
+      return ri;
+    };
+    // load cursor: buffer resources over the unit's reader planes and the lane's offsets in its
+    // first chunk. A wave past its last unit (or without units) loads through empty resources:
+    // the loads read zeros and touch no memory; their values are never used.
+    __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[0].qs, (short)0, 0, kBufferFlags);
+    __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[0].d, (short)0, 0, kBufferFlags);
+    uint32_t vq = 0, vd = 0;
+    int crow = 0, cri = 0;  // compute cursor: output row of this lane, reader
     auto bind_load = [&](const Cursor& c) {
       const int e = uni(sh_seg[c.k][1]);
       const int tt = c.u - uni(sh_seg[c.k][0]);  // tile in the segment
-      int ri = 0;
-      while (ri + 1 < p.n_readers && tt >= p.tile_start[ri + 1]) ++ri;
-      const int64_t chunk0 = ((int64_t)e * p.r[ri].tiles + (tt - p.tile_start[ri])) * KC;
-      lq = p.r[ri].qs + (chunk0 * 64 + lane) * 16;
-      ldp = reinterpret_cast<const uint32_t*>(p.r[ri].d + chunk0 * 64) + (lane >> 1);
+      const int ri = reader_of(tt);
+      const uint32_t chunks = (uint32_t)E * (uint32_t)p.r[ri].tiles * (uint32_t)KC;
+      const uint32_t chunk0 = ((uint32_t)e * (uint32_t)p.r[ri].tiles + (uint32_t)(tt - p.tile_start[ri])) * (uint32_t)KC;
+      rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].qs, (short)0, (int)(chunks * 1024u), kBufferFlags);
+      rd = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[ri].d, (short)0, (int)(chunks * 128u), kBufferFlags);
+      vq = chunk0 * 1024u + 16u * (uint32_t)lane;
+      vd = chunk0 * 128u + 4u * (uint32_t)(lane >> 1);
     };
     auto bind_compute = [&](const Cursor& c) {
       const int tt = c.u - uni(sh_seg[c.k][0]);
-      int ri = 0;
-      while (ri + 1 < p.n_readers && tt >= p.tile_start[ri + 1]) ++ri;
-      cri = ri;
-      crow = (tt - p.tile_start[ri]) * 16 + n;
+      cri = reader_of(tt);
+      crow = (tt - p.tile_start[cri]) * 16 + n;
     };
     Cursor lc{0, 0, 0}, cc{0, 0, 0};
     bool ldone = wa >= wb;
@@ -1568,89 +1598,62 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           start(lc.u + 1, lc);
           bind_load(lc);
         } else {
-          ldone = true;  // further loads repeat the last batch (in bounds, unused)
-          lc.kb -= KU;
+          ldone = true;
+          rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[0].qs, (short)0, 0, kBufferFlags);
+          rd = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[0].d, (short)0, 0, kBufferFlags);
         }
       }
     };
     // one load: KU chunks of codes and their scales, the scales as the 32-bit word that holds
     // the lane's fp16 d_w and its neighbour's (lane pairs read the same word), so that every
     // loop-carried value is a whole register: 16-bit values would be packed in pairs where the
-    // loop paths merge, and that packing waits for nearly every load in flight
+    // loop paths merge, and that packing waits for nearly every load in flight. Chunks past the
+    // unit's last repeat it (in flight or cached; not used).
     uint4 qa[KU], qb[KU];
     uint32_t da_[KU], db_[KU];
     auto load = [&](uint4 (&q)[KU], uint32_t (&d)[KU]) {
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        const int cs = lc.kb + u < KC ? lc.kb + u : KC - 1;
-        const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(lq + (int64_t)cs * 1024));
+        const uint32_t cs = (uint32_t)(lc.kb + u < KC ? lc.kb + u : KC - 1);
+        const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rq, vq + cs * 1024u, 0u, kNt);
         q[u] = make_uint4(x.x, x.y, x.z, x.w);
-        d[u] = __builtin_nontemporal_load(ldp + (int64_t)cs * 32);
+        d[u] = __builtin_amdgcn_raw_buffer_load_b32(rd, vd + cs * 128u, 0u, kNt);
       }
     };
-    // Stage the batch. Codes: direct global-to-LDS copies of 1 KB per wave instruction into
-    // [4 KC][TP][32] per segment slot (lane l: half l & 1 of column (l >> 1) & (TP - 1) of
-    // block i >> (1 + log2 TP), i = 64 q + l for copy instruction q), no registers; a column
-    // past the segment's members copies column 0 and a block past K/32 the row's last block
-    // (finite values the reader never uses, or multiplies by d_w = 0). Scales: item (slot,
-    // block, column slot of 8) loaded into registers and stored as f32 d_a and -8 s_a.
-    // Order: scale loads, copies, then the wave's first two weight loads, then one explicit
-    // wait that leaves exactly those weight loads in flight (the counter retires in order).
+    // Stage the batch by direct global-to-LDS copies (no registers). Codes: 1 KB per wave
+    // instruction into [4 KC][TP][32] per slot (lane l: half l & 1 of column (l >> 1) & (TP - 1)
+    // of block i >> (1 + log2 TP), i = 64 q + l for instruction q). Scales: the raw words
+    // d_a | s_a << 16, 256 bytes per instruction into the -8 s_a array [slot][4 KC][8] (lane l:
+    // column l & 7), converted in place by the lane that copied them once its copies have
+    // landed. A column past the segment's members copies column 0 and a block past K/32 the
+    // row's last block: finite values the reader never uses, or multiplies by d_w = 0. Order:
+    // copies, then the wave's first two weight loads, then one explicit wait that leaves
+    // exactly those weight loads in flight (the counter retires in order).
     {
-      const int nitd = ns * nds;
-      const int iters = (nitd + 2047) / 2048;
-      uint32_t dw[4];
-      bool okd[4];
-      // image rows of this thread's code column and scale column in each slot, 16 bits each
-      // (rows < 4096), two slots per word; a code column past the members takes column 0's
-      // row, a scale column past them 0xffff (stored as zeros)
-      const int cc = (lane >> 1) & (TP - 1), cd = tid & 7;
-      uint32_t rc01 = 0, rc23 = 0, rd01 = 0xffffffffu, rd23 = 0xffffffffu;
+      // image rows of this lane's code column and scale column in each slot, 16 bits each
+      // (rows < 4096), two slots per word; a column past the members takes column 0's row
+      const int ccol = (lane >> 1) & (TP - 1), dcol = lane & 7;
+      uint32_t rc01 = 0, rc23 = 0, rd01 = 0, rd23 = 0;
 #pragma unroll
       for (int k = 0; k < kRoutedMaxSlots; ++k) {
-        const int nck = k < ns ? sh_seg[k][2] : 0;
-        const uint32_t vc = k < ns ? (uint32_t)sh_row[k][cc < nck ? cc : 0] : 0u;
-        const uint32_t vd = cd < nck ? (uint32_t)sh_row[k][cd] : 0xffffu;
-        const int sh = 16 * (k & 1);
-        const uint32_t keep = ~(0xffffu << sh);
-        if (k < 2) {
-          rc01 = (rc01 & keep) | (vc << sh);
-          rd01 = (rd01 & keep) | (vd << sh);
-        } else {
-          rc23 = (rc23 & keep) | (vc << sh);
-          rd23 = (rd23 & keep) | (vd << sh);
+        if (k < ns) {
+          const int nck = sh_seg[k][2];
+          const uint32_t vc = (uint32_t)sh_row[k][ccol < nck ? ccol : 0];
+          const uint32_t vs = (uint32_t)sh_row[k][dcol < nck ? dcol : 0];
+          if (k < 2) {
+            rc01 |= vc << (16 * k);
+            rd01 |= vs << (16 * k);
+          } else {
+            rc23 |= vc << (16 * (k - 2));
+            rd23 |= vs << (16 * (k - 2));
+          }
         }
       }
       auto row_of = [](uint32_t w01, uint32_t w23, int k) {
         return ((k & 2 ? w23 : w01) >> (16 * (k & 1))) & 0xffffu;
       };
-      auto stage_load = [&](int it) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = tid + 512 * j + 2048 * it;
-          const int k = (i >= nds ? 1 : 0) + (i >= 2 * nds ? 1 : 0) + (i >= 3 * nds ? 1 : 0);
-          const int b = (i - k * nds) >> 3;
-          const uint32_t irow = row_of(rd01, rd23, k);
-          okd[j] = i < nitd && irow != 0xffffu && b < p.Kb;
-          dw[j] = p.ds[okd[j] ? irow * (uint32_t)p.RB + (uint32_t)b : 0u];
-        }
-      };
-      auto stage_store = [&](int it) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = tid + 512 * j + 2048 * it;
-          const int k = (i >= nds ? 1 : 0) + (i >= 2 * nds ? 1 : 0) + (i >= 3 * nds ? 1 : 0);
-          const int r = i - k * nds;
-          if (i < nitd) {
-            const uint32_t x = okd[j] ? dw[j] : 0u;
-            float* da = reinterpret_cast<float*>(smem + k * p.slot_bytes + code_bytes);
-            da[r] = h2f(x);
-            da[nds + r] = -8.0f * h2f(x >> 16);
-          }
-        }
-      };
-      stage_load(0);
-      {  // code copies: this wave's instructions w, w + 8, ... of the batch, slot by slot
+      const int Kb = p.Kb;
+      {  // codes: this wave's instructions w, w + 8, ... of the batch, slot by slot
         const int ipk = (ncode + 63) >> 6;  // copy instructions per slot
         const int half = lane & 1, bl = lane >> (1 + p.tp_log2);
         const int bstep = 64 >> (1 + p.tp_log2);  // blocks per instruction
@@ -1662,7 +1665,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         while (k < ns) {
           const int b = q * bstep + bl;
           const uint32_t irow = row_of(rc01, rc23, k);
-          const uint32_t bs = (uint32_t)(b < p.Kb ? b : p.Kb - 1);
+          const uint32_t bs = (uint32_t)(b < Kb ? b : Kb - 1);
           if (64 * q + lane < ncode)
             dma_b128(p.codes + ((irow * (uint32_t)p.RB + bs) * 32u + 16u * half),
                      lds_addr(smem + k * p.slot_bytes + 1024 * q));
@@ -1673,16 +1676,30 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           }
         }
       }
+      const int nit = ns * nds, nid = (nit + 63) >> 6;
+      for (int q = w; q < nid; q += kWaves) {  // raw scale words, flat over the batch's slots
+        const int f = 64 * q + lane;
+        const int k = (f >= nds ? 1 : 0) + (f >= 2 * nds ? 1 : 0) + (f >= 3 * nds ? 1 : 0);
+        const int b = (f - k * nds) >> 3;
+        const uint32_t irow = row_of(rd01, rd23, k);
+        const uint32_t bs = (uint32_t)(b < Kb ? b : Kb - 1);
+        if (f < nit) dma_b32(p.ds + (irow * (uint32_t)p.RB + bs), lds_addr(msA + 64 * q));
+      }
+      // the last copy has been issued (a marker in the assembly for the wait-count check; the
+      // clobber keeps the weight loads after it)
+      asm volatile("; routed staging copies issued" ::: "memory");
       load(qa, da_);
       advance_load();
       load(qb, db_);
       advance_load();
       wait_vmcnt<4 * KU>();
-      stage_store(0);
-      for (int it = 1; it < iters; ++it) {
-        stage_load(it);
-        wait_vmcnt<0>();  // these scale loads are the latest issued
-        stage_store(it);
+      for (int q = w; q < nid; q += kWaves) {
+        const int f = 64 * q + lane;
+        if (f < nit) {
+          const uint32_t x = __float_as_uint(msA[f]);
+          daA[f] = h2f(x);
+          msA[f] = -8.0f * h2f(x >> 16);
+        }
       }
     }
     __syncthreads();
@@ -1708,9 +1725,8 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       bind_a(cc);
       const int dsh = 16 * (lane & 1);  // this lane's half of a scale word
       auto compute = [&](const uint4 (&q)[KU], const uint32_t (&d)[KU]) {
-        const unsigned char* slot = smem + cc.k * p.slot_bytes;
-        const float* daL = reinterpret_cast<const float*>(slot + code_bytes);
-        const float* msL = daL + nds;
+        const float* daL = daA + cc.k * nds;
+        const float* msL = msA + cc.k * nds;
         const int TG = (uni(sh_seg[cc.k][2]) + 3) >> 2;
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
@@ -2067,15 +2083,19 @@ int run_ordinary(ReadArgs& a, hipStream_t s) {
   return launch_read<MODE>(a, G, ntm, lds, s);
 }
 
-// Routed readers: one workgroup per CU over the (expert, pass, tile) units. LDS: `slots`
-// staged segments of [4 KC][tp][32] codes + [4 KC][8] d_a + [4 KC][8] -8 s_a, the zero slot,
-// then the plan arrays sid[pairs, padded to 256] (expert of each live pair), cnt[E], off[E+1],
-// pps[E+1] (first segment of each expert).
+// Routed readers: one workgroup per CU over the (expert, pass, tile) units. LDS: the codes of
+// `slots` staged segments, [4 KC][tp][32] each, then their f32 d_a and -8 s_a, [slot][4 KC][8]
+// each, the zero slot, then the plan arrays sid[pairs, padded to 256] (expert of each live
+// pair), cnt[E], off[E+1], pps[E+1] (first segment of each expert).
 int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   const int tiles = a.tile_start[a.n_readers];
   a.tiles_total = tiles;
   a.pairs_cap = pairs_cap;
   if ((int64_t)(pairs_cap + a.E) * tiles > 0x7fffffff) return QIMG_EUNSUPPORTED;
+  // the weight loads address a reader's planes with 32-bit offsets
+  for (int i = 0; i < a.n_readers; ++i)
+    if ((int64_t)a.E * a.r[i].tiles * a.KC * 1024 > 0x7fffffff) return QIMG_EUNSUPPORTED;
+  for (int i = a.n_readers + 1; i <= QIMG_MAX_READERS; ++i) a.tile_start[i] = 0x7fffffff;
   const int plan = 4 * (((pairs_cap + 255) & ~255) + 3 * a.E + 2);
   const int nb = 4 * a.KC;
   // the widest column pass that leaves room for two staged segments, else for one
@@ -2089,8 +2109,10 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
         a.tp = tp;
         a.tp_log2 = tp == 8 ? 3 : tp == 4 ? 2 : tp == 2 ? 1 : 0;
         a.slots = slots;
-        a.slot_bytes = slot;
-        a.lds_zero = slots * slot;
+        a.slot_bytes = nb * tp * 32;
+        a.lds_da = slots * a.slot_bytes;
+        a.lds_ms = a.lds_da + slots * nb * 32;
+        a.lds_zero = a.lds_ms + slots * nb * 32;
         a.lds_plan = a.lds_zero + 16;
         lds = a.lds_plan + plan;
         break;
@@ -2099,11 +2121,14 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
     if (lds >= 0) break;
   }
   if (lds < 0) return QIMG_EUNSUPPORTED;
+  const int G = cu_count();
+  a.fd_grid = fast_div((uint32_t)G);
+  a.fd_tiles = fast_div((uint32_t)tiles);
   const void* fn = (const void*)mmvq_routed_kernel<kRoutedKu>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
-  hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedKu>), dim3(cu_count()), dim3(kWaves * 64), lds, s, a);
+  hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedKu>), dim3(G), dim3(kWaves * 64), lds, s, a);
   return launch_status();
 }
 

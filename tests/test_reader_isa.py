@@ -46,16 +46,33 @@ def kernels(asm_text, pattern):
 VMEM_LOAD = re.compile(r"^(buffer_load_|global_load_(?!lds))")
 
 
+MARKER = "; routed staging copies issued"
+
+
+def kernel_lines(asm_text, pattern):
+    """Like kernels(), keeping the routed reader's marker comment."""
+    res = {}
+    for m in re.finditer(r"^(_Z\w*%s\w*):" % pattern, asm_text, flags=re.M):
+        body = asm_text[m.end():]
+        body = body[: body.find("s_endpgm")]
+        res[m.group(1)] = [ln.strip() for ln in body.splitlines()
+                           if ln.strip() and (not ln.strip().startswith(";") or ln.strip() == MARKER)]
+    return res
+
+
 def test_staging_wait_counts_the_loads_issued_after_the_copies(asm):
     ks = kernels(asm, "mmvq_tiled_kernel")
     assert len(ks) >= 16, "reader instantiations not found"
-    routed = kernels(asm, "mmvq_routed_kernel")
+    routed = kernel_lines(asm, "mmvq_routed_kernel")
     assert routed, "routed reader not found"
     ks.update(routed)
     for name, lines in ks.items():
         copies = [i for i, ln in enumerate(lines) if ln.startswith("global_load_lds")]
         assert copies, name
-        last = copies[-1]
+        # the routed reader's copies sit in loops whose blocks the compiler may place after
+        # the code that follows them; its marker stands after the last copy in program order
+        marks = [i for i, ln in enumerate(lines) if ln == MARKER]
+        last = marks[0] if marks else copies[-1]
         loads = 0
         for ln in lines[last + 1:]:
             if VMEM_LOAD.match(ln):
