@@ -774,6 +774,8 @@ struct ReadArgs {
   int32_t slots;        // staged (expert, pass) segments per batch
   int32_t slot_bytes;   // LDS code bytes per staged segment
   int32_t lds_da, lds_ms;  // byte offsets of the staged f32 d_a and -8 s_a, [slots][4 KC][8]
+  int32_t lds_xo;          // byte offset of the half-unit carry slots, [8 waves][64] float2
+  int32_t halves, khalf;   // units cut in two K halves at chunk khalf (halves 2), or whole
   int32_t pairs_cap;    // bucket * top_k
   FastDiv fd_grid, fd_tiles;  // division by the workgroup count and by tiles_total
 };
@@ -1359,7 +1361,7 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
 // lane tree): not on the other pairs, the live count or the schedule.
 // ---------------------------------------------------------------------------------------------
 constexpr int kRoutedMaxSlots = 4;
-constexpr int kRoutedKu = 4;  // chunks per load of a routed wave; two loads in flight
+constexpr int kRoutedKu = 2;  // chunks per load of a routed wave; two loads in flight
 
 // Inclusive prefix sum over the 64 lanes in lane order, by DPP moves: shifts by 1, 2, 4 and 8
 // lanes within each row of 16, then the last lane of row 0 into row 1 and of row 2 into row 3
@@ -1544,17 +1546,27 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     }
     __syncthreads();
 
-    // ---- this wave's units [wa, wb) of the batch: the first loads go out with the staging ----
-    const int m = ue - ub;
-    const int wa = ub + (int)(((int64_t)m * w) >> 3), wb = ub + (int)(((int64_t)m * (w + 1)) >> 3);
-    static_assert(kWaves == 8, "unit split by shifts");
+    // ---- this wave's work of the batch: the first loads go out with the staging ----
+    // With p.halves == 2 every unit is cut at chunk H = p.khalf (a multiple of KU fixed by K)
+    // into two half-units, 2 u and 2 u + 1, each summed on its own (chunks in order, then the
+    // lane tree); a pair's output is the first half's sum plus the second's. The wave takes
+    // half-units [ha, hb) of the batch, so that the work of the workgroup splits over its waves
+    // in steps of half a unit. With p.halves == 1 (K too short to cut), H = KC.
+    const int halves = p.halves, H = p.khalf;
+    const int h_lo = halves * ub, hm = halves * (ue - ub);
+    auto hstart = [&](int v) { return h_lo + (int)(((int64_t)hm * v) >> 3); };
+    static_assert(kWaves == 8, "work split by shifts");
+    const int ha = hstart(w), hb = hstart(w + 1);
     struct Cursor {
-      int u, k, kb;
+      int hu, u, k, kb, ke;  // half-unit, unit, slot, next chunk, end chunk
     };
-    auto start = [&](int u, Cursor& c) {
-      c.u = u;
-      c.k = seg_of(u);
-      c.kb = 0;
+    auto start = [&](int hu, Cursor& c) {
+      c.hu = hu;
+      c.u = halves == 2 ? hu >> 1 : hu;
+      const bool second = halves == 2 && (hu & 1);
+      c.k = seg_of(c.u);
+      c.kb = second ? H : 0;
+      c.ke = second ? KC : H;
     };
     auto reader_of = [&](int tt) {  // reader of tile tt of an expert
       int ri = 0;
@@ -1584,19 +1596,20 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       cri = reader_of(tt);
       crow = (tt - p.tile_start[cri]) * 16 + n;
     };
-    Cursor lc{0, 0, 0}, cc{0, 0, 0};
-    bool ldone = wa >= wb;
+    Cursor lc{0, 0, 0, 0, 0}, cc{0, 0, 0, 0, 0};
+    bool ldone = ha >= hb;
     if (!ldone) {
-      start(wa, lc);
+      start(ha, lc);
       bind_load(lc);
     }
     auto advance_load = [&]() {
       if (ldone) return;
       lc.kb += KU;
-      if (lc.kb >= KC) {
-        if (lc.u + 1 < wb) {
-          start(lc.u + 1, lc);
-          bind_load(lc);
+      if (lc.kb >= lc.ke) {
+        if (lc.hu + 1 < hb) {
+          const int pu = lc.u;
+          start(lc.hu + 1, lc);
+          if (lc.u != pu) bind_load(lc);  // the second half of a unit keeps its planes
         } else {
           ldone = true;
           rq = __builtin_amdgcn_make_buffer_rsrc((void*)p.r[0].qs, (short)0, 0, kBufferFlags);
@@ -1608,13 +1621,13 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     // the lane's fp16 d_w and its neighbour's (lane pairs read the same word), so that every
     // loop-carried value is a whole register: 16-bit values would be packed in pairs where the
     // loop paths merge, and that packing waits for nearly every load in flight. Chunks past the
-    // unit's last repeat it (in flight or cached; not used).
+    // half-unit's last repeat it (in flight or cached; not used).
     uint4 qa[KU], qb[KU];
     uint32_t da_[KU], db_[KU];
     auto load = [&](uint4 (&q)[KU], uint32_t (&d)[KU]) {
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        const uint32_t cs = (uint32_t)(lc.kb + u < KC ? lc.kb + u : KC - 1);
+        const uint32_t cs = (uint32_t)(lc.kb + u < lc.ke ? lc.kb + u : lc.ke - 1);
         const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rq, vq + cs * 1024u, 0u, kNt);
         q[u] = make_uint4(x.x, x.y, x.z, x.w);
         d[u] = __builtin_amdgcn_raw_buffer_load_b32(rd, vd + cs * 128u, 0u, kNt);
@@ -1704,13 +1717,22 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     }
     __syncthreads();
 
-    // ---- stream this wave's units ----
-    if (wa < wb) {
-      start(wa, cc);
+    // ---- stream this wave's half-units ----
+    // A unit whose halves fall to two waves: the first half's owner leaves its sums in its
+    // carry slot (LDS, float2 per lane); the second half's owner keeps its own sums and the
+    // unit's store targets, and adds the two after the batch's last barrier.
+    float2* const xo = reinterpret_cast<float2*>(smem + p.lds_xo);  // [kWaves][64]
+    bool pend = false;
+    float pend0 = 0.0f, pend1 = 0.0f;
+    float* pend_out0 = nullptr;
+    float* pend_out1 = nullptr;
+    if (ha < hb) {
+      start(ha, cc);
       bind_compute(cc);
       float acc[8];
 #pragma unroll
       for (int v = 0; v < 8; ++v) acc[v] = 0.0f;
+      float carry0 = 0.0f, carry1 = 0.0f;  // first-half sums of the current unit
       int a_off[2];
       bool a_on[2];
       auto bind_a = [&](const Cursor& c) {
@@ -1731,7 +1753,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
           const int cs = cc.kb + u;
-          if (cs >= KC) break;
+          if (cs >= cc.ke) break;
           v4i blo, bhi;
           blo[0] = (int)(q[u].x & 0x0f0f0f0fu);
           blo[1] = (int)(q[u].y & 0x0f0f0f0fu);
@@ -1762,12 +1784,11 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           }
         }
       };
-      // after a compute step: at the end of a unit, sum the k-group lanes, store, and move the
-      // compute cursor to the next unit
+      // after a compute step: at the end of a half-unit, sum the k-group lanes; at the end of
+      // a unit store (or hand over), and move the compute cursor to the next half-unit
       auto finish_step = [&]() {
         cc.kb += KU;
-        if (cc.kb < KC) return;
-        const int nc = uni(sh_seg[cc.k][2]);
+        if (cc.kb < cc.ke) return;
         // the four k-group lanes of a row, reduced and scattered: a swap of the lanes 32 apart
         // carries columns c and c + 4 at once (lanes g < 2 keep column c, g >= 2 column c + 4,
         // summed over g and g + 2), then a swap of the lanes 16 apart carries two of those, so
@@ -1785,20 +1806,59 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
                                                             false, false);
           v2[c] = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
         }
-        if (crow < p.r[cri].N) {
-          if (2 * g < nc) p.r[cri].out[(int64_t)sh_mem[cc.k][2 * g] * p.r[cri].ld + crow] = v2[0];
-          if (2 * g + 1 < nc) p.r[cri].out[(int64_t)sh_mem[cc.k][2 * g + 1] * p.r[cri].ld + crow] = v2[1];
-        }
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[v] = 0.0f;
-        if (cc.u + 1 < wb) {
-          start(cc.u + 1, cc);
-          bind_compute(cc);
-          bind_a(cc);
+        const bool first = halves == 2 && (cc.hu & 1) == 0;
+        const bool next = cc.hu + 1 < hb;
+        if (first) {
+          if (next) {  // the second half follows in this wave
+            carry0 = v2[0];
+            carry1 = v2[1];
+          } else {
+            xo[w * 64 + lane] = make_float2(v2[0], v2[1]);
+          }
+        } else {
+          const bool own_first = halves == 1 || cc.hu - 1 >= ha;
+          float o0 = v2[0], o1 = v2[1];
+          if (halves == 2 && own_first) {
+            o0 = carry0 + o0;
+            o1 = carry1 + o1;
+          }
+          const int nc = uni(sh_seg[cc.k][2]);
+          const bool row_ok = crow < p.r[cri].N;
+          float* const out = p.r[cri].out + crow;
+          const int64_t ld = p.r[cri].ld;
+          float* const t0 = row_ok && 2 * g < nc ? out + (int64_t)sh_mem[cc.k][2 * g] * ld : nullptr;
+          float* const t1 = row_ok && 2 * g + 1 < nc ? out + (int64_t)sh_mem[cc.k][2 * g + 1] * ld : nullptr;
+          if (own_first) {
+            if (t0) *t0 = o0;
+            if (t1) *t1 = o1;
+          } else {  // the first half belongs to an earlier wave: add after the barrier
+            pend = true;
+            pend0 = o0;
+            pend1 = o1;
+            pend_out0 = t0;
+            pend_out1 = t1;
+          }
+        }
+        if (next) {
+          const int pu = cc.u;
+          start(cc.hu + 1, cc);
+          if (cc.u != pu) {
+            bind_compute(cc);
+            bind_a(cc);
+          }
         }
       };
-      // steps of this wave: ceil(KC / KU) per unit
-      const int S = (wb - wa) * ((KC + KU - 1) / KU);
+      // steps of this wave: H / KU per first half, ceil((KC - H) / KU) per second half (with
+      // one half per unit, ceil(KC / KU))
+      int S;
+      if (halves == 2) {
+        const int n0 = (hb + 1) / 2 - (ha + 1) / 2;  // even half-units in [ha, hb)
+        S = n0 * (H / KU) + (hb - ha - n0) * ((KC - H + KU - 1) / KU);
+      } else {
+        S = (hb - ha) * ((KC + KU - 1) / KU);
+      }
       for (int st = 0; st < S; st += 2) {
         compute(qa, da_);
         finish_step();
@@ -1808,7 +1868,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           compute(qb, db_);
           finish_step();
         }
-        load(qb, db_);  // unconditional: a load past the wave's last batch repeats it (unused)
+        load(qb, db_);  // unconditional: a load past the wave's last half-unit reads nothing
         advance_load();
       }
     }
@@ -1817,6 +1877,13 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     // first included)
     wait_vmcnt<0>();
     __syncthreads();
+    if (pend) {  // the first half's sums: from the last wave before this one with work
+      int v = w - 1;
+      while (v > 0 && hstart(v) == hstart(v + 1)) --v;
+      const float2 x = xo[v * 64 + lane];
+      if (pend_out0) *pend_out0 = x.x + pend0;
+      if (pend_out1) *pend_out1 = x.y + pend1;
+    }
     ub = ue;
   }
   // The plan, exported after the last barrier (a global store before a barrier makes that
@@ -2085,8 +2152,9 @@ int run_ordinary(ReadArgs& a, hipStream_t s) {
 
 // Routed readers: one workgroup per CU over the (expert, pass, tile) units. LDS: the codes of
 // `slots` staged segments, [4 KC][tp][32] each, then their f32 d_a and -8 s_a, [slot][4 KC][8]
-// each, the zero slot, then the plan arrays sid[pairs, padded to 256] (expert of each live
-// pair), cnt[E], off[E+1], pps[E+1] (first segment of each expert).
+// each, the zero slot, the half-unit carry slots, then the plan arrays sid[pairs, padded to
+// 256] (expert of each live pair), cnt[E], off[E+1], pps[E+1] (first segment of each expert).
+constexpr int kXoBytes = kWaves * 64 * 8;
 int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   const int tiles = a.tile_start[a.n_readers];
   a.tiles_total = tiles;
@@ -2103,7 +2171,7 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   for (int need : {2, 1}) {
     for (int tp : {8, 4, 2, 1}) {
       const int slot = nb * tp * 32 + nb * 64;
-      int slots = (kMaxLds - 16 - plan) / slot;
+      int slots = (kMaxLds - 16 - kXoBytes - plan) / slot;
       if (slots > kRoutedMaxSlots) slots = kRoutedMaxSlots;
       if (slots >= need) {
         a.tp = tp;
@@ -2113,7 +2181,8 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
         a.lds_da = slots * a.slot_bytes;
         a.lds_ms = a.lds_da + slots * nb * 32;
         a.lds_zero = a.lds_ms + slots * nb * 32;
-        a.lds_plan = a.lds_zero + 16;
+        a.lds_xo = a.lds_zero + 16;
+        a.lds_plan = a.lds_xo + kXoBytes;
         lds = a.lds_plan + plan;
         break;
       }
@@ -2121,6 +2190,11 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
     if (lds >= 0) break;
   }
   if (lds < 0) return QIMG_EUNSUPPORTED;
+  // K halves: the first a whole number of loads (KU chunks), about half of K; no cut when the
+  // second half would be empty
+  const int H = kRoutedKu * ((a.KC + 2 * kRoutedKu - 1) / (2 * kRoutedKu));
+  a.halves = H < a.KC ? 2 : 1;
+  a.khalf = H < a.KC ? H : a.KC;
   const int G = cu_count();
   a.fd_grid = fast_div((uint32_t)G);
   a.fd_tiles = fast_div((uint32_t)tiles);
