@@ -8,9 +8,13 @@ Timing: a HIP graph holds R instances of the step, each with its own copy of eve
 with R x weights >= 1 GiB so replays stream weights from HBM rather than from the 256 MB
 Infinity Cache (the instances repeat in order until the graph holds at least 32 steps). W
 warmup steps, then exactly K timed steps, bracketed by synchronisation. The reader kernel is
-also timed alone (a graph of reader launches over the same instances) for the roofline line.
+also timed alone (a graph of reader launches over the same instances) for the roofline line,
+beside a plain streaming read of the same byte count (the measured ceiling). The GLU workload's
+graph includes its extra f32 reader of the kept output, also timed alone.
 --moe times the whole routed MoE FFN of the routed workloads the same way.
-The CPU baseline is the plain oracle on the host, single-threaded, on a bounded sample.
+The CPU baseline is the plain oracle on the host on a bounded sample, on all the threads this
+process may use (at most 16; each reader's output rows split over them) and on one thread.
+--pmc-probe and --pmc-summarize take and summarise the reader's HBM counters (rocprofv3).
 
 Prints one JSON line.
 """
@@ -64,6 +68,20 @@ class Instance:
         if wl.routed:
             self.ids = dev(wl.ids)
             self.ws = torch.empty(qimg.workspace_bytes(T, wl.top_k, wl.E) // 4, dtype=torch.int32, device="cuda")
+        self.v = dev(wl.extra_v.reshape(1, K)) if wl.extra_v is not None else None
+        self.fo = torch.empty(T, 1, dtype=torch.float32, device="cuda") if self.v is not None else None
+        self.ceil_buf = None
+
+    def extra(self):
+        """The extra f32 reader of the kept producer output (the GLU workload)."""
+        from q8_activation_quant_amd import qimg
+        live = self.live if self.wl.live is not None else None
+        qimg.f32_reader(self.y, self.v, self.fo, live)
+
+    def ceiling(self):
+        """A plain streaming read of as many bytes as the reader launch moves (its own buffer)."""
+        from q8_activation_quant_amd import qimg
+        qimg.read_ceiling(self.ceil_buf, self.ceil_sink)
 
     def produce(self, with_img=True):
         from q8_activation_quant_amd import qimg
@@ -96,6 +114,8 @@ class Instance:
             self.produce(False)
             self.quantize()
         self.read()
+        if self.v is not None:
+            self.extra()
 
 
 def algorithmic_bytes(wl):
@@ -119,8 +139,10 @@ def algorithmic_bytes(wl):
         w = sum(r.d.shape[-2] * Kb * per_block[r.fmt] for r in wl.readers)
         out = sum(L * r.d.shape[-2] * 4 for r in wl.readers)
         ids = 0
+    # the GLU workload's extra f32 reader: the kept output and the vector read, one f32 per row
+    extra = (L * K * 4 + K * 4 + L * 4) if wl.extra_v is not None else 0
     return {"producer": prod, "image_write": img, "image_read": img, "weights": w, "outputs": out,
-            "ids": ids, "total": prod + 2 * img + w + out + ids,
+            "ids": ids, "extra_f32_reader": extra, "total": prod + 2 * img + w + out + ids + extra,
             "reader_kernel": img + w + out + ids}
 
 
@@ -292,31 +314,84 @@ def time_graph(fns, steps, warmup, runs=3):
     return res
 
 
-def cpu_baseline(wl, budget_s=20.0):
-    """The plain oracle (single thread) over the same component graph; returns us per graph."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Host threads for the all-cores oracle run: the CPUs this process may use, at most 16 (a
+    one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, budget_s=10.0, threads=1):
+    """The plain oracle over the same component graph on `threads` host threads: the producer,
+    the quantizer (and the routing plan) on one, each reader's output rows split into `threads`
+    contiguous slices run in parallel (the oracle's C readers run with the interpreter lock
+    released; slices are cut before timing). Returns (us per graph, median; graphs timed)."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as O
     T, K = wl.T, wl.K
     L = wl.live if wl.live is not None else T
+    jobs = []
+    for r in wl.readers:
+        N = r.d.shape[-2]
+        bounds = np.linspace(0, N, threads + 1).astype(int)
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            if b <= a:
+                continue
+            if wl.routed:
+                jobs.append(("id", np.ascontiguousarray(r.qs[:, a:b]), np.ascontiguousarray(r.d[:, a:b]), None))
+            else:
+                jobs.append((r.fmt, r.qs[a:b], r.d[a:b], None if r.m is None else r.m[a:b]))
+
+    def run_job(job, img):
+        kind, qs, d, m = job
+        if kind == "id":
+            O.mmvq_id(qs, d, wl.E, K, img, T, wl.ids, L)
+        elif kind == "q4_0":
+            O.mmvq(qs, d, K, img, T, L)
+        else:
+            O.mmvq_fmt(kind, qs, d, m, K, img, T, L)
+
+    pool = ThreadPoolExecutor(max_workers=threads) if threads > 1 else None
     times = []
     t_end = time.perf_counter() + budget_s
-    while True:
-        t0 = time.perf_counter()
-        if wl.producer == "rmsnorm":
-            y = O.rmsnorm(wl.x[:L], wl.gamma, 1e-6)
-        else:
-            y = O.glu_ex(wl.gu[:L, :K], wl.gu[:L, K:], wl.producer)
-        img = O.quantize(y, img_rows=T)
-        for r in wl.readers:
+    try:
+        while True:
+            t0 = time.perf_counter()
+            if wl.producer == "rmsnorm":
+                y = O.rmsnorm(wl.x[:L], wl.gamma, 1e-6)
+            else:
+                y = O.glu_ex(wl.gu[:L, :K], wl.gu[:L, K:], wl.producer)
+            img = O.quantize(y, img_rows=T)
             if wl.routed:
                 O.plan(wl.ids, L, wl.E)
-                O.mmvq_id(r.qs, r.d, wl.E, K, img, T, wl.ids, L)
-            elif r.fmt == "q4_0":
-                O.mmvq(r.qs, r.d, K, img, T, L)
+            if pool is not None:
+                list(pool.map(lambda j: run_job(j, img), jobs))
             else:
-                O.mmvq_fmt(r.fmt, r.qs, r.d, r.m, K, img, T, L)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() + times[-1] > t_end or len(times) >= 24:
-            break
+                for j in jobs:
+                    run_job(j, img)
+            if wl.extra_v is not None:
+                O.moe_router(y, wl.extra_v.reshape(1, K), L)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() + times[-1] > t_end or len(times) >= 24:
+                break
+    finally:
+        if pool is not None:
+            pool.shutdown()
     return float(np.median(times)) * 1e6, len(times)
 
 
@@ -327,17 +402,108 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(kind):
-    """HBM bytes per reader launch from the committed rocprofv3 --pmc summary, or None when
-    the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "mmvq_k8192_t8_pmc.json")
-    if not os.path.exists(path):
+def pmc_file(config, live=None, wfmt="q4_0"):
+    """Name (under profiles/) of the counter summary of a workload's reader kernel, or None."""
+    if wfmt != "q4_0":
+        return None
+    names = {1: "mmvq_t1_k2560", 2: "mmvq_k8192_t8", 3: "mmvq_glu_t8_k14336_n4096",
+             4: "mmvq_routed_t8_k2560_e128_gate_up", 6: "mmq_prefill_t3325_k3584"}
+    if config == 5:
+        return "mmvq_routed_bucket128_k2048_e256_live%d_pmc" % (live if live is not None else 128)
+    return names[config] + "_pmc" if config in names and live is None else None
+
+
+def pmc_traffic(config, live=None, wfmt="q4_0"):
+    """HBM bytes per reader launch from the committed rocprofv3 --pmc summary of the workload,
+    or None when there is none or the kernel source changed since the counters were taken."""
+    name = pmc_file(config, live, wfmt)
+    path = os.path.join(ROOT, "profiles", name + ".json") if name else None
+    if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get(kind)
+    return d.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(path):
+    """(dispatch id, kernel name, counter, value) rows of a rocprofv3 counter_collection CSV
+    (a file, or the directory rocprofv3 wrote it under)."""
+    import csv
+    import glob
+    if os.path.isdir(path):
+        hits = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+        if not hits:
+            raise SystemExit("no counter_collection.csv under %s" % path)
+        path = hits[-1]
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def pmc_summarize(config, live, fetch_path, write_path, out_dir=None):
+    """Write profiles/<name>.json and .md from the two counter runs of --pmc-probe: HBM bytes
+    per reader launch = counter KiB x 1024 x the scale that makes the plain copy's counters
+    equal its known bytes."""
+    from q8_activation_quant_amd import workloads as W
+    wl = W.make(config, live=live)
+    algo = algorithmic_bytes(wl)["reader_kernel"]
+    name = pmc_file(config, live)
+    res = {}
+    for cname, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
+        per = {}
+        for disp, kname, c, v in _counter_rows(path):
+            if c == cname:
+                per.setdefault(disp, [kname, 0.0])[1] += v
+        reader = [v for k, v in per.values() if "mmvq_" in k or "mmq_kernel" in k]
+        copy = [v for k, v in per.values() if "copyBuffer" in k]
+        kn = sorted({k for k, v in per.values() if "mmvq_" in k or "mmq_kernel" in k})
+        if not reader or not copy:
+            raise SystemExit("%s: reader or calibration dispatches missing" % cname)
+        res[cname] = {"reader_kib_avg": float(np.mean(reader)), "dispatches": len(reader),
+                      "copy_kib": float(copy[-1]), "kernel": kn[0] if kn else None}
+    copy_bytes = 256 << 20
+    rs = copy_bytes / (res["FETCH_SIZE"]["copy_kib"] * 1024)
+    ws = copy_bytes / (res["WRITE_SIZE"]["copy_kib"] * 1024)
+    rd = res["FETCH_SIZE"]["reader_kib_avg"] * 1024 * rs
+    wr = res["WRITE_SIZE"]["reader_kib_avg"] * 1024 * ws
+    probe = "python3 bench.py --pmc-probe --config %d%s" % (config, "" if live is None else " --live %d" % live)
+    d = {"kernel_name_in_trace": res["FETCH_SIZE"]["kernel"], "workload": WORKLOAD_NAMES[config],
+         "live_rows": live, "kernel_source_sha256_16": kernel_source_hash(),
+         "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_f -o fetch -- " + probe,
+                      "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_w -o write -- " + probe],
+         "calibration": {"kernel": "__amd_rocclr_copyBuffer, %d-byte device copy" % copy_bytes,
+                         "FETCH_SIZE_KiB": res["FETCH_SIZE"]["copy_kib"], "WRITE_SIZE_KiB": res["WRITE_SIZE"]["copy_kib"],
+                         "read_scale": round(rs, 5), "write_scale": round(ws, 5)},
+         "reader_dispatches": res["FETCH_SIZE"]["dispatches"],
+         "reader_FETCH_SIZE_KiB_avg": round(res["FETCH_SIZE"]["reader_kib_avg"], 1),
+         "reader_WRITE_SIZE_KiB_avg": round(res["WRITE_SIZE"]["reader_kib_avg"], 1),
+         "hbm_read_bytes_per_launch": int(round(rd)), "hbm_write_bytes_per_launch": int(round(wr)),
+         "hbm_bytes_per_launch": int(round(rd + wr)), "algorithmic_bytes_per_launch": int(algo)}
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out_dir, name + ".json"), "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    md = ["# HBM traffic of the reader kernel: %s%s" % (WORKLOAD_NAMES[config],
+                                                        "" if live is None else ", live rows %d" % live),
+          "", "Commands (one counter per run; `--pmc-probe` launches the reader once per rotated",
+          "instance, then a plain 256 MiB device copy that calibrates the counters):", ""]
+    md += ["    " + c for c in d["commands"]]
+    md += ["", "| kernel | FETCH_SIZE KiB / dispatch | WRITE_SIZE KiB / dispatch |", "|---|---|---|",
+           "| __amd_rocclr_copyBuffer (%d B copy) | %.1f | %.1f |" % (copy_bytes, res["FETCH_SIZE"]["copy_kib"],
+                                                                   res["WRITE_SIZE"]["copy_kib"]),
+           "| %s (avg of %d) | %.1f | %.1f |" % (d["kernel_name_in_trace"], d["reader_dispatches"],
+                                                d["reader_FETCH_SIZE_KiB_avg"], d["reader_WRITE_SIZE_KiB_avg"]),
+           "", "Scales from the copy: read %.5f, write %.5f." % (rs, ws),
+           "Reader per launch: %.3f MB read + %.3f MB written = %.3f MB against %d algorithmic bytes "
+           "(%+.1f%%)." % (rd / 1e6, wr / 1e6, (rd + wr) / 1e6, algo, 100 * ((rd + wr) / algo - 1)),
+           "Kernel source hash (first 16 hex of SHA-256 of qimg.hip): %s." % d["kernel_source_sha256_16"], ""]
+    with open(os.path.join(out_dir, name + ".md"), "w") as f:
+        f.write("\n".join(md))
+    return d
 
 
 WORKLOAD_NAMES = {
@@ -351,7 +517,7 @@ WORKLOAD_NAMES = {
 
 
 def run(config, steps, warmup, live=None, glu_op="swiglu", want_cpu=True, arms=("fused", "control"),
-        wfmt="q4_0"):
+        wfmt="q4_0", want_ceiling=True):
     torch = _t()
     from q8_activation_quant_amd import workloads as W
     wl = W.make(config, live=live, glu_op=glu_op, wfmt=wfmt)
@@ -371,11 +537,32 @@ def run(config, steps, warmup, live=None, glu_op="swiglu", want_cpu=True, arms=(
         "us_range": {a: [float(min(v)), float(max(v))] for a, v in per_arm.items()},
         "reader_us": float(np.median(kern)), "producer_us": float(np.median(prod)),
     }
-    if want_cpu:
-        res["cpu_us"], res["cpu_reps"] = cpu_baseline(wl)
+    if wl.extra_v is not None:
+        res["extra_us"] = float(np.median(time_graph([i.extra for i in insts], steps, warmup)))
     del insts
     torch.cuda.empty_cache()
+    if want_ceiling:
+        res["ceiling_us"], res["ceiling_bytes"] = time_ceiling(nb["reader_kernel"], steps, warmup)
+    if want_cpu:
+        res["cpu_us"], res["cpu_reps"] = cpu_baseline(wl, threads=1)
+        res["cpu_threads"] = cpu_threads()
+        res["cpu_all_us"], res["cpu_all_reps"] = cpu_baseline(wl, threads=res["cpu_threads"])
     return res
+
+
+def time_ceiling(nbytes, steps, warmup):
+    """Per-launch microseconds of the plain streaming read of nbytes (rounded up to 1 KB) over
+    rotated buffers of at least ROT_BYTES in all, so every launch reads HBM."""
+    torch = _t()
+    from q8_activation_quant_amd import qimg
+    nb = -(-int(nbytes) // 1024) * 1024
+    R = max(2, -(-ROT_BYTES // nb))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.empty(qimg.CEILING_SINK_WORDS, dtype=torch.int32, device="cuda")
+    us = time_graph([(lambda b=b: qimg.read_ceiling(b, sink)) for b in bufs], steps, warmup)
+    del bufs
+    torch.cuda.empty_cache()
+    return float(np.median(us)), nb
 
 
 def main():
@@ -396,7 +583,14 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="counter-collection run: one reader launch per rotated instance of the "
                          "workload, then a plain 256 MiB device copy (the calibration kernel)")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH", "WRITE"),
+                    help="write the workload's counter summary under profiles/ from the rocprofv3 "
+                         "output (CSV file or directory) of the FETCH_SIZE and WRITE_SIZE runs")
     args = ap.parse_args()
+    if args.pmc_summarize:
+        print(json.dumps(pmc_summarize(args.config, args.live if args.config == 5 else None,
+                                       *args.pmc_summarize)), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the design notes "
               "for how it would shard); run with --gpus 1", file=sys.stderr)
@@ -454,8 +648,8 @@ def main():
     wl, nb = r["wl"], r["bytes"]
     us = r["us"]["fused"]
     reader_gbs = nb["reader_kernel"] / (r["reader_us"] * 1e-6) / 1e9
-    # the committed counters cover the Q4_0 readers of the K8192/T8 workload only
-    traffic = pmc_traffic("hbm_bytes_per_launch") if (args.config == 2 and args.wfmt == "q4_0" and args.live is None) else None
+    traffic = pmc_traffic(args.config, wl.live if args.config == 5 else args.live, args.wfmt)
+    ceil_gbs = r["ceiling_bytes"] / (r["ceiling_us"] * 1e-6) / 1e9
     line = {
         "metric": "us per component graph + achieved HBM GB/s (% of peak), 1 MI355X",
         "value": round(us, 3),
@@ -493,8 +687,18 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": nb["reader_kernel"],
             "avg_launch_us": round(r["reader_us"], 3),
+            # the plain streaming read of the same byte count (read_ceiling_kernel, one launch
+            # per rotated buffer): what this GPU reaches on a contiguous read of that size
+            "measured_ceiling": {"achieved": round(ceil_gbs, 1), "unit": "GB/s",
+                                 "frac_of_peak": round(ceil_gbs / PEAK_HBM_GBS, 4),
+                                 "reader_frac_of_ceiling": round(reader_gbs / ceil_gbs, 4),
+                                 "avg_launch_us": round(r["ceiling_us"], 3), "bytes_per_launch": r["ceiling_bytes"]},
         },
     }
+    if "extra_us" in r:
+        line["extra_f32_reader"] = {"avg_launch_us": round(r["extra_us"], 3),
+                                    "bytes_per_launch": nb["extra_f32_reader"],
+                                    "GBs": round(nb["extra_f32_reader"] / (r["extra_us"] * 1e-6) / 1e9, 1)}
     if args.config == 6:
         # the prefill reader is bound by its per-block scaling on the vector ALUs: 2 operations
         # (convert the block's int32 dot, one fused multiply-add by d_w d_a, which the matrix
@@ -509,8 +713,13 @@ def main():
                                 "int8_mfma_Tops": round(2.0 * wl.T * sum(wl.reader_rows) * wl.K
                                                         / (r["reader_us"] * 1e-6) / 1e12, 1)}
     if "cpu_us" in r:
-        line["cpu_baseline"] = {"value": round(r["cpu_us"], 1), "unit": "us", "cores": 1, "kind": "oracle",
-                                "sample": "%d full component graph(s) of the same workload (median)" % r["cpu_reps"]}
+        line["cpu_baseline"] = {"value": round(r["cpu_all_us"], 1), "unit": "us", "cores": r["cpu_threads"],
+                                "kind": "oracle",
+                                "sample": "%d full component graph(s) of the same workload (median); readers' "
+                                          "output rows split over the threads" % r["cpu_all_reps"],
+                                "single_thread": {"value": round(r["cpu_us"], 1), "cores": 1,
+                                                  "sample": "%d full component graph(s) (median)" % r["cpu_reps"]},
+                                "nproc": os.cpu_count(), "cpu_model": cpu_model()}
     print(json.dumps(line), flush=True)
     if args.all:
         for c, live in [(1, None), (3, None), (4, None), (5, 1), (5, 9), (5, 113), (5, 114), (5, 128)]:

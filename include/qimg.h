@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define QIMG_ABI_VERSION 11
+#define QIMG_ABI_VERSION 12
 
 /* status codes */
 #define QIMG_OK 0
@@ -430,6 +430,19 @@ int mmvq_q4_0_q8_1_blockdots(const qimg_q4_0_reader* reader, const void* img, in
 #define QIMG_MATH_QDIV 6
 #define QIMG_MATH_F2H 7
 int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void* stream);
+
+/*
+ * Measurement aid, not a step of the method (no page defines it): the rate this GPU streams a
+ * plain contiguous buffer at, the ceiling a reader's achieved HBM rate is set against. Reads
+ * bytes of buf exactly once: 256 workgroups of 8 waves, each workgroup a contiguous run of
+ * 1 KB pieces that its waves take in turn, four 16-byte nontemporal loads in flight per lane.
+ * Writes one 32-bit XOR of the data per wave to sink, so that no load is dead.
+ *   buf  : device, 16-byte aligned, bytes % 1024 == 0, 0 < bytes < 2^31.
+ *   sink : device uint32[QIMG_CEILING_SINK_WORDS], 4-byte aligned, must not overlap buf.
+ * Errors: QIMG_EINVAL (null pointer, bytes out of range), QIMG_EALIGN, QIMG_EALIAS, QIMG_EHIP.
+ */
+#define QIMG_CEILING_SINK_WORDS 2048
+int qimg_read_ceiling(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

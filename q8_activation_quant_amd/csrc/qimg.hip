@@ -101,6 +101,18 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
   return pair_sum_halves(v);
 }
 
+// XOR over the 64 lanes (every lane receives it)
+__device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
+  v ^= (uint32_t)dpp_n<kDppXor1>((int)v);
+  v ^= (uint32_t)dpp_n<kDppXor2>((int)v);
+  v ^= (uint32_t)dpp_n<kDppHalfMirror>((int)v);
+  v ^= (uint32_t)dpp_n<kDppMirror>((int)v);
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // lanes l and l ^ 16
+  v = r[0] ^ r[1];
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // lanes l and l ^ 32
+  return h[0] ^ h[1];
+}
+
 // balanced pairwise tree over a lane's JW values (JW a power of two)
 template <int JW>
 __device__ __forceinline__ float tree_sum(float (&v)[JW]) {
@@ -1913,6 +1925,41 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   }
 }
 
+// Plain streaming read of a contiguous buffer (the measured ceiling of the readers): workgroup
+// i reads pieces [i per, (i + 1) per) of 1 KB, its wave w pieces w, w + 8, ... with four loads
+// in flight; loads past the wave's last piece go to an out-of-range offset (no memory access).
+constexpr int kCeilWaves = 8, kCeilDepth = 4, kCeilGrid = 256;
+static_assert(kCeilGrid * kCeilWaves == QIMG_CEILING_SINK_WORDS, "one sink word per wave");
+__global__ __launch_bounds__(kCeilWaves * 64) void read_ceiling_kernel(const uint8_t* buf, uint32_t pieces,
+                                                                       uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t per = (pieces + gridDim.x - 1) / gridDim.x;
+  const uint32_t c0 = blockIdx.x * per;
+  const uint32_t c1 = c0 + per < pieces ? c0 + per : pieces;
+  const int n = c0 + w < c1 ? (int)((c1 - c0 - w + kCeilWaves - 1) / kCeilWaves) : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)buf, (short)0, (int)(pieces * 1024u), kBufferFlags);
+  auto off = [&](int j) {
+    return j < n ? (c0 + w + (uint32_t)kCeilWaves * (uint32_t)j) * 1024u + 16u * lane : 0x80000000u;
+  };
+  v4u q[kCeilDepth];
+#pragma unroll
+  for (int j = 0; j < kCeilDepth; ++j) q[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(j), 0u, kNt);
+  uint32_t acc = 0;
+  for (int b = 0; b < n; b += kCeilDepth) {
+#pragma unroll
+    for (int j = 0; j < kCeilDepth; ++j) {
+      acc ^= q[j].x ^ q[j].y ^ q[j].z ^ q[j].w;
+      q[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(b + kCeilDepth + j), 0u, kNt);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCeilDepth; ++j) acc ^= q[j].x;  // the last loads (zeros) land before the exit
+  acc = wave_xor(acc);
+  if (lane == 0) sink[blockIdx.x * kCeilWaves + w] = acc;
+}
+
 // Standard planes -> tiled order (see the reader notes above). Rows and blocks past N and
 // K/32 are written as zeros, so tiles and chunks are always whole. FMT 0 Q4_0 and 2 Q4_1:
 // 1 KB of codes per chunk (lane l: the 16 bytes of block 4 s + l/16 of row l%16); Q8_0:
@@ -2784,6 +2831,15 @@ int qimg_eval_math(int32_t fn, uint32_t first_bits, int64_t n, float* out, void*
     case MATH_GEGLU_QUICK: eval_math_kernel<MATH_GEGLU_QUICK><<<grid, 256, 0, s>>>(first_bits, n, out); break;
     default: eval_math_kernel<MATH_OAI_GATE><<<grid, 256, 0, s>>>(first_bits, n, out); break;
   }
+  return launch_status();
+}
+
+int qimg_read_ceiling(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes <= 0 || bytes % 1024 || bytes >= ((int64_t)1 << 31)) return QIMG_EINVAL;
+  if (!al16(buf) || !al(sink, 4)) return QIMG_EALIGN;
+  if (overlap(span(buf, bytes), span(sink, QIMG_CEILING_SINK_WORDS * 4))) return QIMG_EALIAS;
+  hipLaunchKernelGGL(read_ceiling_kernel, dim3(kCeilGrid), dim3(kCeilWaves * 64), 0, (hipStream_t)stream,
+                     (const uint8_t*)buf, (uint32_t)(bytes / 1024), sink);
   return launch_status();
 }
 

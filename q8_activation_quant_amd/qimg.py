@@ -19,7 +19,7 @@ GLU_OPS = {"swiglu": GLU_SWIGLU, "geglu_erf": GLU_GEGLU_ERF, "reglu": GLU_REGLU,
            "geglu_quick": GLU_GEGLU_QUICK, "swiglu_oai": GLU_SWIGLU_OAI, "swiglu_clamp": GLU_SWIGLU_CLAMP}
 ERR_EXPERT_RANGE, ERR_LIVE_CLAMPED = 1, 2
 MAX_READERS = 8
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 EXPORTS = (
     "qimg_strerror", "qimg_abi_version", "qimg_row_blocks", "qimg_image_bytes",
@@ -30,7 +30,9 @@ EXPORTS = (
     "qimg_emit_rmsnorm_ex", "qimg_emit_glu_ex", "qimg_moe_router", "qimg_moe_topk",
     "qimg_q8_0_tiled_bytes", "qimg_q4_1_tiled_bytes", "qimg_q8_0_tile", "qimg_q4_1_tile",
     "mmvq_q8_0_q8_1", "mmvq_q4_1_q8_1", "mmq_q4_0_q8_1", "qimg_f32_reader", "mmvq_id_q4_0_q8_1_noalloc",
+    "qimg_read_ceiling",
 )
+CEILING_SINK_WORDS = 2048
 MATH_FNS = {"exp": 0, "erfc": 1, "swiglu": 2, "geglu_erf": 3, "rsqrt": 4, "qscale": 5, "qdiv": 6, "f2h": 7, "reglu": 8,
             "geglu": 9, "geglu_quick": 10, "swiglu_oai_gate": 11}
 
@@ -93,6 +95,7 @@ def lib() -> ctypes.CDLL:
             "mmvq_q4_1_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "mmq_q4_0_q8_1": (ctypes.c_int, [ctypes.POINTER(Reader), i32, P, i32, P, i32, P]),
             "qimg_f32_reader": (ctypes.c_int, [P, i64, P, i32, i32, P, i32, P, i64, P]),
+            "qimg_read_ceiling": (ctypes.c_int, [P, i64, P, P]),
             "mmvq_id_q4_0_q8_1_noalloc": (ctypes.c_int, [ctypes.POINTER(ExpertReader), i32, i32, P, P, i32, i32,
                                                          P, i32, P]),
             "qimg_moe_topk": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P]),
@@ -258,6 +261,13 @@ def mmvq_id_noalloc(readers, E, img, ids, live_rows, K, stream=None):
     arr = _readers(readers, ExpertReader)
     _check(lib().mmvq_id_q4_0_q8_1_noalloc(arr, len(readers), E, _ptr(img), _ptr(ids), bucket, top_k,
                                            _ptr(live_rows), K, _stream(stream)), "mmvq_id_q4_0_q8_1_noalloc")
+
+
+def read_ceiling(buf, sink, stream=None):
+    """Measurement aid: stream buf (a contiguous device tensor, bytes % 1024 == 0) once with the
+    plain read kernel; sink: int32 device tensor of CEILING_SINK_WORDS words."""
+    _check(lib().qimg_read_ceiling(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "qimg_read_ceiling")
 
 
 def mmvq_id_per_slot(readers, E, img, ids, live_rows, K, workspace, stream=None):

@@ -413,3 +413,15 @@ def test_noalloc_routed_validation(L):
     # beyond the per-GPU plan array (and the routed pair limit): rejected before anything else
     assert na(bucket=4097, k=1) == qimg.EUNSUPPORTED
     assert na(E=2048) == qimg.EUNSUPPORTED
+
+
+def test_read_ceiling_validation(L):
+    rc = lambda buf=A, n=1 << 20, sink=D: L.qimg_read_ceiling(buf, n, sink, S)
+    assert rc(buf=None) == qimg.EINVAL
+    assert rc(sink=None) == qimg.EINVAL
+    assert rc(n=0) == qimg.EINVAL
+    assert rc(n=1000) == qimg.EINVAL
+    assert rc(n=1 << 31) == qimg.EINVAL
+    assert rc(buf=A + 4) == qimg.EALIGN
+    assert rc(sink=D + 2) == qimg.EALIGN
+    assert rc(sink=A + 1024) == qimg.EALIAS
