@@ -192,7 +192,7 @@ __device__ __forceinline__ float geglu_erf_act(float g) {
 // squares with products: leaf c (4 elements) = fma(x3,w3, fma(x2,w2, fma(x1,w1, x0*w0)));
 // lane l owns leaves c = l + 64 j, j < Jp (next power of two >= ceil(K/256), missing leaves
 // +0), summed by a pairwise tree over j; the 64 lane sums by a pairwise tree (wave_tree_sum).
-// One workgroup per (block of EB experts, group of 8 rows): wave w holds leaves j in
+// One workgroup per (block of EB experts, group of RT rows, RT = 8 or 1): wave w holds leaves j in
 // [w JW, (w+1) JW) of every row and expert (JW = Jp / W), sums them by the lower levels of the
 // tree, and the W wave partials are combined through LDS by its top levels; the (expert, row)
 // dots are then finished by the waves in turn. The activations of the rows are loaded once per
@@ -207,25 +207,26 @@ struct RouterArgs {
   int32_t rows, E, K;
 };
 
-template <int JW, int EB>
+template <int JW, int EB, int RT>
 __global__ __launch_bounds__(1024) void moe_router_kernel(RouterArgs a) {
+  static_assert(RT == 8 || RT == 1, "rows per workgroup");
   const int live = clamp_live(a.live_rows, a.rows, nullptr);
-  const int t0 = blockIdx.y * 8;
+  const int t0 = blockIdx.y * RT;
   if (t0 >= live) return;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* part = reinterpret_cast<float*>(smem);  // [W][EB][8][64]
+  float* part = reinterpret_cast<float*>(smem);  // [W][EB][RT][64]
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
   const int e0 = blockIdx.x * EB;
   const int ne = a.E - e0 < EB ? a.E - e0 : EB;
-  const int nt = live - t0 < 8 ? live - t0 : 8;
+  const int nt = live - t0 < RT ? live - t0 : RT;
   const int C = a.K >> 2;
   // leaves past K re-read leaf 0 (in bounds) and count as +0; experts past E re-read expert e0
   // and rows past the live count re-read row t0 (their results are not stored). All 8 rows'
   // activation leaves are loaded at once (one round trip) unless the rows are long (more than
   // 2 leaves per lane), then row by row.
-  constexpr int XT = (EB > 1 || JW <= 2) ? 8 : 1;
+  constexpr int XT = RT == 1 ? 1 : (EB > 1 || JW <= 2) ? 8 : 1;
   float4 wv[EB][JW], xv[XT][JW];
   auto load_x = [&](int t, float4 (&dst)[JW]) {
     const float* xr = a.x + (int64_t)(t0 + (t < nt ? t : 0)) * a.ldx;
@@ -247,12 +248,14 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(RouterArgs a) {
   if constexpr (XT == 8) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) load_x(t, xv[t]);
+  } else if constexpr (RT == 1) {
+    load_x(0, xv[0]);
   }
 #pragma unroll
   for (int b = 0; b < EB; ++b)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if constexpr (XT == 1) {
+    for (int t = 0; t < RT; ++t) {
+      if constexpr (XT == 1 && RT == 8) {
         if (t >= nt) break;
         load_x(t, xv[0]);
       }
@@ -265,15 +268,15 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(RouterArgs a) {
                                           __builtin_fmaf(v.y, q.y, v.x * q.x)))
                          : 0.0f;
       }
-      part[((w * EB + b) * 8 + t) * 64 + lane] = tree_sum<JW>(leaf);
+      part[((w * EB + b) * RT + t) * 64 + lane] = tree_sum<JW>(leaf);
     }
   __syncthreads();
-  for (int q = w; q < EB * 8; q += W) {
-    const int b = q >> 3, t = q & 7;
+  for (int q = w; q < EB * RT; q += W) {
+    const int b = q / RT, t = q % RT;
     if (b < ne && t < nt) {
       float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = i < W ? part[((i * EB + b) * 8 + t) * 64 + lane] : 0.0f;
+      for (int i = 0; i < 16; ++i) v[i] = i < W ? part[((i * EB + b) * RT + t) * 64 + lane] : 0.0f;
       for (int n = W; n > 1; n >>= 1)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -2703,21 +2706,33 @@ static int f32_rows_dot(const float* x, int64_t ldx, const float* w, int32_t E, 
   // experts per workgroup: 4 for buckets of many rows (each workgroup then loads its rows'
   // activations once for 4 experts) while the wave partials fit in 64 KB of LDS, else 1
   const int EB = (W <= 8 && bucket > 16) ? 4 : 1;
-  const size_t lds = (size_t)W * EB * 8 * 64 * 4;
-  const dim3 grid((unsigned)((E + EB - 1) / EB), (unsigned)((bucket + 7) / 8)), block((unsigned)(W * 64));
+  // rows per workgroup: 8 (sharing each expert's weight loads), or 1 when that leaves fewer
+  // than 128 workgroups (few experts or outputs: a lone row of a long dot is then one
+  // workgroup's work instead of eight rows in turn). The sums are the same either way.
+  const int RT = (EB == 1 && (int64_t)E * ((bucket + 7) / 8) < 128) ? 1 : 8;
+  const size_t lds = (size_t)W * EB * RT * 64 * 4;
+  const dim3 grid((unsigned)((E + EB - 1) / EB), (unsigned)((bucket + RT - 1) / RT)), block((unsigned)(W * 64));
   hipStream_t s = (hipStream_t)stream;
   if (EB == 4) {
     switch (JW) {
-      case 1: hipLaunchKernelGGL((moe_router_kernel<1, 4>), grid, block, lds, s, a); break;
-      case 2: hipLaunchKernelGGL((moe_router_kernel<2, 4>), grid, block, lds, s, a); break;
+      case 1: hipLaunchKernelGGL((moe_router_kernel<1, 4, 8>), grid, block, lds, s, a); break;
+      case 2: hipLaunchKernelGGL((moe_router_kernel<2, 4, 8>), grid, block, lds, s, a); break;
       default: return QIMG_EUNSUPPORTED;  // W <= 8 gives JW <= 2
+    }
+  } else if (RT == 8) {
+    switch (JW) {
+      case 1: hipLaunchKernelGGL((moe_router_kernel<1, 1, 8>), grid, block, lds, s, a); break;
+      case 2: hipLaunchKernelGGL((moe_router_kernel<2, 1, 8>), grid, block, lds, s, a); break;
+      case 4: hipLaunchKernelGGL((moe_router_kernel<4, 1, 8>), grid, block, lds, s, a); break;
+      case 8: hipLaunchKernelGGL((moe_router_kernel<8, 1, 8>), grid, block, lds, s, a); break;
+      default: return QIMG_EUNSUPPORTED;
     }
   } else {
     switch (JW) {
-      case 1: hipLaunchKernelGGL((moe_router_kernel<1, 1>), grid, block, lds, s, a); break;
-      case 2: hipLaunchKernelGGL((moe_router_kernel<2, 1>), grid, block, lds, s, a); break;
-      case 4: hipLaunchKernelGGL((moe_router_kernel<4, 1>), grid, block, lds, s, a); break;
-      case 8: hipLaunchKernelGGL((moe_router_kernel<8, 1>), grid, block, lds, s, a); break;
+      case 1: hipLaunchKernelGGL((moe_router_kernel<1, 1, 1>), grid, block, lds, s, a); break;
+      case 2: hipLaunchKernelGGL((moe_router_kernel<2, 1, 1>), grid, block, lds, s, a); break;
+      case 4: hipLaunchKernelGGL((moe_router_kernel<4, 1, 1>), grid, block, lds, s, a); break;
+      case 8: hipLaunchKernelGGL((moe_router_kernel<8, 1, 1>), grid, block, lds, s, a); break;
       default: return QIMG_EUNSUPPORTED;
     }
   }
