@@ -1440,9 +1440,9 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
 
   // ---- plan: per-expert counts, then offsets and segment starts ----
   for (int e = tid; e < E; e += kWaves * 64) cnt[e] = 0;
-  if (tid < 4) {
-    sh_misc[tid] = 0;
-    reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;
+  if (tid < 8) {
+    if (tid < 4) sh_misc[tid] = 0;
+    reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;  // the 32-byte zero slot
   }
   // the ids of pairs tid + 512 j (P <= pairs_cap <= 8 * 512): buffer loads, which read 0 past
   // the P live pairs' ids; all eight go out, so that their waits are exact
@@ -1748,23 +1748,33 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
 #pragma unroll
       for (int v = 0; v < 8; ++v) acc[v] = 0.0f;
       float carry0 = 0.0f, carry1 = 0.0f;  // first-half sums of the current unit
-      int a_off[2];
-      bool a_on[2];
+      // A operand of this lane for token group tg (row m = n of the product's A, k-group g):
+      // the staged 32 bytes of column 4 tg + (n & 3), block 4 cs + g, at a_base + cs a_step
+      // (low half, high half 16 bytes on), or the 32-byte zero slot (a_step = 0) when the row
+      // is outside the lane's k-group or past the segment's columns
+      int a_base[2], a_step[2];
       auto bind_a = [&](const Cursor& c) {
         const int nc = uni(sh_seg[c.k][2]);
 #pragma unroll
         for (int tg = 0; tg < 2; ++tg) {
           const int col = 4 * tg + (n & 3);
-          a_on[tg] = (n >> 2) == g && col < nc;
-          a_off[tg] = c.k * p.slot_bytes + (g * TP + col) * 32;
+          const bool on = (n >> 2) == g && col < nc;
+          a_base[tg] = on ? c.k * p.slot_bytes + (g * TP + col) * 32 : p.lds_zero;
+          a_step[tg] = on ? 4 * TP * 32 : 0;
         }
       };
       bind_a(cc);
       const int dsh = 16 * (lane & 1);  // this lane's half of a scale word
-      auto compute = [&](const uint4 (&q)[KU], const uint32_t (&d)[KU]) {
+      // One step for NTG token groups (1: up to 4 columns, 2: up to 8): every matrix-core
+      // product and LDS operand of the step first, then the scaling, so that no vector
+      // instruction waits on a product issued just before it. The sums are those of a chunk-by-
+      // chunk loop: each acc element still takes its chunks in order.
+      auto compute_ntg = [&](auto ntg_c, const uint4 (&q)[KU], const uint32_t (&d)[KU]) {
+        constexpr int NTG = decltype(ntg_c)::value;
         const float* daL = daA + cc.k * nds;
         const float* msL = msA + cc.k * nds;
-        const int TG = (uni(sh_seg[cc.k][2]) + 3) >> 2;
+        v4i dd[KU][NTG];
+        float4 da4[KU][NTG], ms4[KU][NTG];
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
           const int cs = cc.kb + u;
@@ -1778,26 +1788,39 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
           bhi[1] = (int)((q[u].y >> 4) & 0x0f0f0f0fu);
           bhi[2] = (int)((q[u].z >> 4) & 0x0f0f0f0fu);
           bhi[3] = (int)((q[u].w >> 4) & 0x0f0f0f0fu);
-          const float dw = h2f(d[u] >> dsh);
           const int blk = 4 * cs + g;
 #pragma unroll
-          for (int tg = 0; tg < 2; ++tg) {
-            if (tg >= TG) break;
-            const int lo = a_on[tg] ? cs * (4 * TP * 32) + a_off[tg] : p.lds_zero;
-            const int hi = a_on[tg] ? lo + 16 : p.lds_zero;
-            const v4i alo = *reinterpret_cast<const v4i*>(smem + lo);
-            const v4i ahi = *reinterpret_cast<const v4i*>(smem + hi);
-            const float4 da4 = *reinterpret_cast<const float4*>(daL + blk * 8 + 4 * tg);
-            const float4 ms4 = *reinterpret_cast<const float4*>(msL + blk * 8 + 4 * tg);
+          for (int tg = 0; tg < NTG; ++tg) {
+            const unsigned char* ap = smem + a_base[tg] + cs * a_step[tg];
+            const v4i alo = *reinterpret_cast<const v4i*>(ap);
+            const v4i ahi = *reinterpret_cast<const v4i*>(ap + 16);
+            da4[u][tg] = *reinterpret_cast<const float4*>(daL + blk * 8 + 4 * tg);
+            ms4[u][tg] = *reinterpret_cast<const float4*>(msL + blk * 8 + 4 * tg);
             const v4i zero = {0, 0, 0, 0};
-            v4i dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo, zero, 0, 0, 0);
-            dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi, dd, 0, 0, 0);
-            acc[4 * tg + 0] = __builtin_fmaf(dw, __builtin_fmaf(da4.x, (float)dd[0], ms4.x), acc[4 * tg + 0]);
-            acc[4 * tg + 1] = __builtin_fmaf(dw, __builtin_fmaf(da4.y, (float)dd[1], ms4.y), acc[4 * tg + 1]);
-            acc[4 * tg + 2] = __builtin_fmaf(dw, __builtin_fmaf(da4.z, (float)dd[2], ms4.z), acc[4 * tg + 2]);
-            acc[4 * tg + 3] = __builtin_fmaf(dw, __builtin_fmaf(da4.w, (float)dd[3], ms4.w), acc[4 * tg + 3]);
+            dd[u][tg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo, zero, 0, 0, 0);
+            dd[u][tg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi, dd[u][tg], 0, 0, 0);
           }
         }
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          if (cc.kb + u >= cc.ke) break;
+          const float dw = h2f(d[u] >> dsh);
+#pragma unroll
+          for (int tg = 0; tg < NTG; ++tg) {
+            const v4i x = dd[u][tg];
+            const float4 a4 = da4[u][tg], m4 = ms4[u][tg];
+            acc[4 * tg + 0] = __builtin_fmaf(dw, __builtin_fmaf(a4.x, (float)x[0], m4.x), acc[4 * tg + 0]);
+            acc[4 * tg + 1] = __builtin_fmaf(dw, __builtin_fmaf(a4.y, (float)x[1], m4.y), acc[4 * tg + 1]);
+            acc[4 * tg + 2] = __builtin_fmaf(dw, __builtin_fmaf(a4.z, (float)x[2], m4.z), acc[4 * tg + 2]);
+            acc[4 * tg + 3] = __builtin_fmaf(dw, __builtin_fmaf(a4.w, (float)x[3], m4.w), acc[4 * tg + 3]);
+          }
+        }
+      };
+      auto compute = [&](const uint4 (&q)[KU], const uint32_t (&d)[KU]) {
+        if (uni(sh_seg[cc.k][2]) > 4)
+          compute_ntg(std::integral_constant<int, 2>{}, q, d);
+        else
+          compute_ntg(std::integral_constant<int, 1>{}, q, d);
       };
       // after a compute step: at the end of a half-unit, sum the k-group lanes; at the end of
       // a unit store (or hand over), and move the compute cursor to the next half-unit
@@ -2202,7 +2225,7 @@ int run_ordinary(ReadArgs& a, hipStream_t s) {
 
 // Routed readers: one workgroup per CU over the (expert, pass, tile) units. LDS: the codes of
 // `slots` staged segments, [4 KC][tp][32] each, then their f32 d_a and -8 s_a, [slot][4 KC][8]
-// each, the zero slot, the half-unit carry slots, then the plan arrays sid[pairs, padded to
+// each, the 32-byte zero slot, the half-unit carry slots, then the plan arrays sid[pairs, padded to
 // 256] (expert of each live pair), cnt[E], off[E+1], pps[E+1] (first segment of each expert).
 constexpr int kXoBytes = kWaves * 64 * 8;
 int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
@@ -2221,7 +2244,7 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   for (int need : {2, 1}) {
     for (int tp : {8, 4, 2, 1}) {
       const int slot = nb * tp * 32 + nb * 64;
-      int slots = (kMaxLds - 16 - kXoBytes - plan) / slot;
+      int slots = (kMaxLds - 32 - kXoBytes - plan) / slot;
       if (slots > kRoutedMaxSlots) slots = kRoutedMaxSlots;
       if (slots >= need) {
         a.tp = tp;
@@ -2231,7 +2254,7 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
         a.lds_da = slots * a.slot_bytes;
         a.lds_ms = a.lds_da + slots * nb * 32;
         a.lds_zero = a.lds_ms + slots * nb * 32;
-        a.lds_xo = a.lds_zero + 16;
+        a.lds_xo = a.lds_zero + 32;
         a.lds_plan = a.lds_xo + kXoBytes;
         lds = a.lds_plan + plan;
         break;
