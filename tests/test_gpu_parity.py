@@ -523,6 +523,35 @@ def test_routed_single_expert_and_all_pairs_bad():
         assert (out.view(np.uint8) == H.SENTINEL_BYTE).all()
 
 
+@pytest.mark.parametrize("K", [128, 1024, 1536, 2560])
+def test_routed_k_halves_and_one_row_runs(K):
+    # K 128: units whole (one chunk); 1024, 1536, 2560: cut into two K halves (4 + 4, 6 + 6,
+    # 10 + 10 chunks). Few tiles per expert and many workgroups, so a unit's halves often fall to
+    # two waves (the first half's sums then go through a carry slot); every live row must still
+    # equal its one-row run byte for byte
+    print("routed K halves", K, flush=True)
+    g = np.random.default_rng(K)
+    B, E, k = 64, 12, 3
+    x = g.standard_normal((B, K)).astype(np.float32)
+    gamma = g.normal(1.0, 0.1, K).astype(np.float32)
+    ids, w = W.topk_ids(g, B, E, k)
+    for live in (B, 3):
+        wl = W.Workload(0, "parts", B, K, "rmsnorm", x=x, gamma=gamma,
+                        readers=[W.q4_0_weights(g, (E, 40), K)], E=E, top_k=k, ids=ids, route_w=w, live=live)
+        attach_dev_weights(wl)
+        y, img = run_producer(wl, live=live)
+        _, img_o = check_producer(wl, y, img, live=live)
+        outs, ws = run_routed(wl, H.dev(img), ids, live=live)
+        check_plan(ws, ids, live, E, k)
+        check_routed(wl, img_o, outs, live)
+        for t in sorted({0, live // 2, live - 1}):
+            w1 = W.Workload(0, "one row", 1, K, "rmsnorm", x=x[t:t + 1].copy(), gamma=gamma,
+                            readers=wl.readers, E=E, top_k=k, ids=ids[t:t + 1].copy())
+            y1, img1 = run_producer(w1)
+            o1, _ = run_routed(w1, H.dev(img1), w1.ids)
+            assert np.array_equal(o1[0][0].view(np.uint32), outs[0][t].view(np.uint32)), "row %d" % t
+
+
 # ---- padded bucket -------------------------------------------------------------------------------
 @pytest.mark.parametrize("live", [1, 9, 113, 114, 128])
 def test_padded_bucket(live):
