@@ -1366,14 +1366,14 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
 // pass of up to TP of its pairs; units are ordered by (expert, pass, tile), and an (expert,
 // pass) is a segment of T units, T = tiles per expert. Workgroup i takes units
 // [U i / G, U (i + 1) / G) in batches of up to `slots` segments, whose image columns it stages
-// in LDS (all K blocks); its waves split the batch's units contiguously. A wave streams its
-// units one tile at a time over the full K, KU chunks per load, two loads in flight; the loads
-// of the next unit go out before the current one ends, so the stream does not drain between
-// units. The first weight loads of a batch go out right after the loads of its staged image
-// columns. After the last chunk of a unit
-// the four k-group lanes of each row are summed and the lanes store their outputs directly. The
-// sum for a pair depends only on its image row and expert (chunks in K order, then the fixed
-// lane tree): not on the other pairs, the live count or the schedule.
+// in LDS (all K blocks). Each unit is cut along K into two halves at a chunk fixed by K (or kept
+// whole when K is too short), and the batch's half-units are split contiguously over the waves.
+// A wave streams its half-units one tile at a time, KU chunks per load, two loads in flight; the
+// loads of the next half-unit go out before the current one ends, so the stream does not drain.
+// After the last chunk of a half the four k-group lanes of each row are summed; the two half
+// sums are added (through an LDS carry slot when two waves hold them) and stored. The sum for a
+// pair depends only on its image row and expert (each half's chunks in K order, the fixed lane
+// tree, then first + second): not on the other pairs, the live count or the schedule.
 // ---------------------------------------------------------------------------------------------
 constexpr int kRoutedMaxSlots = 4;
 constexpr int kRoutedKu = 2;  // chunks per load of a routed wave; two loads in flight
