@@ -1212,7 +1212,9 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 // Per 4-block chunk: the 64 image rows x 4 blocks are staged in LDS (double buffered, the next
 // chunk's loads in flight during the products), then 16 products and the scaling
 // acc += d_w (d_a sumi - 8 s_a) per block. Image rows past the live count, rows past N and
-// blocks past K/32 contribute nothing and are not stored.
+// blocks past K/32 contribute nothing and are not stored. Every LDS operand is laid out so that
+// lane l reads at 4 l or 8 l bytes of a 256- or 512-byte run (no bank conflicts), and the f16
+// operand slots that must be zero are read from words that stay zero instead of being masked.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMmqWaves = 4;
 constexpr int kMmqMinRows = 64;  // Q4_0 readers of this many image rows or more use this kernel
@@ -1224,12 +1226,18 @@ typedef long v1l;
 // core. Each (image row, weight row, block) then costs a convert and one fma:
 //   acc += (d_w d_a) sumi;     out = acc - 8 sum_b d_w s_a.
 __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
-  // [buf][block][image row][32 codes + 4 pad]: the 36-byte row pitch spreads the 16 image rows
-  // of a product over distinct LDS banks
-  __shared__ __align__(16) unsigned char s_codes[2][4][64][36];
-  __shared__ __align__(16) uint16_t s_das[2][64][8];             // d_a[4 blocks], s_a[4 blocks]
-  __shared__ __align__(16) uint32_t s_wq[kMmqWaves][64][4];      // regrouped weight codes
-  __shared__ __align__(16) uint16_t s_wd[kMmqWaves][16][4];      // weight scales [row][block]
+  // image codes [buf][block][sub-tile j][k group g][image row n of the sub-tile][2 dwords]: lane
+  // (n, g) = n + 16 g reads its two dwords (bytes 4g..4g+3 and 16+4g..16+4g+3 of image row
+  // 16 j + n) at byte 8 lane of the sub-tile's 512, so a read covers consecutive banks
+  __shared__ __align__(16) uint2 s_codes[2][4][4][4][16];
+  // d_a[4 blocks] | s_a[4 blocks] per image row; row 64 stays zero and is what the lanes of k
+  // groups 1..3 read (their f16 operand slots must be zero)
+  __shared__ __align__(16) uint16_t s_das[2][65][8];
+  __shared__ __align__(16) uint32_t s_wq[kMmqWaves][4][64];  // regrouped weight codes [block][lane]
+  // weight-side f16 operands, zero outside the lanes of k group 0: per block b the word with
+  // d_w[row][b] in slot b, and the word with the 4 blocks' d_w
+  __shared__ __align__(16) uint64_t s_wdb[kMmqWaves][4][64];
+  __shared__ __align__(16) uint64_t s_wd4[kMmqWaves][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -1246,6 +1254,15 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
   const int lt = tile - p.tile_start[ri];
   const uint8_t* wq = p.r[ri].qs + ((int64_t)lt * KC * 64 + lane) * 16;
   const uint16_t* wdp = p.r[ri].d + (int64_t)lt * KC * 64 + lane;
+
+  // the zero words: each wave its own scale operands, thread 0 the zero rows of both buffers
+  {
+    uint4* z = reinterpret_cast<uint4*>(&s_wdb[w][0][0]);
+    z[lane] = make_uint4(0, 0, 0, 0);
+    z[lane + 64] = make_uint4(0, 0, 0, 0);
+    s_wd4[w][lane] = 0ull;
+    if (tid < 2) *reinterpret_cast<uint4*>(&s_das[tid][64][0]) = make_uint4(0, 0, 0, 0);
+  }
 
   // staging of one chunk: thread tid -> image row c0 + (tid & 63), block 4 s + (tid >> 6)
   const int sr = tid & 63, sb = tid >> 6;
@@ -1269,17 +1286,19 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
     wdv = wdp[(int64_t)s * 64];
   };
   auto store_chunk = [&](int buf) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&s_codes[buf][sb][sr][0]);  // 4-byte aligned
-    dst[0] = ic0.x; dst[1] = ic0.y; dst[2] = ic0.z; dst[3] = ic0.w;
-    dst[4] = ic1.x; dst[5] = ic1.y; dst[6] = ic1.z; dst[7] = ic1.w;
+    s_codes[buf][sb][sr >> 4][0][sr & 15] = make_uint2(ic0.x, ic1.x);
+    s_codes[buf][sb][sr >> 4][1][sr & 15] = make_uint2(ic0.y, ic1.y);
+    s_codes[buf][sb][sr >> 4][2][sr & 15] = make_uint2(ic0.z, ic1.z);
+    s_codes[buf][sb][sr >> 4][3][sr & 15] = make_uint2(ic0.w, ic1.w);
     s_das[buf][sr][sb] = (uint16_t)(idw & 0xffffu);
     s_das[buf][sr][4 + sb] = (uint16_t)(idw >> 16);
     // lane (row n, block g) holds bytes 0..15 of block g: dword k goes to lane (n, k), slot g
-    s_wq[w][n + 16 * 0][g] = wv.x;
-    s_wq[w][n + 16 * 1][g] = wv.y;
-    s_wq[w][n + 16 * 2][g] = wv.z;
-    s_wq[w][n + 16 * 3][g] = wv.w;
-    s_wd[w][n][g] = wdv;
+    s_wq[w][g][n + 16 * 0] = wv.x;
+    s_wq[w][g][n + 16 * 1] = wv.y;
+    s_wq[w][g][n + 16 * 2] = wv.z;
+    s_wq[w][g][n + 16 * 3] = wv.w;
+    reinterpret_cast<uint16_t*>(&s_wdb[w][g][n])[g] = wdv;
+    reinterpret_cast<uint16_t*>(&s_wd4[w][n])[g] = wdv;
   };
   float acc[4][4];
   v4f sacc[4];
@@ -1289,6 +1308,8 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[j][v] = 0.0f;
   }
+  // the scale rows this lane reads: its image rows in k group 0, the zero row elsewhere
+  const int das_row = g == 0 ? n : 64, das_step = g == 0 ? 16 : 0;
 
   load_chunk(0);
   store_chunk(0);
@@ -1296,33 +1317,28 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
   for (int s = 0; s < KC; ++s) {
     const int buf = s & 1;
     if (s + 1 < KC) load_chunk(s + 1);
-    // this lane's weights: bytes 4g..4g+3 of blocks 4s..4s+3 of row n; the f16 operands of
-    // the scale products live in the lanes of k group 0 (the other k slots are zero)
-    const uint4 wr = *reinterpret_cast<const uint4*>(&s_wq[w][lane][0]);
-    const uint32_t wb[4] = {wr.x, wr.y, wr.z, wr.w};
-    const uint64_t dwv = g == 0 ? *reinterpret_cast<const uint64_t*>(&s_wd[w][n][0]) : 0ull;
+    const uint64_t dwv = s_wd4[w][lane];
     uint64_t dav[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint64_t* ds4 = reinterpret_cast<const uint64_t*>(&s_das[buf][16 * j + n][0]);
-      dav[j] = g == 0 ? ds4[0] : 0ull;
-      const uint64_t sav = g == 0 ? ds4[1] : 0ull;
-      sacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_v4h(dwv), as_v4h(sav), sacc[j], 0, 0, 0);
+      const uint64_t* ds4 = reinterpret_cast<const uint64_t*>(&s_das[buf][das_row + das_step * j][0]);
+      dav[j] = ds4[0];
+      sacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_v4h(dwv), as_v4h(ds4[1]), sacc[j], 0, 0, 0);
     }
-    // one block at a time (a full unroll keeps every block's products live: 324 registers)
+    // one block per loop step: unrolled, the compiler hoists every block's products (206
+    // registers instead of 116: two waves per SIMD instead of four)
 #pragma unroll 1
     for (int b = 0; b < 4; ++b) {
-      const uint32_t lo = wb[b] & 0x0f0f0f0fu, hi = (wb[b] >> 4) & 0x0f0f0f0fu;
+      const uint32_t wbb = s_wq[w][b][lane];
+      const uint32_t lo = wbb & 0x0f0f0f0fu, hi = (wbb >> 4) & 0x0f0f0f0fu;
       const v1l a = (v1l)(((uint64_t)hi << 32) | lo);
-      const uint64_t dwb = dwv & (0xffffull << (16 * b));  // d_w of block b in k slot b
+      const uint64_t dwb = s_wdb[w][b][lane];
       v4i dd[4];
       v4f dwda[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const unsigned char* cp = &s_codes[buf][b][16 * j + n][0];
-        const uint32_t clo = *reinterpret_cast<const uint32_t*>(cp + 4 * g);
-        const uint32_t chi = *reinterpret_cast<const uint32_t*>(cp + 16 + 4 * g);
-        const v1l bb = (v1l)(((uint64_t)chi << 32) | clo);
+        const uint2 cc = s_codes[buf][b][j][g][n];
+        const v1l bb = (v1l)(((uint64_t)cc.y << 32) | cc.x);
         const v4i zero = {0, 0, 0, 0};
         const v4f fzero = {0.0f, 0.0f, 0.0f, 0.0f};
         dd[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bb, zero, 0, 0, 0);
