@@ -1375,8 +1375,9 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
 // (LDS atomics); one scan gives each expert's pair offset and the first of its work units. The
 // members of an expert in ascending pair order come from a scan of the ids with wave ballots
 // (no sort): a wave walks the ids 64 at a time and places each match at its rank. The plan is
-// exported to the workspace at the end (workgroup 0: counts, offsets, error word; every wave of
-// the grid: the members of the experts e = wave, wave + waves in grid, ...).
+// exported to the workspace: the members of each segment (a pass of up to TP pairs of one
+// expert) by the workgroup holding the segment's first unit, as it stages it; the counts,
+// offsets and error word by workgroup 0 at the end.
 //
 // Work. A unit is one 16-row tile (over the concatenated readers) of one active expert for one
 // pass of up to TP of its pairs; units are ordered by (expert, pass, tile), and an (expert,
@@ -1664,6 +1665,16 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
         d[u] = __builtin_amdgcn_raw_buffer_load_b32(rd, vd + cs * 128u, 0u, kNt);
       }
     };
+    // The plan's members of each segment whose first unit this workgroup holds (so every
+    // segment is exported by exactly one workgroup), stored ahead of the staging copies: the
+    // staging wait below then covers these stores as well, and no barrier waits for them.
+    if (w < ns) {
+      const int st = uni(sh_seg[w][0]);
+      if (st >= ub && st < ue) {
+        const int e = uni(sh_seg[w][1]), nc = uni(sh_seg[w][2]), lo = uni(sh_seg[w][3]) * TP;
+        if (lane < nc) p.ws[4 + 2 * E + 1 + off[e] + lo + lane] = sh_mem[w][lane];
+      }
+    }
     // Stage the batch by direct global-to-LDS copies (no registers). Codes: 1 KB per wave
     // instruction into [4 KC][TP][32] per slot (lane l: half l & 1 of column (l >> 1) & (TP - 1)
     // of block i >> (1 + log2 TP), i = 64 q + l for instruction q). Scales: the raw words
@@ -1940,10 +1951,9 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     }
     ub = ue;
   }
-  // The plan, exported after the last barrier (a global store before a barrier makes that
-  // barrier wait for every load in flight): workgroup 0 the counts, offsets and error word,
-  // every wave the members of the experts e = wave, wave + waves in grid, ... in ascending
-  // pair order.
+  // The rest of the plan, exported after the last barrier (a global store before a barrier
+  // makes that barrier wait for every load in flight): workgroup 0 the counts, offsets and
+  // error word (the members went out with each batch's staging).
   if (blockIdx.x == 0) {
     int32_t* counts = p.ws + 4;
     int32_t* offsets = counts + E;
@@ -1958,12 +1968,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
       p.ws[3] = 0;
       offsets[E] = off[E];
     }
-  }
-  {
-    int32_t* members = p.ws + 4 + 2 * E + 1;
-    const int waves = (int)gridDim.x * kWaves;
-    for (int e = (int)blockIdx.x * kWaves + w; e < E; e += waves)
-      if (cnt[e] > 0) ballot_members(sid, P, e, 0, cnt[e], members + off[e], lane);
   }
 }
 
