@@ -628,6 +628,42 @@ def test_padded_bucket_graph_replay_at_changing_live_counts():
         check_routed(w_live, img_o, [H.host(o) for o in outs], live)
 
 
+def skewed_ids(g, pattern, B, E, k):
+    """Routing ids concentrated on few experts (distinct within a row): every row on the same
+    k experts, or one expert in every row's first slot with the other slots from top-k."""
+    if pattern == "same_experts":
+        base = (np.arange(k, dtype=np.int32) * 37 + 3) % E
+        return np.stack([g.permutation(base) for _ in range(B)]).astype(np.int32)
+    ids, _ = W.topk_ids(g, B, E, k)
+    hot = 5
+    for r in range(B):
+        rest = [e for e in ids[r] if e != hot][: k - 1]
+        ids[r] = [hot] + rest
+    return ids.astype(np.int32)
+
+
+@pytest.mark.parametrize("pattern,live", [("same_experts", 512), ("same_experts", 201),
+                                          ("one_hot_expert", 512)])
+def test_routed_plan_skewed(pattern, live):
+    # skewed routing at the pair limit: up to 512 pairs of one expert, i.e. 64 segments of 8
+    # columns whose members are exported by as many workgroups; the plan must still list each
+    # expert's pairs in ascending order and every pair's outputs must match the oracle
+    g = np.random.default_rng(3 + live)
+    B, K, E, k = 512, 2048, 256, 8
+    x = g.standard_normal((B, K)).astype(np.float32)
+    gamma = g.normal(1.0, 0.1, K).astype(np.float32)
+    ids = skewed_ids(g, pattern, B, E, k)
+    w = np.full((B, k), 1.0 / k, np.float32)
+    wl = W.Workload(0, "skewed", B, K, "rmsnorm", x=x, gamma=gamma,
+                    readers=[W.q4_0_weights(g, (E, 24), K)], E=E, top_k=k, ids=ids, route_w=w, live=live)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl, live=live)
+    _, img_o = check_producer(wl, y, img, live=live)
+    outs, ws = run_routed(wl, H.dev(img), ids, live=live)
+    check_plan(ws, ids, live, E, k)
+    check_routed(wl, img_o, outs, live)
+
+
 @pytest.mark.parametrize("live", [512, 455])
 def test_routed_plan_at_the_pair_limit(live):
     # bucket 512 x top-8 = 4096 pairs (the largest plan one launch takes), far past the 1,024
