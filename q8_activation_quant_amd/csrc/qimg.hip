@@ -17,9 +17,9 @@
 //                            (v_mfma_i32_16x16x64_i8) over tiled weights, the live image rows as
 //                            columns; M = 2: block-dot export; M = 3, 4: Q8_0, Q4_1 weights.
 //   mmq_kernel               prefill reader for many image rows (v_mfma_i32_16x16x32_i8).
-//   mmvq_routed_kernel<N,U,P> routed readers: the plan of the live pairs built in LDS by every
-//                            workgroup, then (expert, pass, tile)
-//                            units streamed over full K.
+//   mmvq_routed_kernel<KU,S> routed readers: the plan of the live pairs built by every
+//                            workgroup (in LDS; S: at most 64 pairs, in registers by a wave-wide
+//                            sort), then (expert, pass, tile) units streamed in two K halves.
 //   moe_router_kernel, moe_topk_kernel, moe_combine_kernel: the rest of a routed MoE FFN.
 //   tile_weights_kernel<F>   one-time reordering of standard Q4_0 / Q8_0 / Q4_1 planes into
 //                            reader tiles.
@@ -1432,7 +1432,64 @@ __device__ __forceinline__ void ballot_members(const int32_t* sid, int P, int e,
   }
 }
 
-template <int KU>
+// The value of lane l ^ J (J a power of two up to 32): DPP within rows of 16 (xor 4 and 8 as
+// two mirrors each), permlane swaps across rows. A swap returns the lane's own value and its
+// partner's; the partner's is the one that differs (keys below are distinct across lanes).
+constexpr int kDppQuadRev = 0x1b;  // quad_perm [3,2,1,0]
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) {
+    return (uint32_t)dpp_n<kDppXor1>((int)v);
+  } else if constexpr (J == 2) {
+    return (uint32_t)dpp_n<kDppXor2>((int)v);
+  } else if constexpr (J == 4) {
+    return (uint32_t)dpp_n<kDppQuadRev>(dpp_n<kDppHalfMirror>((int)v));
+  } else if constexpr (J == 8) {
+    return (uint32_t)dpp_n<kDppHalfMirror>(dpp_n<kDppMirror>((int)v));
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return r[0] != v ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] != v ? r[0] : r[1];
+  }
+}
+// One compare-exchange of a bitonic sort network over the 64 lanes (block size K, distance J):
+// the lower lane of a pair keeps the smaller key in ascending blocks, the larger in descending.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(uint32_t& key, int lane) {
+  const uint32_t o = lane_xor<J>(key);
+  const bool keep_min = ((lane & J) == 0) == ((lane & K) == 0);
+  key = keep_min ? (key < o ? key : o) : (key > o ? key : o);
+}
+// Ascending sort of one distinct 32-bit key per lane over the wave.
+__device__ __forceinline__ uint32_t wave_sort64(uint32_t key, int lane) {
+  bitonic_step<2, 1>(key, lane);
+  bitonic_step<4, 2>(key, lane);
+  bitonic_step<4, 1>(key, lane);
+  bitonic_step<8, 4>(key, lane);
+  bitonic_step<8, 2>(key, lane);
+  bitonic_step<8, 1>(key, lane);
+  bitonic_step<16, 8>(key, lane);
+  bitonic_step<16, 4>(key, lane);
+  bitonic_step<16, 2>(key, lane);
+  bitonic_step<16, 1>(key, lane);
+  bitonic_step<32, 16>(key, lane);
+  bitonic_step<32, 8>(key, lane);
+  bitonic_step<32, 4>(key, lane);
+  bitonic_step<32, 2>(key, lane);
+  bitonic_step<32, 1>(key, lane);
+  bitonic_step<64, 32>(key, lane);
+  bitonic_step<64, 16>(key, lane);
+  bitonic_step<64, 8>(key, lane);
+  bitonic_step<64, 4>(key, lane);
+  bitonic_step<64, 2>(key, lane);
+  bitonic_step<64, 1>(key, lane);
+  return key;
+}
+
+template <int KU, bool SMALL>
 __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ __align__(16) int sh_wave[2][kWaves];  // per-wave totals of the plan scans
@@ -1455,83 +1512,113 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   int32_t* off = cnt + E;                                          // [E + 1] pair offsets
   int32_t* pps = off + E + 1;                                      // [E + 1] first segment
 
-  // ---- plan: per-expert counts, then offsets and segment starts ----
-  for (int e = tid; e < E; e += kWaves * 64) cnt[e] = 0;
-  if (tid < 8) {
+  // ---- plan ----
+  // A launch of at most 64 pairs (SMALL: bucket * top_k <= 64) keeps its plan in registers:
+  // every wave sorts the keys
+  // (expert << 6 | pair) of the live pairs across its lanes (lanes past P and ids out of range
+  // sort last), so the sorted order lists each expert's pairs in ascending pair order, and the
+  // segments (runs of up to TP pairs of one expert) follow from ballots over it: no LDS plan,
+  // atomic or barrier before the staging. Larger launches count per expert in LDS.
+  constexpr bool small = SMALL;
+  int s_e = 0, s_pair = 0, s_first = 0, s_seg = -1, s_count = 0, s_valid_n = 0;
+  bool s_valid = false, s_start = false, s_bad = false;
+  if (tid < 8) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;  // the 32-byte zero slot
+  if constexpr (small) {
+    const __amdgpu_buffer_rsrc_t rid =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.ids, (short)0, P * 4, kBufferFlags);
+    const int id = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, 4u * (uint32_t)lane, 0u, 0);
+    const bool ok = lane < P && (uint32_t)id < (uint32_t)E;
+    s_bad = __ballot(lane < P && !ok) != 0ull;
+    const uint32_t key = wave_sort64(((uint32_t)(ok ? id : 0xfffff) << 6) | (uint32_t)lane, lane);
+    s_e = (int)(key >> 6);
+    s_pair = (int)(key & 63u);
+    s_valid = s_e < E;
+    const int prev = __builtin_amdgcn_ds_bpermute(((lane + 63) & 63) << 2, s_e);
+    const uint64_t le = ~0ull >> (63 - lane);  // lanes 0 .. lane
+    const uint64_t chg = __ballot(s_valid && (lane == 0 || prev != s_e));
+    s_first = s_valid ? 63 - __builtin_clzll((chg & le) | 1ull) : lane;  // first lane of the expert
+    s_start = s_valid && ((lane - s_first) & (TP - 1)) == 0;
+    const uint64_t smask = __ballot(s_start);
+    s_count = __popcll(smask);  // segments
+    s_seg = __popcll(smask & le) - 1;
+    s_valid_n = __popcll(__ballot(s_valid));
+    // the plan's members (ascending by expert, then pair): one wave of the grid stores them
+    if (blockIdx.x == 0 && w == 0 && s_valid) p.ws[4 + 2 * E + 1 + lane] = s_pair;
+  } else {
+    for (int e = tid; e < E; e += kWaves * 64) cnt[e] = 0;
     if (tid < 4) sh_misc[tid] = 0;
-    reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;  // the 32-byte zero slot
-  }
-  // the ids of pairs tid + 512 j (P <= pairs_cap <= 8 * 512): buffer loads, which read 0 past
-  // the P live pairs' ids; all eight go out, so that their waits are exact
-  const __amdgpu_buffer_rsrc_t rid =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.ids, (short)0, P * 4, kBufferFlags);
-  int idv[8];
+    // the ids of pairs tid + 512 j (P <= pairs_cap <= 8 * 512): buffer loads, which read 0 past
+    // the P live pairs' ids; all eight go out, so that their waits are exact
+    const __amdgpu_buffer_rsrc_t rid =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.ids, (short)0, P * 4, kBufferFlags);
+    int idv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    idv[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, 4u * (uint32_t)(tid + 512 * j), 0u, 0);
-  __syncthreads();
-  {
-    const int nj = (Pp + 511) >> 9;
-    bool bad = false;
+    for (int j = 0; j < 8; ++j)
+      idv[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, 4u * (uint32_t)(tid + 512 * j), 0u, 0);
+    __syncthreads();
+    {
+      const int nj = (Pp + 511) >> 9;
+      bool bad = false;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < nj) {
-        const int pi = tid + 512 * j, id = idv[j];
-        const bool ok = pi < P && (uint32_t)id < (uint32_t)E;
-        bad |= pi < P && !ok;
-        if (pi < Pp) sid[pi] = ok ? id : -1;
-        if (ok) atomicAdd(&cnt[id], 1);
+      for (int j = 0; j < 8; ++j) {
+        if (j < nj) {
+          const int pi = tid + 512 * j, id = idv[j];
+          const bool ok = pi < P && (uint32_t)id < (uint32_t)E;
+          bad |= pi < P && !ok;
+          if (pi < Pp) sid[pi] = ok ? id : -1;
+          if (ok) atomicAdd(&cnt[id], 1);
+        }
       }
-    }
-    if (bad) sh_misc[0] = 1;
-  }
-  __syncthreads();
-  {  // thread t: experts t and t + 512 (E <= 1024)
-    const int ea = tid, eb = tid + kWaves * 64;
-    const int ca = ea < E ? cnt[ea] : 0, cb = eb < E ? cnt[eb] : 0;
-    // pairs in the low 16 bits, segments (passes of up to TP pairs) in the high 16: each total
-    // is at most the pair count (<= 4096), so no carry crosses
-    const int va = ca | (((ca + TP - 1) >> p.tp_log2) << 16);
-    const int vb = cb | (((cb + TP - 1) >> p.tp_log2) << 16);
-    const int ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
-    if (lane == 63) {
-      sh_wave[0][w] = ia;
-      sh_wave[1][w] = ib;
+      if (bad) sh_misc[0] = 1;
     }
     __syncthreads();
-    int xa = 0, xb = 0, ta = 0, tb = 0;
+    {  // thread t: experts t and t + 512 (E <= 1024)
+      const int ea = tid, eb = tid + kWaves * 64;
+      const int ca = ea < E ? cnt[ea] : 0, cb = eb < E ? cnt[eb] : 0;
+      // pairs in the low 16 bits, segments (passes of up to TP pairs) in the high 16: each total
+      // is at most the pair count (<= 4096), so no carry crosses
+      const int va = ca | (((ca + TP - 1) >> p.tp_log2) << 16);
+      const int vb = cb | (((cb + TP - 1) >> p.tp_log2) << 16);
+      const int ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
+      if (lane == 63) {
+        sh_wave[0][w] = ia;
+        sh_wave[1][w] = ib;
+      }
+      __syncthreads();
+      int xa = 0, xb = 0, ta = 0, tb = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      const int a = sh_wave[0][i], b = sh_wave[1][i];
-      xa += i < w ? a : 0;
-      xb += i < w ? b : 0;
-      ta += a;
-      tb += b;
+      for (int i = 0; i < kWaves; ++i) {
+        const int a = sh_wave[0][i], b = sh_wave[1][i];
+        xa += i < w ? a : 0;
+        xb += i < w ? b : 0;
+        ta += a;
+        tb += b;
+      }
+      const int pa = xa + ia - va, pb = ta + xb + ib - vb;  // before experts ea and eb
+      if (ea < E) {
+        off[ea] = pa & 0xffff;
+        pps[ea] = (int)((uint32_t)pa >> 16);
+      }
+      if (eb < E) {
+        off[eb] = pb & 0xffff;
+        pps[eb] = (int)((uint32_t)pb >> 16);
+      }
+      if (tid == 0) {
+        const uint32_t tot = (uint32_t)(ta + tb);
+        off[E] = (int)(tot & 0xffffu);
+        pps[E] = (int)(tot >> 16);
+        sh_misc[1] = (int)(tot >> 16);
+      }
     }
-    const int pa = xa + ia - va, pb = ta + xb + ib - vb;  // before experts ea and eb
-    if (ea < E) {
-      off[ea] = pa & 0xffff;
-      pps[ea] = (int)((uint32_t)pa >> 16);
-    }
-    if (eb < E) {
-      off[eb] = pb & 0xffff;
-      pps[eb] = (int)((uint32_t)pb >> 16);
-    }
-    if (tid == 0) {
-      const uint32_t tot = (uint32_t)(ta + tb);
-      off[E] = (int)(tot & 0xffffu);
-      pps[E] = (int)(tot >> 16);
-      sh_misc[1] = (int)(tot >> 16);
-    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- work ----
   // values read from LDS that are the same in every lane are made wave-uniform, so that the
   // reader descriptors they select are fetched with scalar loads
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
   // every segment holds T units (its tiles), so segment s covers units [s T, s T + T)
-  const int U = uni(sh_misc[1]) * T;
+  const int U = (small ? s_count : uni(sh_misc[1])) * T;
   const int G = gridDim.x;
   const int wr = xcd_rank(blockIdx.x, G);
   // [u0, u1) = [floor(U wr / G), floor(U (wr + 1) / G)) in 32-bit arithmetic (U = q G + r,
@@ -1548,35 +1635,64 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     const int s_lo = fdiv(ub, p.fd_tiles), s_last = fdiv(u1 - 1, p.fd_tiles);
     const int ns = s_last - s_lo + 1 < p.slots ? s_last - s_lo + 1 : p.slots;
     const int ue = (s_lo + ns) * T < u1 ? (s_lo + ns) * T : u1;
-    {  // the batch's segments, found by the threads of their experts
-      auto find = [&](int e) {
-        const int a0 = pps[e], a1 = pps[e + 1];
-        const int sa = a0 > s_lo ? a0 : s_lo, sb = a1 < s_lo + ns ? a1 : s_lo + ns;
-        for (int sg = sa; sg < sb; ++sg) {
-          const int k = sg - s_lo, pass = sg - a0;
-          const int left = cnt[e] - pass * TP;
-          sh_seg[k][0] = sg * T;
-          sh_seg[k][1] = e;
-          sh_seg[k][2] = left < TP ? left : TP;
-          sh_seg[k][3] = pass;
+    if constexpr (small) {
+      // the batch's segments and their members from the sorted keys: every wave writes the
+      // same values and reads back only what it wrote itself, so no barrier is needed
+#pragma unroll
+      for (int k = 0; k < kRoutedMaxSlots; ++k) {
+        if (k < ns) {
+          const uint64_t m = __ballot(s_start && s_seg == s_lo + k);
+          const int sk = (int)__builtin_ctzll(m | (1ull << 63));  // the segment's first lane
+          const int e = __builtin_amdgcn_readlane(s_e, sk);
+          const int pass = (sk - __builtin_amdgcn_readlane(s_first, sk)) >> p.tp_log2;
+          const int left = __popcll(__ballot(s_valid && s_e == e)) - pass * TP;
+          if (lane == 0) {
+            sh_seg[k][0] = (s_lo + k) * T;
+            sh_seg[k][1] = e;
+            sh_seg[k][2] = left < TP ? left : TP;
+            sh_seg[k][3] = pass;
+          }
+        } else if (lane == 0) {
+          sh_seg[k][0] = 0x7fffffff;
         }
-      };
-      if (tid < E) find(tid);
-      if (tid + kWaves * 64 < E) find(tid + kWaves * 64);
-      if (tid < kRoutedMaxSlots && tid >= ns) sh_seg[tid][0] = 0x7fffffff;
+      }
+      const int kk = s_seg - s_lo;
+      if (s_valid && kk >= 0 && kk < ns) {
+        const int c = (lane - s_first) & (TP - 1);
+        sh_mem[kk][c] = s_pair;
+        sh_row[kk][c] = s_pair / p.img_div;
+      }
+    } else {
+      {  // the batch's segments, found by the threads of their experts
+        auto find = [&](int e) {
+          const int a0 = pps[e], a1 = pps[e + 1];
+          const int sa = a0 > s_lo ? a0 : s_lo, sb = a1 < s_lo + ns ? a1 : s_lo + ns;
+          for (int sg = sa; sg < sb; ++sg) {
+            const int k = sg - s_lo, pass = sg - a0;
+            const int left = cnt[e] - pass * TP;
+            sh_seg[k][0] = sg * T;
+            sh_seg[k][1] = e;
+            sh_seg[k][2] = left < TP ? left : TP;
+            sh_seg[k][3] = pass;
+          }
+        };
+        if (tid < E) find(tid);
+        if (tid + kWaves * 64 < E) find(tid + kWaves * 64);
+        if (tid < kRoutedMaxSlots && tid >= ns) sh_seg[tid][0] = 0x7fffffff;
+      }
+      __syncthreads();
+      // members of the batch's segments (wave k: segment k) and their image rows
+      if (w < ns) {
+        const int e = uni(sh_seg[w][1]), nc = uni(sh_seg[w][2]), lo = uni(sh_seg[w][3]) * TP;
+        ballot_members(sid, P, e, lo, lo + nc, sh_mem[w], lane);
+        if (lane < nc) sh_row[w][lane] = sh_mem[w][lane] / p.img_div;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     const int seg0 = s_lo * T;
     auto seg_of = [&](int u) {  // segment index in the batch of unit u (u in [ub, ue))
       return (u >= seg0 + T ? 1 : 0) + (u >= seg0 + 2 * T ? 1 : 0) + (u >= seg0 + 3 * T ? 1 : 0);
     };
-    // members of the batch's segments (wave k: segment k) and their image rows
-    if (w < ns) {
-      const int e = uni(sh_seg[w][1]), nc = uni(sh_seg[w][2]), lo = uni(sh_seg[w][3]) * TP;
-      ballot_members(sid, P, e, lo, lo + nc, sh_mem[w], lane);
-      if (lane < nc) sh_row[w][lane] = sh_mem[w][lane] / p.img_div;
-    }
-    __syncthreads();
 
     // ---- this wave's work of the batch: the first loads go out with the staging ----
     // With p.halves == 2 every unit is cut at chunk H = p.khalf (a multiple of KU fixed by K)
@@ -1668,7 +1784,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
     // The plan's members of each segment whose first unit this workgroup holds (so every
     // segment is exported by exactly one workgroup), stored ahead of the staging copies: the
     // staging wait below then covers these stores as well, and no barrier waits for them.
-    if (w < ns) {
+    if (!small && w < ns) {
       const int st = uni(sh_seg[w][0]);
       if (st >= ub && st < ue) {
         const int e = uni(sh_seg[w][1]), nc = uni(sh_seg[w][2]), lo = uni(sh_seg[w][3]) * TP;
@@ -1957,16 +2073,38 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   if (blockIdx.x == 0) {
     int32_t* counts = p.ws + 4;
     int32_t* offsets = counts + E;
-    for (int e = tid; e < E; e += blockDim.x) {
-      counts[e] = cnt[e];
-      offsets[e] = off[e];
+    if constexpr (small) {
+      // lower bound of expert e in the sorted keys: a binary search over the lanes (every lane
+      // searches, so that every source lane of the permutes is active)
+      auto lb = [&](int e) {
+        int lo = 0;
+#pragma unroll
+        for (int st = 32; st > 0; st >>= 1)
+          if (__builtin_amdgcn_ds_bpermute((lo + st - 1) << 2, s_e) < e) lo += st;
+        return __builtin_amdgcn_ds_bpermute(lo << 2, s_e) < e ? lo + 1 : lo;
+      };
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e = tid + kWaves * 64 * i, ec = e < E ? e : E;
+        const int a = lb(ec), b = lb(ec + 1);
+        if (e < E) {
+          counts[e] = b - a;
+          offsets[e] = a;
+        }
+      }
+    } else {
+      for (int e = tid; e < E; e += blockDim.x) {
+        counts[e] = cnt[e];
+        offsets[e] = off[e];
+      }
     }
     if (tid == 0) {
-      p.ws[0] = (sh_misc[0] ? QIMG_ERR_EXPERT_RANGE : 0) | (clamped ? QIMG_ERR_LIVE_CLAMPED : 0);
+      const bool bad = small ? s_bad : sh_misc[0] != 0;
+      p.ws[0] = (bad ? QIMG_ERR_EXPERT_RANGE : 0) | (clamped ? QIMG_ERR_LIVE_CLAMPED : 0);
       p.ws[1] = P;
       p.ws[2] = 0;
       p.ws[3] = 0;
-      offsets[E] = off[E];
+      offsets[E] = small ? s_valid_n : off[E];
     }
   }
 }
@@ -2257,7 +2395,9 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   for (int i = 0; i < a.n_readers; ++i)
     if ((int64_t)a.E * a.r[i].tiles * a.KC * 1024 > 0x7fffffff) return QIMG_EUNSUPPORTED;
   for (int i = a.n_readers + 1; i <= QIMG_MAX_READERS; ++i) a.tile_start[i] = 0x7fffffff;
-  const int plan = 4 * (((pairs_cap + 255) & ~255) + 3 * a.E + 2);
+  // a launch of at most 64 pairs keeps its plan in registers (no LDS plan arrays)
+  const bool small = pairs_cap <= 64;
+  const int plan = small ? 0 : 4 * (((pairs_cap + 255) & ~255) + 3 * a.E + 2);
   const int nb = 4 * a.KC;
   // the widest column pass that leaves room for two staged segments, else for one
   int lds = -1;
@@ -2291,11 +2431,15 @@ int run_routed(ReadArgs& a, int pairs_cap, hipStream_t s) {
   const int G = cu_count();
   a.fd_grid = fast_div((uint32_t)G);
   a.fd_tiles = fast_div((uint32_t)tiles);
-  const void* fn = (const void*)mmvq_routed_kernel<kRoutedKu>;
+  const void* fn = small ? (const void*)mmvq_routed_kernel<kRoutedKu, true>
+                         : (const void*)mmvq_routed_kernel<kRoutedKu, false>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return QIMG_EHIP;
-  hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedKu>), dim3(G), dim3(kWaves * 64), lds, s, a);
+  if (small)
+    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedKu, true>), dim3(G), dim3(kWaves * 64), lds, s, a);
+  else
+    hipLaunchKernelGGL((mmvq_routed_kernel<kRoutedKu, false>), dim3(G), dim3(kWaves * 64), lds, s, a);
   return launch_status();
 }
 
