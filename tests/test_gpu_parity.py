@@ -523,6 +523,22 @@ def test_routed_single_expert_and_all_pairs_bad():
         assert (out.view(np.uint8) == H.SENTINEL_BYTE).all()
 
 
+@pytest.mark.parametrize("live", [0, 1, 3])
+def test_routed_register_plan_partial_bucket(live):
+    # a bucket of 8 rows x top-8 (64 pairs: the launch keeps its plan in registers) with only
+    # `live` rows live: padding rows' ids are never planned and their outputs stay unwritten
+    wl = W.make(4, small=True)
+    attach_dev_weights(wl)
+    y, img = run_producer(wl, live=live)
+    _, img_o = check_producer(wl, y, img, live=live)
+    outs, ws = run_routed(wl, H.dev(img), wl.ids, live=live)
+    check_plan(ws, wl.ids, live, wl.E, wl.top_k)
+    if live:
+        check_routed(wl, img_o, outs, live)
+    for out in outs:
+        assert (out[live:].view(np.uint8) == H.SENTINEL_BYTE).all()
+
+
 @pytest.mark.parametrize("K", [128, 1024, 1536, 2560])
 def test_routed_k_halves_and_one_row_runs(K):
     # K 128: units whole (one chunk); 1024, 1536, 2560: cut into two K halves (4 + 4, 6 + 6,
