@@ -242,7 +242,8 @@ size_t mmvq_id_workspace_bytes(int32_t bucket, int32_t top_k, int32_t E);
  * work and no writes; launches stay sized for the bucket and read the live count at run time).
  * For every live pair p = row*top_k + slot (row < live, e = ids[p] in [0, E)):
  *   out_r[p][n] = the ordinary reader formula with expert e's weights and image row `row`.
- *   ids       : device int32 [bucket][top_k]; entries of padding rows are never read
+ *   ids       : device int32 [bucket][top_k] (the whole buffer may be read); entries of padding
+ *               rows are never used
  *   live_rows : device int32 (clamped to [0, bucket]), or NULL for all bucket rows
  *   img       : image with `bucket` rows
  *   workspace : device, >= mmvq_id_workspace_bytes(bucket, top_k, E), 16-byte aligned.

@@ -1371,7 +1371,7 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
 // Routed readers (MUL_MAT_ID).
 //
 // Plan ([P3] What this changes: only the live rows' pairs are planned; padding ids are never
-// read). Every workgroup reads the live pairs' expert ids into LDS and counts them per expert
+// used). Every workgroup reads the live pairs' expert ids into LDS and counts them per expert
 // (LDS atomics); one scan gives each expert's pair offset and the first of its work units. The
 // members of an expert in ascending pair order come from a scan of the ids with wave ballots
 // (no sort): a wave walks the ids 64 at a time and places each match at its rank. The plan is
@@ -1501,6 +1501,17 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int n = lane & 15, g = lane >> 4;
   const int E = p.E, T = p.tiles_total, TP = p.tp, KC = p.KC;
+  // The ids are read over the whole bucket (its buffer holds bucket x top_k entries) and before
+  // the live count, so that their loads do not wait for it; entries of padding rows are masked
+  // off below and never used. Buffer loads read 0 past the bucket's pairs; every load goes out,
+  // so that the waits for them are exact. SMALL: pair lane of each wave; otherwise pairs
+  // tid + 512 j (pairs_cap <= 8 * 512).
+  const __amdgpu_buffer_rsrc_t rid =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.ids, (short)0, p.pairs_cap * 4, kBufferFlags);
+  int idv[SMALL ? 1 : 8];
+#pragma unroll
+  for (int j = 0; j < (SMALL ? 1 : 8); ++j)
+    idv[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, 4u * (uint32_t)((SMALL ? lane : tid) + 512 * j), 0u, 0);
   int clamped = 0;
   const int live = clamp_live(p.live_rows, p.rows, &clamped);
   const int P = live * p.top_k;     // <= rows * top_k = pairs_cap
@@ -1524,9 +1535,7 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   bool s_valid = false, s_start = false, s_bad = false;
   if (tid < 8) reinterpret_cast<uint32_t*>(smem + p.lds_zero)[tid] = 0u;  // the 32-byte zero slot
   if constexpr (small) {
-    const __amdgpu_buffer_rsrc_t rid =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.ids, (short)0, P * 4, kBufferFlags);
-    const int id = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, 4u * (uint32_t)lane, 0u, 0);
+    const int id = idv[0];
     const bool ok = lane < P && (uint32_t)id < (uint32_t)E;
     s_bad = __ballot(lane < P && !ok) != 0ull;
     const uint32_t key = wave_sort64(((uint32_t)(ok ? id : 0xfffff) << 6) | (uint32_t)lane, lane);
@@ -1547,14 +1556,6 @@ __global__ __launch_bounds__(kWaves * 64) void mmvq_routed_kernel(ReadArgs p) {
   } else {
     for (int e = tid; e < E; e += kWaves * 64) cnt[e] = 0;
     if (tid < 4) sh_misc[tid] = 0;
-    // the ids of pairs tid + 512 j (P <= pairs_cap <= 8 * 512): buffer loads, which read 0 past
-    // the P live pairs' ids; all eight go out, so that their waits are exact
-    const __amdgpu_buffer_rsrc_t rid =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.ids, (short)0, P * 4, kBufferFlags);
-    int idv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      idv[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, 4u * (uint32_t)(tid + 512 * j), 0u, 0);
     __syncthreads();
     {
       const int nj = (Pp + 511) >> 9;
