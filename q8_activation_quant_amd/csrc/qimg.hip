@@ -1205,16 +1205,16 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 // A workgroup computes 64 weight rows (4 waves, one 16-row tile each) x 64 image rows (4
 // sub-tiles of 16). Product orientation: A = weights (M = the wave's 16 rows), B = image codes
 // (N = 16 image rows), D[row 4g + v][image row] in lane (image row, g). K order inside a block:
-// lane group g takes nibble bytes 4g..4g+3 of a weight block (elements 4g..4g+3 in the low
-// nibbles, 16+4g..16+4g+3 in the high ones) and the image codes of the same elements, so the
-// reader tiles made for the mat-vec readers serve as they are: a wave regroups its 16 bytes per
-// lane through LDS (lane (row, b) holds block b; lane (row, g) needs bytes 4g..4g+3 of each).
-// Per 4-block chunk: the 64 image rows x 4 blocks are staged in LDS (double buffered, the next
-// chunk's loads in flight during the products), then 16 products and the scaling
-// acc += d_w (d_a sumi - 8 s_a) per block. Image rows past the live count, rows past N and
-// blocks past K/32 contribute nothing and are not stored. Every LDS operand is laid out so that
-// lane l reads at 4 l or 8 l bytes of a 256- or 512-byte run (no bank conflicts), and the f16
-// operand slots that must be zero are read from words that stay zero instead of being masked.
+// k group g takes elements 8g..8g+7, i.e. image bytes 8g..8g+7 and the nibbles of weight bytes
+// 8(g & 1)..8(g & 1)+7 (the low nibbles for g < 2, the high ones for g >= 2: byte i of a Q4_0
+// block holds elements i and i + 16), so the reader tiles made for the mat-vec readers serve as
+// they are. Per 4-block chunk the image rows' codes and each wave's weight codes are copied into
+// LDS by direct global-to-LDS copies (double buffered: the next chunk's copies are in flight
+// during the products) and the scale words go through registers; then per block 4 products and
+// the scaling acc += d_w (d_a sumi - 8 s_a). Image rows past the live count, rows past N and
+// blocks past K/32 contribute nothing and are not stored. Every LDS operand read falls on
+// distinct banks (an image row's 16-byte pieces are stored in an order permuted by the row),
+// and the f16 operand slots that must be zero are read from words that stay zero.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMmqWaves = 4;
 constexpr int kMmqMinRows = 64;  // Q4_0 readers of this many image rows or more use this kernel
@@ -1226,17 +1226,17 @@ typedef long v1l;
 // core. Each (image row, weight row, block) then costs a convert and one fma:
 //   acc += (d_w d_a) sumi;     out = acc - 8 sum_b d_w s_a.
 __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
-  // image codes [buf][block][sub-tile j][k group g][image row n of the sub-tile][2 dwords]: lane
-  // (n, g) = n + 16 g reads its two dwords (bytes 4g..4g+3 and 16+4g..16+4g+3 of image row
-  // 16 j + n) at byte 8 lane of the sub-tile's 512, so a read covers consecutive banks
-  __shared__ __align__(16) uint2 s_codes[2][4][4][4][16];
+  // image codes of a chunk, [buf][row][8 pieces of 16 bytes]: piece P of local row r sits at
+  // position P ^ ((r >> 1) & 7), so that the product operand reads (8 bytes per lane: row
+  // 16 j + n, bytes 8 g .. 8 g + 7 of a block) fall on distinct banks
+  __shared__ __align__(16) uint8_t s_img[2][64 * 128];
   // d_a[4 blocks] | s_a[4 blocks] per image row; row 64 stays zero and is what the lanes of k
   // groups 1..3 read (their f16 operand slots must be zero)
   __shared__ __align__(16) uint16_t s_das[2][65][8];
-  __shared__ __align__(16) uint32_t s_wq[kMmqWaves][4][64];  // regrouped weight codes [block][lane]
-  // weight-side f16 operands, zero outside the lanes of k group 0: per block b the word with
-  // d_w[row][b] in slot b, and the word with the 4 blocks' d_w
-  __shared__ __align__(16) uint64_t s_wdb[kMmqWaves][4][64];
+  // the wave's weight codes of a chunk in their tiled order ([lane (row, block)][16 bytes]),
+  // double buffered
+  __shared__ __align__(16) uint32_t s_wt[kMmqWaves][2][256];
+  // weight-side f16 operand: per lane of k group 0 (row n) the 4 blocks' d_w, zero elsewhere
   __shared__ __align__(16) uint64_t s_wd4[kMmqWaves][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1257,47 +1257,47 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
 
   // the zero words: each wave its own scale operands, thread 0 the zero rows of both buffers
   {
-    uint4* z = reinterpret_cast<uint4*>(&s_wdb[w][0][0]);
-    z[lane] = make_uint4(0, 0, 0, 0);
-    z[lane + 64] = make_uint4(0, 0, 0, 0);
     s_wd4[w][lane] = 0ull;
     if (tid < 2) *reinterpret_cast<uint4*>(&s_das[tid][64][0]) = make_uint4(0, 0, 0, 0);
   }
 
-  // staging of one chunk: thread tid -> image row c0 + (tid & 63), block 4 s + (tid >> 6)
-  const int sr = tid & 63, sb = tid >> 6;
-  uint4 ic0, ic1;
+  // Staging of one chunk. The image codes and the weight codes go by direct global-to-LDS
+  // copies: wave w copies local image rows 16 w + 8 i + (lane >> 3), i < 2 (lane position
+  // lane & 7 of its row gets piece (lane & 7) ^ f), and its own weight tile's 1 KB of codes in
+  // their tiled order. The scale words go through registers: thread (row sr, block sb) loads
+  // its row's d_a | s_a word, each lane its weight row's d_w. Image rows past the live count
+  // copy the last live row and blocks past K/32 the row's last block (finite scales; the weight
+  // tiles hold d_w = 0 there, and the outputs of those image rows are not stored).
+  const uint8_t* csrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int lr = 16 * w + 8 * i + (lane >> 3);
+    const int row = c0 + lr < live ? c0 + lr : live - 1;
+    csrc[i] = p.codes + ((size_t)row * p.RB) * 32 + 16 * ((lane & 7) ^ ((lr >> 1) & 7));
+  }
+  const int sr = tid >> 2, sb = tid & 3;
+  const int srow = c0 + sr < live ? c0 + sr : live - 1;
   uint32_t idw;
-  uint4 wv;
   uint16_t wdv;
-  auto load_chunk = [&](int s) {
-    const int row = c0 + sr, blk = 4 * s + sb;
-    const bool ok = row < live && blk < p.Kb;
-    const uint32_t off = ok ? (uint32_t)(row * p.RB + blk) : 0u;
-    const uint4* src = reinterpret_cast<const uint4*>(p.codes + (size_t)off * 32);
-    ic0 = src[0];
-    ic1 = src[1];
-    idw = p.ds[off];
-    if (!ok) {
-      ic0 = ic1 = make_uint4(0, 0, 0, 0);
-      idw = 0u;
-    }
-    wv = *reinterpret_cast<const uint4*>(wq + (int64_t)s * 1024);
+  auto load_scales = [&](int s) {
+    const int blk = 4 * s + sb < p.Kb ? 4 * s + sb : p.Kb - 1;
+    idw = p.ds[(size_t)srow * p.RB + blk];
     wdv = wdp[(int64_t)s * 64];
   };
-  auto store_chunk = [&](int buf) {
-    s_codes[buf][sb][sr >> 4][0][sr & 15] = make_uint2(ic0.x, ic1.x);
-    s_codes[buf][sb][sr >> 4][1][sr & 15] = make_uint2(ic0.y, ic1.y);
-    s_codes[buf][sb][sr >> 4][2][sr & 15] = make_uint2(ic0.z, ic1.z);
-    s_codes[buf][sb][sr >> 4][3][sr & 15] = make_uint2(ic0.w, ic1.w);
+  auto copy_chunk = [&](int s, int buf) {
+    dma_b128(csrc[0] + (size_t)s * 128, lds_addr(&s_img[buf][(16 * w) * 128]));
+    dma_b128(csrc[1] + (size_t)s * 128, lds_addr(&s_img[buf][(16 * w + 8) * 128]));
+    dma_b128(wq + (int64_t)s * 1024, lds_addr(&s_wt[w][buf][0]));
+  };
+  // Product operands. K order of a block: lane k group g takes elements 8 g .. 8 g + 7, i.e.
+  // image bytes 8 g .. 8 g + 7 and the weight nibbles of bytes 8 (g & 1) .. 8 (g & 1) + 7, low
+  // nibbles for g < 2 and high ones for g >= 2 (byte i of a Q4_0 block holds elements i and
+  // i + 16). This lane's image operand of block b, sub-tile j: a_img ^ (32 b), plus 2048 j.
+  const uint32_t a_img = n * 128 + 16 * (((n >> 1) & 7) ^ (g >> 1)) + 8 * (g & 1);
+  const int wsh = 4 * (g >> 1);
+  auto store_scales = [&](int buf) {
     s_das[buf][sr][sb] = (uint16_t)(idw & 0xffffu);
     s_das[buf][sr][4 + sb] = (uint16_t)(idw >> 16);
-    // lane (row n, block g) holds bytes 0..15 of block g: dword k goes to lane (n, k), slot g
-    s_wq[w][g][n + 16 * 0] = wv.x;
-    s_wq[w][g][n + 16 * 1] = wv.y;
-    s_wq[w][g][n + 16 * 2] = wv.z;
-    s_wq[w][g][n + 16 * 3] = wv.w;
-    reinterpret_cast<uint16_t*>(&s_wdb[w][g][n])[g] = wdv;
     reinterpret_cast<uint16_t*>(&s_wd4[w][n])[g] = wdv;
   };
   float acc[4][4];
@@ -1311,12 +1311,19 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
   // the scale rows this lane reads: its image rows in k group 0, the zero row elsewhere
   const int das_row = g == 0 ? n : 64, das_step = g == 0 ? 16 : 0;
 
-  load_chunk(0);
-  store_chunk(0);
+  // the scale loads go out before the copies; one wait covers both (the copies are not
+  // counted by the compiler)
+  load_scales(0);
+  copy_chunk(0, 0);
+  wait_vmcnt<0>();
+  store_scales(0);
   __syncthreads();
   for (int s = 0; s < KC; ++s) {
     const int buf = s & 1;
-    if (s + 1 < KC) load_chunk(s + 1);
+    if (s + 1 < KC) {
+      load_scales(s + 1);
+      copy_chunk(s + 1, buf ^ 1);
+    }
     const uint64_t dwv = s_wd4[w][lane];
     uint64_t dav[4];
 #pragma unroll
@@ -1325,20 +1332,26 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
       dav[j] = ds4[0];
       sacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_v4h(dwv), as_v4h(ds4[1]), sacc[j], 0, 0, 0);
     }
-    // one block per loop step: unrolled, the compiler hoists every block's products (206
-    // registers instead of 116: two waves per SIMD instead of four)
-#pragma unroll 1
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t wbb = s_wq[w][b][lane];
-      const uint32_t lo = wbb & 0x0f0f0f0fu, hi = (wbb >> 4) & 0x0f0f0f0fu;
+    // the LDS operands of block b are read one block ahead (two operand sets, ping-pong); the
+    // products and scaling of each block stay in a scheduling region of their own
+    struct Ops { uint2 wb; uint2 cc[4]; };
+    auto ops = [&](int b, Ops& o) {
+      o.wb = *reinterpret_cast<const uint2*>(&s_wt[w][buf][(16 * b + n) * 4 + 2 * (g & 1)]);
+      const uint32_t ab = a_img ^ (32u * b);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o.cc[j] = *reinterpret_cast<const uint2*>(&s_img[buf][ab + 2048 * j]);
+    };
+    // the weight-side f16 operand of block b's d_w d_a product: the chunk's d_w word with the
+    // other blocks' slots cleared (zero outside the lanes of k group 0, as that word is)
+    auto block = [&](const Ops& o, int b) {
+      const uint64_t dwb = dwv & (0xffffull << (16 * b));
+      const uint32_t lo = (o.wb.x >> wsh) & 0x0f0f0f0fu, hi = (o.wb.y >> wsh) & 0x0f0f0f0fu;
       const v1l a = (v1l)(((uint64_t)hi << 32) | lo);
-      const uint64_t dwb = s_wdb[w][b][lane];
       v4i dd[4];
       v4f dwda[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint2 cc = s_codes[buf][b][j][g][n];
-        const v1l bb = (v1l)(((uint64_t)cc.y << 32) | cc.x);
+        const v1l bb = (v1l)(((uint64_t)o.cc[j].y << 32) | o.cc[j].x);
         const v4i zero = {0, 0, 0, 0};
         const v4f fzero = {0.0f, 0.0f, 0.0f, 0.0f};
         dd[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bb, zero, 0, 0, 0);
@@ -1348,8 +1361,27 @@ __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[j][v] = __builtin_fmaf(dwda[j][v], (float)dd[j][v], acc[j][v]);
+      // the block's scaling is done here (not sunk below the next blocks' products)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        asm volatile("" : "+v"(acc[j][0]), "+v"(acc[j][1]), "+v"(acc[j][2]), "+v"(acc[j][3]));
+    };
+    Ops oa, ob;
+    ops(0, oa);
+    ops(1, ob);
+    block(oa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    ops(2, oa);
+    block(ob, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    ops(3, ob);
+    block(oa, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    block(ob, 3);
+    if (s + 1 < KC) {
+      wait_vmcnt<0>();
+      store_scales(buf ^ 1);
     }
-    if (s + 1 < KC) store_chunk(buf ^ 1);
     __syncthreads();
   }
   if (!has) return;
