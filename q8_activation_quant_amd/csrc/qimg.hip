@@ -16,7 +16,7 @@
 //   mmvq_tiled_kernel<N,M,G> ordinary Q4_0 x Q8_1 readers on the matrix cores
 //                            (v_mfma_i32_16x16x64_i8) over tiled weights, the live image rows as
 //                            columns; M = 2: block-dot export; M = 3, 4: Q8_0, Q4_1 weights.
-//   mmq_kernel               prefill reader for many image rows (v_mfma_i32_16x16x32_i8).
+//   mmq_kernel               prefill reader for many image rows (v_mfma_i32_32x32x32_i8).
 //   mmvq_routed_kernel<KU,S> routed readers: the plan of the live pairs built by every
 //                            workgroup (in LDS; S: at most 64 pairs, in registers by a wave-wide
 //                            sort), then (expert, pass, tile) units streamed in two K halves.
@@ -1197,205 +1197,182 @@ __global__ __launch_bounds__(kOrdWaves * 64) void mmvq_tiled_kernel(ReadArgs p) 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill readers (many image rows: a prompt's tokens): Q4_0 x Q8_1 on v_mfma_i32_16x16x32_i8,
+// Prefill readers (many image rows: a prompt's tokens): Q4_0 x Q8_1 on v_mfma_i32_32x32x32_i8,
 // one 32-value block per product, so every block's int32 dot gets its own scales
 // ("r49 - A-quantize prepass shared-A dedup", section 2 Principle: the activation is
 // quantized once and every projection that reads it shares that one image).
 //
-// A workgroup computes 64 weight rows (4 waves, one 16-row tile each) x 64 image rows (4
-// sub-tiles of 16). Product orientation: A = weights (M = the wave's 16 rows), B = image codes
-// (N = 16 image rows), D[row 4g + v][image row] in lane (image row, g). K order inside a block:
-// k group g takes elements 8g..8g+7, i.e. image bytes 8g..8g+7 and the nibbles of weight bytes
-// 8(g & 1)..8(g & 1)+7 (the low nibbles for g < 2, the high ones for g >= 2: byte i of a Q4_0
-// block holds elements i and i + 16), so the reader tiles made for the mat-vec readers serve as
-// they are. Per 4-block chunk the image rows' codes and each wave's weight codes are copied into
-// LDS by direct global-to-LDS copies (double buffered: the next chunk's copies are in flight
-// during the products) and the scale words go through registers; then per block 4 products and
-// the scaling acc += d_w (d_a sumi - 8 s_a). Image rows past the live count, rows past N and
-// blocks past K/32 contribute nothing and are not stored. Every LDS operand read falls on
-// distinct banks (an image row's 16-byte pieces are stored in an order permuted by the row),
-// and the f16 operand slots that must be zero are read from words that stay zero.
+// A workgroup computes 64 weight rows (4 tiles of 16) x 64 image rows with 4 waves, each 32
+// weight rows x 32 image rows. Product orientation: A = weights (32 rows), B = image codes (32
+// image rows). Per 4-block chunk the image rows' codes and scale words and the weight tiles'
+// codes and scales are copied into LDS by direct global-to-LDS copies (double buffered: the next
+// chunk's copies are in flight during the products), so nothing is staged through registers;
+// then per block one product and the scaling acc += d_w (d_a sumi - 8 s_a). Image rows past
+// the live count, rows past N and blocks past K/32 contribute nothing and are not stored. Every
+// LDS operand read is 16 bytes per lane and falls on distinct banks (an image row's 16-byte
+// pieces are stored in an order permuted by the row), and the reader tiles made for the mat-vec
+// readers serve as they are.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMmqWaves = 4;
 constexpr int kMmqMinRows = 64;  // Q4_0 readers of this many image rows or more use this kernel
 typedef long v1l;
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // The scales go through f16 products (exact in f32): per block the outer product
-// d_w[row] d_a[image row] (k slot b of an f16 product whose other slots are zero), and per
-// chunk the sums over its 4 blocks of d_w s_a (k slots 0..3), accumulated over K by the matrix
-// core. Each (image row, weight row, block) then costs a convert and one fma:
+// d_w[row] d_a[image row] (one non-zero k slot on the weight side), and per chunk the sums over
+// its 4 blocks of d_w s_a, accumulated over K by the matrix core. Each (image row, weight row,
+// block) then costs a convert and one fma:
 //   acc += (d_w d_a) sumi;     out = acc - 8 sum_b d_w s_a.
 __global__ __launch_bounds__(kMmqWaves * 64, 2) void mmq_kernel(ReadArgs p) {
-  // image codes of a chunk, [buf][row][8 pieces of 16 bytes]: piece P of local row r sits at
-  // position P ^ ((r >> 1) & 7), so that the product operand reads (8 bytes per lane: row
-  // 16 j + n, bytes 8 g .. 8 g + 7 of a block) fall on distinct banks
+  // A chunk's operands are copied into LDS by direct global-to-LDS copies, double buffered (the
+  // next chunk's copies are in flight while a chunk is computed). Image codes, [buf][row][8
+  // pieces of 16 bytes]: piece P of local row r sits at position P ^ (r & 7), so that the product
+  // operand reads (16 bytes per lane, 8 lanes per bank cycle: 8 consecutive rows, one piece
+  // each) fall on distinct banks.
   __shared__ __align__(16) uint8_t s_img[2][64 * 128];
-  // d_a[4 blocks] | s_a[4 blocks] per image row; row 64 stays zero and is what the lanes of k
-  // groups 1..3 read (their f16 operand slots must be zero)
-  __shared__ __align__(16) uint16_t s_das[2][65][8];
-  // the wave's weight codes of a chunk in their tiled order ([lane (row, block)][16 bytes]),
-  // double buffered
+  // image scale words d_a | s_a << 16, [buf][row][block]
+  __shared__ __align__(16) uint32_t s_isc[2][64][4];
+  // the workgroup's 4 weight tiles of a chunk: codes in their tiled order ([lane (row, block)]
+  // [16 bytes]) and scales d_w [block][row]
   __shared__ __align__(16) uint32_t s_wt[kMmqWaves][2][256];
-  // weight-side f16 operand: per lane of k group 0 (row n) the 4 blocks' d_w, zero elsewhere
-  __shared__ __align__(16) uint64_t s_wd4[kMmqWaves][64];
+  __shared__ __align__(16) uint16_t s_wsc[kMmqWaves][2][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
   const int live = clamp_live(p.live_rows, p.rows, nullptr);
   const int c0 = blockIdx.y * 64;
   if (c0 >= live) return;  // whole workgroup
   const int KC = p.KC;
-  // this wave's weight tile (tiles past the end repeat the last one; nothing is stored)
-  const int tile_raw = blockIdx.x * kMmqWaves + w;
-  const bool has = tile_raw < p.tiles_total;
-  const int tile = has ? tile_raw : p.tiles_total - 1;
-  int ri = 0;
-  while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
-  const int lt = tile - p.tile_start[ri];
-  const uint8_t* wq = p.r[ri].qs + ((int64_t)lt * KC * 64 + lane) * 16;
-  const uint16_t* wdp = p.r[ri].d + (int64_t)lt * KC * 64 + lane;
+  // weight tile t of the workgroup is tile 4 blockIdx.x + t (tiles past the end repeat the last
+  // one; nothing is stored for them); wave w copies tile w, and computes weight rows
+  // 32 (w >> 1) .. + 31 (tiles 2 (w >> 1) and 2 (w >> 1) + 1) x image rows 32 (w & 1) .. + 31
+  auto tile_of = [&](int t, int& ri, int& lt) {
+    const int tr = blockIdx.x * kMmqWaves + t;
+    const int tile = tr < p.tiles_total ? tr : p.tiles_total - 1;
+    ri = 0;
+    while (ri + 1 < p.n_readers && tile >= p.tile_start[ri + 1]) ++ri;
+    lt = tile - p.tile_start[ri];
+    return tr < p.tiles_total;
+  };
+  int cri, clt;
+  tile_of(w, cri, clt);
+  const uint8_t* wq = p.r[cri].qs + ((int64_t)clt * KC * 64 + lane) * 16;
+  const uint8_t* wdp = reinterpret_cast<const uint8_t*>(p.r[cri].d + (int64_t)clt * KC * 64) + 4 * (lane & 31);
 
-  // the zero words: each wave its own scale operands, thread 0 the zero rows of both buffers
-  {
-    s_wd4[w][lane] = 0ull;
-    if (tid < 2) *reinterpret_cast<uint4*>(&s_das[tid][64][0]) = make_uint4(0, 0, 0, 0);
-  }
-
-  // Staging of one chunk. The image codes and the weight codes go by direct global-to-LDS
-  // copies: wave w copies local image rows 16 w + 8 i + (lane >> 3), i < 2 (lane position
-  // lane & 7 of its row gets piece (lane & 7) ^ f), and its own weight tile's 1 KB of codes in
-  // their tiled order. The scale words go through registers: thread (row sr, block sb) loads
-  // its row's d_a | s_a word, each lane its weight row's d_w. Image rows past the live count
-  // copy the last live row and blocks past K/32 the row's last block (finite scales; the weight
-  // tiles hold d_w = 0 there, and the outputs of those image rows are not stored).
+  // The copies of one chunk, 5 per wave: local image rows 16 w + 8 i + (lane >> 3), i < 2 (lane
+  // position lane & 7 of its row gets piece (lane & 7) ^ (lane >> 3)); the scale words of local
+  // image rows 16 w + (lane >> 2), block lane & 3; weight tile w's codes (1 KB) and scales (128
+  // bytes, lanes < 32). Image rows past the live count copy the last live row and blocks past
+  // K/32 the row's last block (finite scales; the weight tiles hold d_w = 0 there, and the
+  // outputs of those image rows are not stored).
   const uint8_t* csrc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int lr = 16 * w + 8 * i + (lane >> 3);
     const int row = c0 + lr < live ? c0 + lr : live - 1;
-    csrc[i] = p.codes + ((size_t)row * p.RB) * 32 + 16 * ((lane & 7) ^ ((lr >> 1) & 7));
+    csrc[i] = p.codes + ((size_t)row * p.RB) * 32 + 16 * ((lane & 7) ^ (lr & 7));
   }
-  const int sr = tid >> 2, sb = tid & 3;
-  const int srow = c0 + sr < live ? c0 + sr : live - 1;
-  uint32_t idw;
-  uint16_t wdv;
-  auto load_scales = [&](int s) {
-    const int blk = 4 * s + sb < p.Kb ? 4 * s + sb : p.Kb - 1;
-    idw = p.ds[(size_t)srow * p.RB + blk];
-    wdv = wdp[(int64_t)s * 64];
+  const int srow = c0 + 16 * w + (lane >> 2) < live ? c0 + 16 * w + (lane >> 2) : live - 1;
+  const uint32_t* ssrc = p.ds + (size_t)srow * p.RB;
+  // LDS byte addresses (wave-uniform) of this wave's copy destinations in buffer 0
+  const uint32_t l_img = lds_addr(&s_img[0][(16 * w) * 128]), l_isc = lds_addr(&s_isc[0][16 * w][0]);
+  const uint32_t l_wt = lds_addr(&s_wt[w][0][0]), l_wsc = lds_addr(&s_wsc[w][0][0]);
+  auto copy_chunk = [&](int s, int q) {
+    dma_b128(csrc[0] + (size_t)s * 128, l_img + q * (64 * 128));
+    dma_b128(csrc[1] + (size_t)s * 128, l_img + q * (64 * 128) + 1024);
+    const int blk = 4 * s + (lane & 3) < p.Kb ? 4 * s + (lane & 3) : p.Kb - 1;
+    dma_b32(ssrc + blk, l_isc + q * (64 * 16));
+    dma_b128(wq + (int64_t)s * 1024, l_wt + q * 1024);
+    if (lane < 32) dma_b32(wdp + (int64_t)s * 128, l_wsc + q * 128);
   };
-  auto copy_chunk = [&](int s, int buf) {
-    dma_b128(csrc[0] + (size_t)s * 128, lds_addr(&s_img[buf][(16 * w) * 128]));
-    dma_b128(csrc[1] + (size_t)s * 128, lds_addr(&s_img[buf][(16 * w + 8) * 128]));
-    dma_b128(wq + (int64_t)s * 1024, lds_addr(&s_wt[w][buf][0]));
-  };
-  // Product operands. K order of a block: lane k group g takes elements 8 g .. 8 g + 7, i.e.
-  // image bytes 8 g .. 8 g + 7 and the weight nibbles of bytes 8 (g & 1) .. 8 (g & 1) + 7, low
-  // nibbles for g < 2 and high ones for g >= 2 (byte i of a Q4_0 block holds elements i and
-  // i + 16). This lane's image operand of block b, sub-tile j: a_img ^ (32 b), plus 2048 j.
-  const uint32_t a_img = n * 128 + 16 * (((n >> 1) & 7) ^ (g >> 1)) + 8 * (g & 1);
-  const int wsh = 4 * (g >> 1);
-  auto store_scales = [&](int buf) {
-    s_das[buf][sr][sb] = (uint16_t)(idw & 0xffffu);
-    s_das[buf][sr][4 + sb] = (uint16_t)(idw >> 16);
-    reinterpret_cast<uint16_t*>(&s_wd4[w][n])[g] = wdv;
-  };
-  float acc[4][4];
-  v4f sacc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sacc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[j][v] = 0.0f;
-  }
-  // the scale rows this lane reads: its image rows in k group 0, the zero row elsewhere
-  const int das_row = g == 0 ? n : 64, das_step = g == 0 ? 16 : 0;
 
-  // the scale loads go out before the copies; one wait covers both (the copies are not
-  // counted by the compiler)
-  load_scales(0);
+  // Products on v_mfma_i32_32x32x32_i8, one block each: lane (i, h) = (lane & 31, lane >> 5)
+  // holds elements 16 h .. 16 h + 15 of the block, i.e. image piece 2 b + h of image row i and
+  // the low (h = 0) or high (h = 1) nibbles of weight row i's 16 block bytes (byte k holds
+  // elements k and k + 16). D[8 u + 4 h + v][i] lands in lane (i, h), register 4 u + v.
+  const int i32 = lane & 31, h = lane >> 5;
+  const int wr = w >> 1, wc = w & 1;
+  const int tt = 2 * wr + (i32 >> 4), r16 = i32 & 15;  // this lane's weight tile and row in it
+  const int ir = 32 * wc + i32;                          // this lane's local image row
+  const uint32_t a_img = ir * 128 + 16 * (h ^ (ir & 7));  // block b: a_img ^ (32 b)
+  // Scale products (f16, exact in f32) on v_mfma_f32_32x32x8_f16, k group h holding blocks 2 h and
+  // 2 h + 1 as (d_a, s_a, d_a, s_a) on the image side; the weight side is, per block b, d_w in
+  // slot 2 (b & 1) of group b >> 1 (the d_w d_a outer product), and per chunk (0, d_w, 0, d_w)
+  // in both groups (the chunk's sum of d_w s_a).
+  float acc[16];
+  v16f sacc;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    acc[k] = 0.0f;
+    sacc[k] = 0.0f;
+  }
+
   copy_chunk(0, 0);
   wait_vmcnt<0>();
-  store_scales(0);
   __syncthreads();
   for (int s = 0; s < KC; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < KC) {
-      load_scales(s + 1);
-      copy_chunk(s + 1, buf ^ 1);
-    }
-    const uint64_t dwv = s_wd4[w][lane];
-    uint64_t dav[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint64_t* ds4 = reinterpret_cast<const uint64_t*>(&s_das[buf][das_row + das_step * j][0]);
-      dav[j] = ds4[0];
-      sacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_v4h(dwv), as_v4h(ds4[1]), sacc[j], 0, 0, 0);
-    }
+    const int q = s & 1;
+    if (s + 1 < KC) copy_chunk(s + 1, q ^ 1);
+    const uint64_t wsw = (uint64_t)s_wsc[tt][q][32 * h + r16] | ((uint64_t)s_wsc[tt][q][32 * h + 16 + r16] << 32);
+    const uint64_t dav = *reinterpret_cast<const uint64_t*>(&s_isc[q][ir][2 * h]);
+    sacc = __builtin_amdgcn_mfma_f32_32x32x8f16(as_v4h(wsw << 16), as_v4h(dav), sacc, 0, 0, 0);
     // the LDS operands of block b are read one block ahead (two operand sets, ping-pong); the
     // products and scaling of each block stay in a scheduling region of their own
-    struct Ops { uint2 wb; uint2 cc[4]; };
+    struct Ops { uint4 wb; uint4 ib; };
     auto ops = [&](int b, Ops& o) {
-      o.wb = *reinterpret_cast<const uint2*>(&s_wt[w][buf][(16 * b + n) * 4 + 2 * (g & 1)]);
-      const uint32_t ab = a_img ^ (32u * b);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o.cc[j] = *reinterpret_cast<const uint2*>(&s_img[buf][ab + 2048 * j]);
+      o.wb = *reinterpret_cast<const uint4*>(&s_wt[tt][q][(16 * b + r16) * 4]);
+      o.ib = *reinterpret_cast<const uint4*>(&s_img[q][a_img ^ (32u * b)]);
     };
-    // the weight-side f16 operand of block b's d_w d_a product: the chunk's d_w word with the
-    // other blocks' slots cleared (zero outside the lanes of k group 0, as that word is)
     auto block = [&](const Ops& o, int b) {
-      const uint64_t dwb = dwv & (0xffffull << (16 * b));
-      const uint32_t lo = (o.wb.x >> wsh) & 0x0f0f0f0fu, hi = (o.wb.y >> wsh) & 0x0f0f0f0fu;
-      const v1l a = (v1l)(((uint64_t)hi << 32) | lo);
-      v4i dd[4];
-      v4f dwda[4];
+      const uint64_t dwb = h == (b >> 1) ? (wsw & (b & 1 ? 0xffffffff00000000ull : 0xffffffffull)) : 0ull;
+      const int sh = 4 * h;
+      const v4i a = {(int)((o.wb.x >> sh) & 0x0f0f0f0fu), (int)((o.wb.y >> sh) & 0x0f0f0f0fu),
+                     (int)((o.wb.z >> sh) & 0x0f0f0f0fu), (int)((o.wb.w >> sh) & 0x0f0f0f0fu)};
+      const v4i bb = {(int)o.ib.x, (int)o.ib.y, (int)o.ib.z, (int)o.ib.w};
+      v16i zero;
+      v16f fzero;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v1l bb = (v1l)(((uint64_t)o.cc[j].y << 32) | o.cc[j].x);
-        const v4i zero = {0, 0, 0, 0};
-        const v4f fzero = {0.0f, 0.0f, 0.0f, 0.0f};
-        dd[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bb, zero, 0, 0, 0);
-        dwda[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_v4h(dwb), as_v4h(dav[j]), fzero, 0, 0, 0);
+      for (int k = 0; k < 16; ++k) {
+        zero[k] = 0;
+        fzero[k] = 0.0f;
       }
+      const v16i dd = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bb, zero, 0, 0, 0);
+      const v16f dwda = __builtin_amdgcn_mfma_f32_32x32x8f16(as_v4h(dwb), as_v4h(dav), fzero, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[j][v] = __builtin_fmaf(dwda[j][v], (float)dd[j][v], acc[j][v]);
+      for (int k = 0; k < 16; ++k) acc[k] = __builtin_fmaf(dwda[k], (float)dd[k], acc[k]);
       // the block's scaling is done here (not sunk below the next blocks' products)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        asm volatile("" : "+v"(acc[j][0]), "+v"(acc[j][1]), "+v"(acc[j][2]), "+v"(acc[j][3]));
+      for (int k = 0; k < 16; k += 4)
+        asm volatile("" : "+v"(acc[k]), "+v"(acc[k + 1]), "+v"(acc[k + 2]), "+v"(acc[k + 3]));
     };
-    Ops oa, ob;
-    ops(0, oa);
-    ops(1, ob);
-    block(oa, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    ops(2, oa);
-    block(ob, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    ops(3, ob);
-    block(oa, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    block(ob, 3);
-    if (s + 1 < KC) {
-      wait_vmcnt<0>();
-      store_scales(buf ^ 1);
+    Ops oa;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      ops(b, oa);
+      block(oa, b);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the next chunk's copies have landed (nothing else in the loop uses the counter)
+    if (s + 1 < KC) wait_vmcnt<0>();
     __syncthreads();
   }
-  if (!has) return;
-  const ReaderDesc& r = p.r[ri];
-  const int row0 = lt * 16 + 4 * g;
+  // lane (i, h), register 4 u + v: weight row 8 u + 4 h + v of the wave's 32 (tile 2 wr + (u >> 1)),
+  // image row 32 wc + i
+  const int col = c0 + 32 * wc + i32;
+  if (col >= live) return;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = c0 + 16 * j + n;
-    if (col < live) {
-      float* o = r.out + (int64_t)col * r.ld + row0;
+  for (int half = 0; half < 2; ++half) {
+    int ri, lt;
+    if (!tile_of(2 * wr + half, ri, lt)) continue;
+    const ReaderDesc& r = p.r[ri];
+    float* o = r.out + (int64_t)col * r.ld;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (row0 + v < r.N) o[v] = __builtin_fmaf(-8.0f, sacc[j][v], acc[j][v]);
-    }
+    for (int u = 2 * half; u < 2 * half + 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = lt * 16 + 8 * (u & 1) + 4 * h + v;
+        if (row < r.N) o[row] = __builtin_fmaf(-8.0f, sacc[4 * u + v], acc[4 * u + v]);
+      }
   }
 }
 
