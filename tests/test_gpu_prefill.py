@@ -54,7 +54,8 @@ def check(out, r, img_o, img_rows, rows, K, what):
 
 
 @pytest.mark.parametrize("T,live,K,Ns", [(200, 187, 2592, (37, 64, 16)), (64, None, 32, (5,)),
-                                         (130, 65, 8192, (48, 16))])
+                                         (130, 65, 8192, (48, 16)), (96, 1, 544, (24, 40)),
+                                         (128, 0, 256, (16,))])
 def test_prefill_reader_ragged(T, live, K, Ns):
     g = np.random.default_rng(T + K)
     x = g.standard_normal((T, K)).astype(np.float32)
@@ -63,9 +64,10 @@ def test_prefill_reader_ragged(T, live, K, Ns):
     _, img = produce(x, gamma, live)
     outs = read(readers, img, T, K, live)
     L = T if live is None else live
-    img_o = O.quantize(O.rmsnorm(x[:L], gamma, W.EPS), img_rows=T)
+    img_o = O.quantize(O.rmsnorm(x[:L], gamma, W.EPS), img_rows=T) if L else None
     for i, (r, out) in enumerate(zip(readers, outs)):
-        check(out, r, img_o, T, L, K, "prefill reader %d" % i)
+        if L:
+            check(out, r, img_o, T, L, K, "prefill reader %d" % i)
         assert (out[L:].view(np.uint8) == H.SENTINEL_BYTE).all(), "rows past the live count written"
 
 
